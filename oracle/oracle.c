@@ -1,0 +1,345 @@
+/*
+ * oracle.c -- plain CPU reference for the seven Benchmark Streaming (BS)
+ * operations of "Portable high-order finite element kernels I: Streaming
+ * Operations" (arXiv 2009.10917), and for the mesh tables they run on.
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark load this library. It shares no source with
+ * the HIP library and includes none of its headers.
+ *
+ * Arithmetic: IEEE binary64, round to nearest even, every product and sum
+ * rounded on its own (built with -ffp-contract=off; the only fused
+ * multiply-add is the explicit fma() of the error-free product below).
+ *
+ * Functions and the passages they follow (arXiv 2009.10917 unless noted):
+ *   or_copy       BS1 copy, y = x                 (BS test list, "copy")
+ *   or_axpy       BS2 y = alpha x + beta y         (CG vector operations, "vector addition")
+ *   or_dot        BS4 alpha = x . y                (CG vector operations, "dot product")
+ *   or_norm       BS3, the square root of x . x    (CG vector operations, "norm")
+ *   or_cg_update  BS5 fused CG update              (BS test list: CG steps 8-10 fused)
+ *   or_scatter    BS7 v_L = Z v_G                  (eq. 3; scatterIds with negative = masked)
+ *   or_gather     BS6 v_G = Z^T v_L                (eq. 3 and the gather operator after it)
+ *   or_gll_nodes  GLL points of degree p           (nodes of eqs. 1-2)
+ *   or_mesh_box   I_l->g of a box hex mesh         (eqs. 1-3; arXiv 1506.05996, local-to-global table)
+ *   or_g2l        CSR form of I_g->l               (arXiv 1506.05996, global-to-local table)
+ *
+ * The reductions (dot, norm, the residual norm of the fused update) are
+ * evaluated accurately with Dot2 of Ogita, Rump and Oishi ("Accurate sum and
+ * dot product", SIAM J. Sci. Comput. 26(6), 2005): error-free products and
+ * sums inside fixed chunks of 2^16 terms, then the chunk results summed with
+ * cascaded error-free sums in chunk order. The result does not depend on the
+ * thread count and is far more accurate than the 1e-12 relative tolerance the
+ * GPU is held to.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_CHUNK 65536
+
+/* ---------------------------------------------------------------- BS1 --- */
+/* y = x as a bit copy: NaN payloads and signed zeros are preserved. */
+void or_copy(int64_t n, const double *x, double *y)
+{
+    if (n > 0) memcpy(y, x, (size_t)n * sizeof(double));
+}
+
+/* ---------------------------------------------------------------- BS2 --- */
+/* y = (alpha * x) + (beta * y), each product rounded, then the sum rounded.
+ * y is always read, also for beta == 0. */
+void or_axpy(int64_t n, double alpha, const double *x, double beta, double *y)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        double t1 = alpha * x[i];
+        double t2 = beta * y[i];
+        y[i] = t1 + t2;
+    }
+}
+
+/* ------------------------------------------- accurate reductions (Dot2) --- */
+static void two_sum(double a, double b, double *s, double *e)
+{
+    double x = a + b;
+    double z = x - a;
+    *e = (a - (x - z)) + (b - z);
+    *s = x;
+}
+
+static void two_prod(double a, double b, double *p, double *e)
+{
+    double x = a * b;
+    *e = fma(a, b, -x);
+    *p = x;
+}
+
+/* Dot2 over one chunk: returns the leading sum in *hi and the accumulated
+ * error terms in *lo. */
+static void dot2_chunk(int64_t n, const double *x, const double *y, double *hi, double *lo)
+{
+    double p = 0.0, s = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        double h, r, q;
+        two_prod(x[i], y[i], &h, &r);
+        two_sum(p, h, &p, &q);
+        s = s + (q + r);
+    }
+    *hi = p;
+    *lo = s;
+}
+
+double or_dot(int64_t n, const double *x, const double *y)
+{
+    if (n <= 0) return 0.0;
+    int64_t nc = (n + OR_CHUNK - 1) / OR_CHUNK;
+    double *part = (double *)malloc((size_t)(2 * nc) * sizeof(double));
+    if (!part) return NAN;
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < nc; ++c) {
+        int64_t a = c * OR_CHUNK;
+        int64_t len = (n - a < OR_CHUNK) ? (n - a) : OR_CHUNK;
+        dot2_chunk(len, x + a, y + a, &part[2 * c], &part[2 * c + 1]);
+    }
+    /* cascaded error-free summation of hi_0, lo_0, hi_1, lo_1, ... in order */
+    double pi = part[0], sigma = 0.0;
+    for (int64_t k = 1; k < 2 * nc; ++k) {
+        double q;
+        two_sum(pi, part[k], &pi, &q);
+        sigma = sigma + q;
+    }
+    free(part);
+    return pi + sigma;
+}
+
+/* ---------------------------------------------------------------- BS3 --- */
+double or_norm(int64_t n, const double *x)
+{
+    return sqrt(or_dot(n, x, x));
+}
+
+/* ---------------------------------------------------------------- BS5 --- */
+/* x = x + (alpha p); r = r - (alpha q); returns r . r of the updated r. */
+double or_cg_update(int64_t n, double alpha, const double *p, const double *q,
+                    double *x, double *r)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        double ap = alpha * p[i];
+        double aq = alpha * q[i];
+        x[i] = x[i] + ap;
+        r[i] = r[i] - aq;
+    }
+    return or_dot(n, r, r);
+}
+
+/* ---------------------------------------------------------------- BS7 --- */
+/* v_L[i] = v_G[l2g[i]]; a negative id is a masked row of Z, giving +0.0. */
+void or_scatter(int64_t n_local, const int32_t *l2g, const double *v_global, double *v_local)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n_local; ++i)
+        v_local[i] = (l2g[i] >= 0) ? v_global[l2g[i]] : 0.0;
+}
+
+/* ---------------------------------------------------------------- BS6 --- */
+/* v_G = Z^T v_L straight from the definition of Z: every global entry starts
+ * at +0.0 and receives the local values that map to it, in ascending local
+ * index. Masked (negative) ids contribute nothing. */
+void or_gather(int64_t n_local, int64_t n_global, const int32_t *l2g,
+               const double *v_local, double *v_global)
+{
+    for (int64_t g = 0; g < n_global; ++g) v_global[g] = 0.0;
+    for (int64_t i = 0; i < n_local; ++i)
+        if (l2g[i] >= 0) v_global[l2g[i]] = v_global[l2g[i]] + v_local[i];
+}
+
+/* -------------------------------------------------------- GLL points --- */
+/* Legendre P_p(t) and P_{p-1}(t) by the three-term recurrence. */
+static void legendre(int p, double t, double *Pp, double *Pm)
+{
+    double a = 1.0, b = t;            /* P_0, P_1 */
+    if (p == 0) { *Pp = 1.0; *Pm = 0.0; return; }
+    for (int k = 1; k < p; ++k) {
+        double c = ((2.0 * k + 1.0) * t * b - k * a) / (k + 1.0);
+        a = b;
+        b = c;
+    }
+    *Pp = b;
+    *Pm = a;
+}
+
+/* The p+1 Gauss-Lobatto-Legendre points on [-1, 1], ascending: the end points
+ * and the roots of P_p'. Newton's method from the Chebyshev-Lobatto points,
+ * with P_p' = p (t P_p - P_{p-1}) / (t^2 - 1) and, from Legendre's equation,
+ * P_p'' = (2 t P_p' - p (p+1) P_p) / (1 - t^2). Returns 0, or -1 if p < 1. */
+int or_gll_nodes(int p, double *r)
+{
+    if (p < 1) return -1;
+    r[0] = -1.0;
+    r[p] = 1.0;
+    for (int i = 1; i < p; ++i) {
+        double t = -cos(M_PI * i / p);
+        for (int it = 0; it < 100; ++it) {
+            double P, Pm;
+            legendre(p, t, &P, &Pm);
+            double d1 = p * (t * P - Pm) / (t * t - 1.0);
+            double d2 = (2.0 * t * d1 - p * (p + 1.0) * P) / (1.0 - t * t);
+            double dt = d1 / d2;
+            t -= dt;
+            if (fabs(dt) < 1e-16) break;
+        }
+        r[i] = t;
+    }
+    return 0;
+}
+
+/* --------------------------------------------------------- box mesh --- */
+static int cmp_double(const void *pa, const void *pb)
+{
+    double a = *(const double *)pa, b = *(const double *)pb;
+    return (a < b) ? -1 : (a > b);
+}
+
+/* Position of the GLL point r_i in cell c of one axis: c + (1 + r_i)/2. The
+ * end points r_0 = -1 and r_p = 1 land exactly on c and c+1, so neighbouring
+ * cells share their boundary positions. */
+static double axis_pos(int64_t c, double ri)
+{
+    return (double)c + (1.0 + ri) / 2.0;
+}
+
+/* Sorted distinct positions of one axis with `cells` cells; returns count. */
+static int64_t axis_values(int64_t cells, int p, const double *r, double *u)
+{
+    int64_t m = 0;
+    for (int64_t c = 0; c < cells; ++c)
+        for (int i = 0; i <= p; ++i) u[m++] = axis_pos(c, r[i]);
+    qsort(u, (size_t)m, sizeof(double), cmp_double);
+    int64_t d = 0;
+    for (int64_t t = 0; t < m; ++t)
+        if (t == 0 || u[t] != u[d - 1]) u[d++] = u[t];
+    return d;
+}
+
+/* Index of v in the sorted distinct array u[0..n-1] (v is present). */
+static int64_t axis_rank(const double *u, int64_t n, double v)
+{
+    int64_t lo = 0, hi = n - 1;
+    while (lo < hi) {
+        int64_t mid = (lo + hi) / 2;
+        if (u[mid] < v) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+}
+
+/*
+ * I_l->g of the box [0,ex]x[0,ey]x[0,ez] cut into unit hexahedra, each
+ * carrying the (p+1)^3 tensor-product GLL nodes mapped from the reference
+ * cube. Global nodes are the distinct physical positions: two local nodes
+ * share a global id exactly when their positions coincide. Ids run over the
+ * distinct positions in lexicographic order, x fastest, then y, then z;
+ * node_perm (optional) renames id g to node_perm[g].
+ *
+ * Positions are compared through their per-axis ranks among the distinct
+ * coordinate values of that axis: equal positions have equal rank triples and
+ * the rank triple orders positions lexicographically. The distinct triples
+ * present are then numbered in that order.
+ *
+ * Local storage is element by element; inside an element the node (i,j,k)
+ * sits at i + (p+1)(j + (p+1)k). Storage slot s holds element elem_perm[s]
+ * (optional; identity otherwise), element e being (e % ex, (e/ex) % ey,
+ * e/(ex*ey)).
+ *
+ * Returns the number of global nodes, or -1 on bad arguments or no memory.
+ */
+int64_t or_mesh_box(int ex, int ey, int ez, int p, const int32_t *elem_perm,
+                    const int32_t *node_perm, int32_t *l2g)
+{
+    if (ex < 1 || ey < 1 || ez < 1 || p < 1) return -1;
+    const int64_t nq = p + 1, Np = nq * nq * nq;
+    const int64_t K = (int64_t)ex * ey * ez, NL = K * Np;
+    double *r = (double *)malloc((size_t)nq * sizeof(double));
+    double *ux = (double *)malloc((size_t)(ex * nq) * sizeof(double));
+    double *uy = (double *)malloc((size_t)(ey * nq) * sizeof(double));
+    double *uz = (double *)malloc((size_t)(ez * nq) * sizeof(double));
+    int64_t *key = (int64_t *)malloc((size_t)NL * sizeof(int64_t));
+    if (!r || !ux || !uy || !uz || !key) goto fail;
+    or_gll_nodes(p, r);
+    int64_t nx = axis_values(ex, p, r, ux);
+    int64_t ny = axis_values(ey, p, r, uy);
+    int64_t nz = axis_values(ez, p, r, uz);
+    int64_t nkeys = nx * ny * nz;
+    int32_t *rank = (int32_t *)calloc((size_t)nkeys, sizeof(int32_t));
+    if (!rank) goto fail;
+    for (int64_t s = 0; s < K; ++s) {
+        int64_t e = elem_perm ? elem_perm[s] : s;
+        int64_t cx = e % ex, cy = (e / ex) % ey, cz = e / ((int64_t)ex * ey);
+        for (int64_t k = 0; k < nq; ++k)
+            for (int64_t j = 0; j < nq; ++j)
+                for (int64_t i = 0; i < nq; ++i) {
+                    int64_t L = s * Np + i + nq * (j + nq * k);
+                    int64_t ix = axis_rank(ux, nx, axis_pos(cx, r[i]));
+                    int64_t iy = axis_rank(uy, ny, axis_pos(cy, r[j]));
+                    int64_t iz = axis_rank(uz, nz, axis_pos(cz, r[k]));
+                    key[L] = (iz * ny + iy) * nx + ix;
+                    rank[key[L]] = 1;
+                }
+    }
+    int64_t NG = 0;
+    for (int64_t t = 0; t < nkeys; ++t) {
+        int32_t present = rank[t];
+        rank[t] = (int32_t)NG;
+        NG += present;
+    }
+    for (int64_t L = 0; L < NL; ++L) {
+        int32_t g = rank[key[L]];
+        l2g[L] = node_perm ? node_perm[g] : g;
+    }
+    free(rank);
+    free(key); free(uz); free(uy); free(ux); free(r);
+    return NG;
+fail:
+    free(key); free(uz); free(uy); free(ux); free(r);
+    return -1;
+}
+
+/* ---------------------------------------------------- CSR of I_g->l --- */
+typedef struct { int32_t g; int64_t i; } or_pair;
+
+static int cmp_pair(const void *pa, const void *pb)
+{
+    const or_pair *a = (const or_pair *)pa, *b = (const or_pair *)pb;
+    if (a->g != b->g) return a->g < b->g ? -1 : 1;
+    return (a->i < b->i) ? -1 : (a->i > b->i);
+}
+
+/* For each global node g, ids[off[g] .. off[g+1]-1] lists the local indices
+ * i with l2g[i] == g, ascending. Masked (negative) entries are left out.
+ * Returns the number of entries, or -1 on an id out of range / no memory. */
+int64_t or_g2l(int64_t n_local, int64_t n_global, const int32_t *l2g,
+               int32_t *off, int32_t *ids)
+{
+    or_pair *pr = (or_pair *)malloc((size_t)(n_local > 0 ? n_local : 1) * sizeof(or_pair));
+    if (!pr) return -1;
+    int64_t m = 0;
+    for (int64_t i = 0; i < n_local; ++i) {
+        if (l2g[i] < 0) continue;
+        if (l2g[i] >= n_global) { free(pr); return -1; }
+        pr[m].g = l2g[i];
+        pr[m].i = i;
+        ++m;
+    }
+    qsort(pr, (size_t)m, sizeof(or_pair), cmp_pair);
+    int64_t t = 0;
+    for (int64_t g = 0; g < n_global; ++g) {
+        off[g] = (int32_t)t;
+        while (t < m && pr[t].g == g) {
+            ids[t] = (int32_t)pr[t].i;
+            ++t;
+        }
+    }
+    off[n_global] = (int32_t)t;
+    free(pr);
+    return m;
+}
