@@ -1,0 +1,325 @@
+"""Python binding of libbs: the Benchmark Streaming operations on MI355X.
+
+Argument marshalling only. Every operation runs in the HIP kernels of
+``libbs.so`` (built in-tree for gfx950 by ``_build.py``); this module checks
+shapes and dtypes, takes raw pointers from torch tensors, and turns a nonzero
+status into ``BSError``. There is no fallback: if the library or a GPU is
+missing, the calls raise.
+
+Device operations take torch tensors on a HIP device (float64 vectors, int32
+index tables) and enqueue on the current torch stream unless ``stream`` is
+given. Reductions write their scalar into a one-element float64 device tensor
+and return it, so no call synchronises the host. The table builders take and
+return numpy arrays on the host.
+
+Names and semantics are those of ``include/bs.h``: BS1 copy, BS2 AXPY, BS3
+norm, BS4 dot, BS5 fused CG update, BS6 gather, BS7 scatter ("Portable
+high-order finite element kernels I: Streaming Operations", arXiv
+2009.10917).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libbs.so")
+
+BS_OK, BS_EINVAL, BS_EALIGN, BS_ERANGE, BS_EHIP, BS_ENOMEM = 0, -1, -2, -3, -4, -5
+
+_i64 = ctypes.c_int64
+_dbl = ctypes.c_double
+_ptr = ctypes.c_void_p
+_int = ctypes.c_int
+
+
+class BSError(RuntimeError):
+    def __init__(self, status, what):
+        super().__init__(f"{what}: {_lib().bs_strerror(status).decode()} ({status})")
+        self.status = status
+
+
+_L = None
+_lock = threading.Lock()
+
+# (name, argtypes) of every entry point in include/bs.h
+SIGNATURES = {
+    "bs_strerror": ([_int], ctypes.c_char_p),
+    "bs_version": ([], _int),
+    "bs_ctx_create": ([_int, ctypes.POINTER(_ptr)], _int),
+    "bs_ctx_destroy": ([_ptr], None),
+    "bs_ctx_info": ([_ptr, ctypes.POINTER(_int), ctypes.POINTER(_int), ctypes.POINTER(_int)], _int),
+    "bs_copy": ([_ptr, _i64, _ptr, _ptr, _ptr], _int),
+    "bs_axpy": ([_ptr, _i64, _dbl, _ptr, _dbl, _ptr, _ptr], _int),
+    "bs_norm": ([_ptr, _i64, _ptr, _ptr, _ptr], _int),
+    "bs_dot": ([_ptr, _i64, _ptr, _ptr, _ptr, _ptr], _int),
+    "bs_cg_update": ([_ptr, _i64, _dbl, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr], _int),
+    "bs_scatter": ([_ptr, _i64, _ptr, _ptr, _ptr, _ptr], _int),
+    "bs_gather": ([_ptr, _i64, _ptr, _ptr, _ptr, _ptr, _ptr, _i64, _ptr], _int),
+    "bs_mesh_box_count": ([_int, _int, _int, _int, ctypes.POINTER(_i64), ctypes.POINTER(_i64)], _int),
+    "bs_mesh_box_l2g": ([_int, _int, _int, _int, _ptr, _ptr, _ptr], _int),
+    "bs_validate_l2g": ([_i64, _i64, _ptr], _int),
+    "bs_index_g2l": ([_i64, _i64, _ptr, _ptr, _ptr], _int),
+    "bs_gather_plan": ([_i64, _ptr, _int, _ptr, ctypes.POINTER(_i64)], _int),
+}
+
+
+def _lib():
+    global _L
+    if _L is None:
+        with _lock:
+            if _L is None:
+                if not os.path.exists(LIB_PATH):
+                    raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+                L = ctypes.CDLL(LIB_PATH)
+                for name, (args, res) in SIGNATURES.items():
+                    fn = getattr(L, name)
+                    fn.argtypes = args
+                    fn.restype = res
+                _L = L
+    return _L
+
+
+def _check(status, what):
+    if status != BS_OK:
+        raise BSError(status, what)
+
+
+# ---------------------------------------------------------------- context --
+
+class Context:
+    """A library context on one device (owns the reduction scratch)."""
+
+    def __init__(self, device: int = 0):
+        h = _ptr()
+        _check(_lib().bs_ctx_create(int(device), ctypes.byref(h)), "bs_ctx_create")
+        self._h = h
+        self.device = int(device)
+
+    @property
+    def handle(self):
+        return self._h
+
+    def info(self):
+        d, c, m = _int(), _int(), _int()
+        _check(_lib().bs_ctx_info(self._h, ctypes.byref(d), ctypes.byref(c), ctypes.byref(m)), "bs_ctx_info")
+        return {"device": d.value, "cu_count": c.value, "max_partials": m.value}
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            _lib().bs_ctx_destroy(self._h)
+            self._h = _ptr()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+_contexts = {}
+
+
+def context(device=None) -> Context:
+    """The shared per-device context (created on first use)."""
+    import torch
+    dev = torch.cuda.current_device() if device is None else int(device)
+    ctx = _contexts.get(dev)
+    if ctx is None:
+        ctx = _contexts[dev] = Context(dev)
+    return ctx
+
+
+# ------------------------------------------------------------ marshalling --
+
+def _dev_tensor(t, dtype, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a torch tensor on a HIP device")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream, device):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ctx_dev(t, ctx):
+    if ctx is None:
+        ctx = context(t.device.index)
+    return ctx
+
+
+def _scalar_out(out, like):
+    import torch
+    if out is None:
+        out = torch.empty(1, dtype=torch.float64, device=like.device)
+    _dev_tensor(out, torch.float64, "out")
+    if out.numel() < 1:
+        raise ValueError("out must hold one float64")
+    return out
+
+
+# ------------------------------------------------------------ operations --
+
+def bs_copy(x, y, *, ctx=None, stream=None):
+    """BS1: y[:] = x (bit copy)."""
+    import torch
+    if x.numel() != y.numel():
+        raise ValueError("x and y differ in length")
+    ctx = _ctx_dev(x, ctx)
+    _check(_lib().bs_copy(ctx.handle, x.numel(), _dev_tensor(x, torch.float64, "x"),
+                          _dev_tensor(y, torch.float64, "y"), _stream(stream, x.device)), "bs_copy")
+    return y
+
+
+def bs_axpy(alpha, x, beta, y, *, ctx=None, stream=None):
+    """BS2: y = (alpha*x) + (beta*y) in place."""
+    import torch
+    if x.numel() != y.numel():
+        raise ValueError("x and y differ in length")
+    ctx = _ctx_dev(x, ctx)
+    _check(_lib().bs_axpy(ctx.handle, x.numel(), float(alpha), _dev_tensor(x, torch.float64, "x"),
+                          float(beta), _dev_tensor(y, torch.float64, "y"), _stream(stream, x.device)),
+           "bs_axpy")
+    return y
+
+
+def bs_norm(x, out=None, *, ctx=None, stream=None):
+    """BS3: out[0] = sqrt(sum x^2) on the device; returns out."""
+    import torch
+    ctx = _ctx_dev(x, ctx)
+    out = _scalar_out(out, x)
+    _check(_lib().bs_norm(ctx.handle, x.numel(), _dev_tensor(x, torch.float64, "x"), out.data_ptr(),
+                          _stream(stream, x.device)), "bs_norm")
+    return out
+
+
+def bs_dot(x, y, out=None, *, ctx=None, stream=None):
+    """BS4: out[0] = sum x*y on the device; returns out."""
+    import torch
+    if x.numel() != y.numel():
+        raise ValueError("x and y differ in length")
+    ctx = _ctx_dev(x, ctx)
+    out = _scalar_out(out, x)
+    _check(_lib().bs_dot(ctx.handle, x.numel(), _dev_tensor(x, torch.float64, "x"),
+                         _dev_tensor(y, torch.float64, "y"), out.data_ptr(), _stream(stream, x.device)),
+           "bs_dot")
+    return out
+
+
+def bs_cg_update(alpha, p, q, x, r, out=None, *, ctx=None, stream=None):
+    """BS5: x += alpha p, r -= alpha q in place; out[0] = |r|^2; returns out."""
+    import torch
+    n = p.numel()
+    if not (q.numel() == x.numel() == r.numel() == n):
+        raise ValueError("p, q, x, r differ in length")
+    ctx = _ctx_dev(p, ctx)
+    out = _scalar_out(out, p)
+    _check(_lib().bs_cg_update(ctx.handle, n, float(alpha), _dev_tensor(p, torch.float64, "p"),
+                               _dev_tensor(q, torch.float64, "q"), _dev_tensor(x, torch.float64, "x"),
+                               _dev_tensor(r, torch.float64, "r"), out.data_ptr(),
+                               _stream(stream, p.device)), "bs_cg_update")
+    return out
+
+
+def bs_scatter(l2g, v_global, v_local, *, ctx=None, stream=None):
+    """BS7: v_local = Z v_global through l2g (negative ids give +0.0)."""
+    import torch
+    if l2g.numel() != v_local.numel():
+        raise ValueError("l2g and v_local differ in length")
+    ctx = _ctx_dev(v_local, ctx)
+    _check(_lib().bs_scatter(ctx.handle, l2g.numel(), _dev_tensor(l2g, torch.int32, "l2g"),
+                             _dev_tensor(v_global, torch.float64, "v_global"),
+                             _dev_tensor(v_local, torch.float64, "v_local"),
+                             _stream(stream, v_local.device)), "bs_scatter")
+    return v_local
+
+
+def bs_gather(off, ids, v_local, v_global, block_starts=None, *, ctx=None, stream=None):
+    """BS6: v_global = Z^T v_local through the CSR (off, ids), ascending order."""
+    import torch
+    ng = v_global.numel()
+    if off.numel() != ng + 1:
+        raise ValueError("off must hold n_global + 1 entries")
+    ctx = _ctx_dev(v_global, ctx)
+    bp, nb = None, 0
+    if block_starts is not None:
+        bp = _dev_tensor(block_starts, torch.int32, "block_starts")
+        nb = block_starts.numel() - 1
+    _check(_lib().bs_gather(ctx.handle, ng, _dev_tensor(off, torch.int32, "off"),
+                            _dev_tensor(ids, torch.int32, "ids"),
+                            _dev_tensor(v_local, torch.float64, "v_local"),
+                            _dev_tensor(v_global, torch.float64, "v_global"), bp, nb,
+                            _stream(stream, v_global.device)), "bs_gather")
+    return v_global
+
+
+# ------------------------------------------------------------ host tables --
+
+def _host_i32(a, name):
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.int32:
+        raise TypeError(f"{name} must be int32")
+    return a
+
+
+def bs_mesh_box_count(ex, ey, ez, order):
+    nl, ng = _i64(), _i64()
+    _check(_lib().bs_mesh_box_count(ex, ey, ez, order, ctypes.byref(nl), ctypes.byref(ng)), "bs_mesh_box_count")
+    return nl.value, ng.value
+
+
+def bs_mesh_box_l2g(ex, ey, ez, order, elem_perm=None, node_perm=None):
+    """I_l->g of a box mesh (int32 numpy array of length n_local)."""
+    nl, _ = bs_mesh_box_count(ex, ey, ez, order)
+    l2g = np.empty(nl, dtype=np.int32)
+    ep = None if elem_perm is None else _host_i32(elem_perm, "elem_perm")
+    npm = None if node_perm is None else _host_i32(node_perm, "node_perm")
+    _check(_lib().bs_mesh_box_l2g(ex, ey, ez, order, None if ep is None else ep.ctypes.data,
+                                  None if npm is None else npm.ctypes.data, l2g.ctypes.data), "bs_mesh_box_l2g")
+    return l2g
+
+
+def bs_validate_l2g(l2g, n_global):
+    l2g = _host_i32(l2g, "l2g")
+    _check(_lib().bs_validate_l2g(l2g.size, int(n_global), l2g.ctypes.data), "bs_validate_l2g")
+
+
+def bs_index_g2l(l2g, n_global):
+    """CSR of I_g->l: (off int32[n_global+1], ids int32[entries])."""
+    l2g = _host_i32(l2g, "l2g")
+    off = np.empty(int(n_global) + 1, dtype=np.int32)
+    ids = np.empty(max(1, l2g.size), dtype=np.int32)
+    _check(_lib().bs_index_g2l(l2g.size, int(n_global), l2g.ctypes.data, off.ctypes.data, ids.ctypes.data),
+           "bs_index_g2l")
+    return off, ids[:int(off[-1])]
+
+
+def bs_gather_plan(off, nodes_per_block=2048):
+    """blockStarts for the LDS-staged gather (int32 numpy array)."""
+    off = _host_i32(off, "off")
+    ng = off.size - 1
+    bs = np.empty(ng + 1, dtype=np.int32)
+    nb = _i64()
+    _check(_lib().bs_gather_plan(ng, off.ctypes.data, int(nodes_per_block), bs.ctypes.data, ctypes.byref(nb)),
+           "bs_gather_plan")
+    return bs[:nb.value + 1].copy()
+
+
+__all__ = [
+    "BSError", "Context", "context", "LIB_PATH", "SIGNATURES",
+    "bs_copy", "bs_axpy", "bs_norm", "bs_dot", "bs_cg_update", "bs_scatter", "bs_gather",
+    "bs_mesh_box_count", "bs_mesh_box_l2g", "bs_validate_l2g", "bs_index_g2l", "bs_gather_plan",
+]

@@ -1,0 +1,176 @@
+/*
+ * bs.h -- C ABI of the MI355X (gfx950) Benchmark Streaming library.
+ *
+ * The seven streaming operations of a Conjugate Gradient solve on high-order
+ * hexahedral meshes, as named in "Portable high-order finite element kernels
+ * I: Streaming Operations" (arXiv 2009.10917, the BS test list): BS1 copy,
+ * BS2 AXPY, BS3 norm, BS4 inner product, BS5 fused CG update, BS6 gather,
+ * BS7 scatter; plus the host-side builder of the index tables they need
+ * (I_l->g and the CSR form of I_g->l of "GPU accelerated spectral finite
+ * elements on all-hex meshes", arXiv 1506.05996).
+ *
+ * Conventions for every call below:
+ *  - Vector and index pointers passed to the bs_* device operations are HIP
+ *    device pointers owned by the caller. The library never allocates, frees
+ *    or retains them. Scalars results are written to a caller-owned device
+ *    double, so no call forces a host synchronisation.
+ *  - Arithmetic is IEEE binary64, round to nearest even, each product and sum
+ *    rounded separately (no fused multiply-add) wherever a result is required
+ *    to be bit-exact. Indices are int32.
+ *  - Every device operation is enqueued on `stream` (a hipStream_t passed as
+ *    void*; NULL is the default stream) and returns at once. A fault inside a
+ *    kernel surfaces at the caller's next synchronisation, not here.
+ *  - Return value: BS_OK, or a negative bs_status; on error nothing has been
+ *    enqueued. n == 0 is a no-op for vector outputs; reductions then store
+ *    +0.0. n < 0, or a NULL pointer with n > 0, is BS_EINVAL. Double pointers
+ *    must be 8-byte aligned and int32 pointers 4-byte aligned (BS_EALIGN).
+ *  - A context owns the reduction scratch of one device. Calls that use the
+ *    same context must be ordered (one stream, or explicit dependencies);
+ *    concurrent reductions on one context race.
+ */
+#ifndef BS_H
+#define BS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BS_OK = 0,
+    BS_EINVAL = -1, /* bad size, NULL pointer, bad mesh argument, bad table   */
+    BS_EALIGN = -2, /* pointer not aligned to its element size                */
+    BS_ERANGE = -3, /* size beyond what int32 indices or the builder can hold */
+    BS_EHIP = -4,   /* the HIP runtime reported an error (launch, device)     */
+    BS_ENOMEM = -5  /* host or device allocation failed                       */
+} bs_status;
+
+typedef struct bs_ctx bs_ctx;
+
+/* Text for a status code (static storage; never NULL). */
+const char *bs_strerror(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int bs_version(void);
+
+/* Create a context on HIP device `device`: queries its compute-unit count and
+ * allocates the reduction scratch (partials and a completion counter) on that
+ * device. *out receives the context; the caller releases it with
+ * bs_ctx_destroy. Errors: BS_EINVAL (out NULL), BS_EHIP (no such device),
+ * BS_ENOMEM. */
+int bs_ctx_create(int device, bs_ctx **out);
+
+/* Release a context and its scratch. Waits for the device to finish work that
+ * may use the scratch. NULL is accepted. */
+void bs_ctx_destroy(bs_ctx *ctx);
+
+/* Device and compute-unit count of a context; NULL outputs are skipped. */
+int bs_ctx_info(const bs_ctx *ctx, int *device, int *cu_count, int *max_partials);
+
+/* ------------------------------------------------------------------------
+ * BS1 copy (arXiv 2009.10917, BS test list): y[i] = x[i] for 0 <= i < n, a
+ * bit copy (NaN payloads and signed zeros kept). x and y are contiguous
+ * double[n]; x == y is allowed, any other overlap is undefined. */
+int bs_copy(bs_ctx *ctx, int64_t n, const double *x, double *y, void *stream);
+
+/* BS2 AXPY, the CG "vector addition" y = alpha x + beta y (arXiv
+ * 2009.10917, CG vector-operation list): y[i] = (alpha*x[i]) + (beta*y[i]),
+ * each product rounded, then the sum; bit-exact. y is read also when
+ * beta == 0. x, y contiguous double[n]; x == y allowed. */
+int bs_axpy(bs_ctx *ctx, int64_t n, double alpha, const double *x, double beta,
+            double *y, void *stream);
+
+/* BS3 norm (arXiv 2009.10917, CG vector-operation list and the two-kernel
+ * reduction of the implementation section): *result = sqrt(sum x[i]^2), the
+ * 2-norm, written to the device double `result`. The sum is reduced in a
+ * fixed order that depends only on n and the device's compute-unit count, so
+ * repeated calls give the same bits; it agrees with the exact value to a
+ * relative 1e-12. x contiguous double[n]. */
+int bs_norm(bs_ctx *ctx, int64_t n, const double *x, double *result, void *stream);
+
+/* BS4 inner product (arXiv 2009.10917, CG vector-operation list): *result =
+ * sum x[i]*y[i] into the device double `result`, same reduction guarantees as
+ * bs_norm. x, y contiguous double[n]. */
+int bs_dot(bs_ctx *ctx, int64_t n, const double *x, const double *y, double *result,
+           void *stream);
+
+/* BS5 fused CG update (arXiv 2009.10917, BS test list: CG steps 8-10 in one
+ * pass, saving a read and a write of r): x[i] = x[i] + (alpha*p[i]);
+ * r[i] = r[i] - (alpha*q[i]) (bit-exact), and *rr = sum of the updated r[i]^2
+ * into the device double `rr` (reduction guarantees as bs_norm). p, q, x, r
+ * contiguous double[n] and pairwise distinct. */
+int bs_cg_update(bs_ctx *ctx, int64_t n, double alpha, const double *p, const double *q,
+                 double *x, double *r, double *rr, void *stream);
+
+/* BS7 scatter v_L = Z v_G (arXiv 2009.10917, eq. 3 and the scatterIds array
+ * of the implementation section; arXiv 1506.05996, local-to-global table):
+ * v_local[i] = v_global[l2g[i]] for l2g[i] >= 0, and +0.0 for a negative
+ * (masked) id. l2g int32[n_local] in element-major local order; v_local
+ * double[n_local]; v_global double[>= 1 + max id]. Ids are not range-checked
+ * on the device: check tables once with bs_validate_l2g. n_local > INT32_MAX
+ * is BS_ERANGE. */
+int bs_scatter(bs_ctx *ctx, int64_t n_local, const int32_t *l2g, const double *v_global,
+               double *v_local, void *stream);
+
+/* BS6 gather v_G = Z^T v_L (arXiv 2009.10917, eq. 3, the gather operator and
+ * the CSR/blockStarts kernel of the implementation section; arXiv
+ * 1506.05996, global-to-local table): v_global[g] = sum of v_local[ids[j]] for
+ * off[g] <= j < off[g+1], added left to right starting from +0.0, so with ids
+ * ascending inside each row the result is bit-identical to Z^T v_L summed in
+ * ascending local index. off int32[n_global+1], ids int32[off[n_global]],
+ * v_local double[> max id], v_global double[n_global]. block_starts NULL
+ * selects the row-per-lane kernel; otherwise int32[n_blocks+1] from
+ * bs_gather_plan selects the LDS-staged kernel (same bits). n_global or the
+ * entry count beyond INT32_MAX is BS_ERANGE. */
+int bs_gather(bs_ctx *ctx, int64_t n_global, const int32_t *off, const int32_t *ids,
+              const double *v_local, double *v_global, const int32_t *block_starts,
+              int64_t n_blocks, void *stream);
+
+/* ---------------------------------------------------- host-side tables --
+ * These run on the host, need no GPU, and write caller-allocated host arrays.
+ */
+
+/* Sizes of a box mesh of ex*ey*ez hexahedra of order `order`:
+ * *n_local = ex*ey*ez*(order+1)^3, *n_global = (ex*order+1)(ey*order+1)(ez*order+1).
+ * BS_EINVAL for a dimension or order < 1, BS_ERANGE if either exceeds INT32_MAX. */
+int bs_mesh_box_count(int ex, int ey, int ez, int order, int64_t *n_local, int64_t *n_global);
+
+/* I_l->g of the structured box of unit hexahedra with (order+1)^3 GLL nodes
+ * each (arXiv 2009.10917, eqs. 1-3; arXiv 1506.05996, local-to-global
+ * table). Element e = cx + ex*(cy + ey*cz); slot s of local storage holds
+ * element elem_perm[s] (NULL: s). Within a slot the node (i,j,k) sits at
+ * s*(order+1)^3 + i + (order+1)*(j + (order+1)*k). Its lexicographic global
+ * id is gx + Gx*(gy + Gy*gz) with gx = cx*order + i, Gx = ex*order + 1 (same for
+ * y, z); node_perm (NULL: identity) renames id g to node_perm[g]. Both
+ * permutations must be permutations (checked: BS_EINVAL). l2g receives
+ * int32[n_local]. */
+int bs_mesh_box_l2g(int ex, int ey, int ez, int order, const int32_t *elem_perm,
+                    const int32_t *node_perm, int32_t *l2g);
+
+/* Check that every id is < n_global (negative ids are masks): BS_OK or
+ * BS_EINVAL. */
+int bs_validate_l2g(int64_t n_local, int64_t n_global, const int32_t *l2g);
+
+/* CSR form of I_g->l: a stable counting-sort transpose of l2g. off receives
+ * int32[n_global+1]; ids receives the off[n_global] local indices (at most
+ * n_local; masked entries are left out), ascending within each row. An id
+ * >= n_global is BS_EINVAL. */
+int bs_index_g2l(int64_t n_local, int64_t n_global, const int32_t *l2g, int32_t *off,
+                 int32_t *ids);
+
+/* blockStarts of the LDS-staged gather (arXiv 2009.10917, implementation
+ * section, BS6): rows are cut into consecutive blocks holding about
+ * nodes_per_block CSR entries each (never more, unless a single row is
+ * longer), so each thread block reads and writes about the same amount.
+ * block_starts receives n_blocks+1 row indices (capacity n_global+1 suffices),
+ * block_starts[0] = 0 and block_starts[n_blocks] = n_global. nodes_per_block
+ * must be in [1, 4096] (BS_EINVAL). */
+int bs_gather_plan(int64_t n_global, const int32_t *off, int nodes_per_block,
+                   int32_t *block_starts, int64_t *n_blocks);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BS_H */

@@ -1,0 +1,185 @@
+"""CPU tests of libbs: the exported C ABI, argument checks that fail before
+any HIP call, and the host-side tables against the oracle's independent
+builder (exact equality).
+
+The host tables follow "GPU accelerated spectral finite elements on all-hex
+meshes" (arXiv 1506.05996, local-to-global and global-to-local tables) and
+the blockStarts array of "Portable high-order finite element kernels I"
+(arXiv 2009.10917, implementation section, BS6).
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import bs_inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="session")
+def bs():
+    import cg_streaming_vector_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from cg_streaming_vector_amd import _build
+        _build.build()
+    m._lib()
+    return m
+
+
+def header_symbols():
+    src = open(os.path.join(ROOT, "include", "bs.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(bs_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol(bs):
+    syms = header_symbols()
+    assert len(syms) >= 17
+    L = ctypes.CDLL(bs.LIB_PATH)
+    for s in syms:
+        assert hasattr(L, s), s
+    # the binding declares exactly the header's entry points
+    assert sorted(bs.SIGNATURES) == syms
+
+
+def test_strerror_and_version(bs):
+    L = bs._lib()
+    assert L.bs_strerror(0) == b"ok"
+    for code in (-1, -2, -3, -4, -5):
+        assert L.bs_strerror(code) not in (b"ok", b"unknown status")
+    assert L.bs_strerror(-99) == b"unknown status"
+    assert L.bs_version() >= 100
+
+
+def test_null_context_is_einval_before_any_hip_call(bs):
+    L = bs._lib()
+    assert L.bs_copy(None, 10, None, None, None) == bs.BS_EINVAL
+    assert L.bs_axpy(None, 10, 1.0, None, 1.0, None, None) == bs.BS_EINVAL
+    assert L.bs_norm(None, 10, None, None, None) == bs.BS_EINVAL
+    assert L.bs_dot(None, 10, None, None, None, None) == bs.BS_EINVAL
+    assert L.bs_cg_update(None, 10, 1.0, None, None, None, None, None, None) == bs.BS_EINVAL
+    assert L.bs_scatter(None, 10, None, None, None, None) == bs.BS_EINVAL
+    assert L.bs_gather(None, 10, None, None, None, None, None, 0, None) == bs.BS_EINVAL
+    assert L.bs_ctx_create(0, None) == bs.BS_EINVAL
+    assert L.bs_ctx_info(None, None, None, None) == bs.BS_EINVAL
+    L.bs_ctx_destroy(None)
+
+
+# ------------------------------------------------------------- mesh sizes --
+
+def test_box_counts(bs):
+    assert bs.bs_mesh_box_count(8, 8, 8, 3) == (32768, 15625)
+    assert bs.bs_mesh_box_count(32, 32, 32, 7) == (16777216, 11390625)
+    assert bs.bs_mesh_box_count(40, 40, 40, 5) == (13824000, 8120601)
+    assert bs.bs_mesh_box_count(24, 24, 24, 15) == (56623104, 47045881)
+    assert bs.bs_mesh_box_count(3, 2, 1, 2) == (6 * 27, 7 * 5 * 3)
+    for bad in [(0, 1, 1, 1), (1, 1, 1, 0), (1, -2, 1, 3)]:
+        with pytest.raises(bs.BSError) as e:
+            bs.bs_mesh_box_count(*bad)
+        assert e.value.status == bs.BS_EINVAL
+    with pytest.raises(bs.BSError) as e:
+        bs.bs_mesh_box_count(1000, 1000, 1000, 7)
+    assert e.value.status == bs.BS_ERANGE
+
+
+# ------------------------------------------- tables against the oracle ----
+
+@pytest.mark.parametrize("dims,N", [((1, 1, 1), 1), ((2, 2, 2), 2), ((3, 2, 4), 3), ((8, 8, 8), 3),
+                                    ((5, 5, 5), 6), ((2, 3, 2), 15)])
+def test_box_l2g_matches_oracle(bs, orc, dims, N):
+    l2g = bs.bs_mesh_box_l2g(*dims, N)
+    ol2g, ng = orc.mesh_box(*dims, N)
+    assert np.array_equal(l2g, ol2g)
+    assert ng == bs.bs_mesh_box_count(*dims, N)[1]
+
+
+def test_box_shuffled_matches_oracle(bs, orc):
+    E, N = 6, 5
+    G = E * N + 1
+    ep = bs_inputs.permutation(71, E ** 3)
+    npm = bs_inputs.permutation(72, G ** 3)
+    l2g = bs.bs_mesh_box_l2g(E, E, E, N, ep, npm)
+    ol2g, _ = orc.mesh_box(E, E, E, N, ep, npm)
+    assert np.array_equal(l2g, ol2g)
+
+
+def test_box_rejects_non_permutations(bs):
+    ep = np.arange(8, dtype=np.int32)
+    ep[3] = 2
+    with pytest.raises(bs.BSError):
+        bs.bs_mesh_box_l2g(2, 2, 2, 1, ep, None)
+    npm = np.arange(27, dtype=np.int32)
+    npm[0] = 27
+    with pytest.raises(bs.BSError):
+        bs.bs_mesh_box_l2g(2, 2, 2, 1, None, npm)
+
+
+@pytest.mark.slow
+def test_full_size_tables_match_oracle(bs, orc):
+    """The 32^3 order-7 box and the shuffled 40^3 order-5 box, exactly."""
+    l2g = bs.bs_mesh_box_l2g(32, 32, 32, 7)
+    ol2g, ng = orc.mesh_box(32, 32, 32, 7)
+    assert np.array_equal(l2g, ol2g)
+    off, ids = bs.bs_index_g2l(l2g, ng)
+    ooff, oids = orc.g2l(ol2g, ng)
+    assert np.array_equal(off, ooff) and np.array_equal(ids, oids)
+    ep, npm = bs_inputs.mesh_perms("c4_shuffled40_N5", 40, 5)
+    l2g = bs.bs_mesh_box_l2g(40, 40, 40, 5, ep, npm)
+    ol2g, ng = orc.mesh_box(40, 40, 40, 5, ep, npm)
+    assert np.array_equal(l2g, ol2g)
+
+
+@pytest.mark.parametrize("masked", [False, True])
+def test_g2l_matches_oracle(bs, orc, masked):
+    E, N = 5, 4
+    ep = bs_inputs.permutation(73, E ** 3)
+    npm = bs_inputs.permutation(74, (E * N + 1) ** 3)
+    l2g, ng = orc.mesh_box(E, E, E, N, ep, npm)
+    if masked:
+        l2g = l2g.copy()
+        l2g[bs_inputs.splitmix64(75, l2g.size) % np.uint64(7) == 0] = -1
+    off, ids = bs.bs_index_g2l(l2g, ng)
+    ooff, oids = orc.g2l(l2g, ng)
+    assert np.array_equal(off, ooff)
+    assert np.array_equal(ids, oids)
+
+
+def test_g2l_rejects_out_of_range(bs):
+    l2g = np.array([0, 1, 5], dtype=np.int32)
+    with pytest.raises(bs.BSError):
+        bs.bs_index_g2l(l2g, 5)
+    with pytest.raises(bs.BSError):
+        bs.bs_validate_l2g(l2g, 5)
+    bs.bs_validate_l2g(l2g, 6)
+    bs.bs_validate_l2g(np.array([-1, 2], dtype=np.int32), 3)
+
+
+@pytest.mark.parametrize("npb", [1, 8, 256, 512, 2048, 4096])
+def test_gather_plan(bs, npb):
+    l2g = bs.bs_mesh_box_l2g(6, 5, 4, 3)
+    ng = bs.bs_mesh_box_count(6, 5, 4, 3)[1]
+    off, _ = bs.bs_index_g2l(l2g, ng)
+    plan = bs.bs_gather_plan(off, npb)
+    assert plan[0] == 0 and plan[-1] == ng
+    assert np.all(np.diff(plan) >= 1)
+    ent = off[plan[1:]] - off[plan[:-1]]
+    rows = np.diff(plan)
+    # never above the target unless the block is one long row
+    assert np.all((ent <= npb) | (rows == 1))
+    # greedy: adding the next row would have exceeded the target
+    nxt = off[np.minimum(plan[1:-1] + 1, ng)] - off[plan[:-2]]
+    assert np.all(nxt > npb)
+
+
+def test_gather_plan_long_rows(bs):
+    # one node with 10 entries, the rest single
+    off = np.array([0, 1, 11, 12, 13], dtype=np.int32)
+    plan = bs.bs_gather_plan(off, 4)
+    assert list(plan) == [0, 1, 2, 4]
+    with pytest.raises(bs.BSError):
+        bs.bs_gather_plan(off, 0)
+    with pytest.raises(bs.BSError):
+        bs.bs_gather_plan(off, 5000)

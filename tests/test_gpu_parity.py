@@ -1,0 +1,369 @@
+"""GPU parity: the HIP library against the CPU oracle on the same seeded inputs.
+
+Bar (arXiv 2009.10917 defines the operations; the tolerances are this
+library's contract): bit-exact for copy, AXPY, the fused update's x and r,
+scatter and both gather kernels; relative 1e-12 for norm, dot and the fused
+update's |r|^2. Sizes span several tiles with ragged tails, the empty and
+one-element cases, misaligned operands, and the full workloads: the 32^3
+order-7 box, the shuffled 40^3 order-5 box, the 24^3 order-15 box, and the
+2^10 .. 2^28 vector sweep, launched exactly as the benchmark launches them.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import bs_inputs
+
+pytestmark = pytest.mark.gpu
+
+RTOL = 1e-12
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    import cg_streaming_vector_amd as bs
+    import oracle
+    if not torch.cuda.is_available():
+        raise RuntimeError("GPU tests need a HIP device")
+    oracle.lib()
+    return bs, oracle, torch, torch.device("cuda:0")
+
+
+def dev(torch, device, a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def host(t):
+    return t.cpu().numpy()
+
+
+def assert_bits(got, want, what=""):
+    g = np.asarray(got, dtype=np.float64).view(np.uint64)
+    w = np.asarray(want, dtype=np.float64).view(np.uint64)
+    assert g.shape == w.shape, what
+    bad = np.nonzero(g != w)[0]
+    assert bad.size == 0, f"{what}: {bad.size} mismatches, first at {bad[:5]}"
+
+
+def assert_rel(got, want, what=""):
+    assert abs(got - want) <= RTOL * abs(want) or got == want, f"{what}: {got!r} vs {want!r}"
+
+
+# -------------------------------------------------------- vector ops ------
+
+SIZES = [1, 2, 3, 4, 5, 7, 8, 255, 256, 257, 1023, 1024, 1025, 4099, 65537, 262147, 1 << 20, (1 << 20) + 5,
+         3_000_001]
+
+
+def run_vector_ops(env, n, seed, offset=(0, 0, 0, 0)):
+    """All five vector ops at length n; offset[k] shifts operand k by elements
+    inside a larger buffer (to test 8- but not 16-byte aligned pointers)."""
+    bs, orc, torch, d = env
+    v = {k: bs_inputs.uniform_pm1(seed + i, n) for i, k in enumerate("xpqr")}
+
+    def place(a, o):
+        buf = torch.empty(n + 2, dtype=torch.float64, device=d)
+        t = buf[o:o + n]
+        t.copy_(torch.from_numpy(a))
+        return t
+
+    x, p, q, r = (place(v[k], offset[i]) for i, k in enumerate("xpqr"))
+    # copy
+    y = place(np.zeros(n), offset[1])
+    bs.bs_copy(x, y)
+    assert_bits(host(y), v["x"], f"copy n={n}")
+    # axpy with the benchmark's coefficients and a general pair
+    for a, b in [(0.37, 1.0), (-1.5, 0.25)]:
+        y = place(v["p"], offset[1])
+        bs.bs_axpy(a, x, b, y)
+        assert_bits(host(y), orc.axpy(a, v["x"], b, v["p"]), f"axpy n={n} a={a} b={b}")
+    # norm, dot
+    assert_rel(bs.bs_norm(x).item(), orc.norm(v["x"]), f"norm n={n}")
+    assert_rel(bs.bs_dot(x, p).item(), orc.dot(v["x"], v["p"]), f"dot n={n}")
+    # fused update
+    rr = bs.bs_cg_update(0.37, p, q, x, r).item()
+    ox, orr_, orr = orc.cg_update(0.37, v["p"], v["q"], v["x"], v["r"])
+    assert_bits(host(x), ox, f"cg x n={n}")
+    assert_bits(host(r), orr_, f"cg r n={n}")
+    assert_rel(rr, orr, f"cg rr n={n}")
+
+
+@pytest.mark.parametrize("n", SIZES)
+def test_vector_ops_sizes(env, n):
+    run_vector_ops(env, n, 100 + n % 97)
+
+
+@pytest.mark.parametrize("offset", [(1, 1, 1, 1), (1, 0, 1, 0), (0, 1, 1, 1), (1, 1, 0, 0)])
+@pytest.mark.parametrize("n", [1, 2, 9, 4097, 100_003])
+def test_vector_ops_alignment(env, n, offset):
+    run_vector_ops(env, n, 300, offset)
+
+
+def test_vector_ops_empty(env):
+    bs, orc, torch, d = env
+    e = torch.empty(0, dtype=torch.float64, device=d)
+    out = torch.full((1,), 7.0, dtype=torch.float64, device=d)
+    bs.bs_copy(e, e)
+    bs.bs_axpy(1.0, e, 1.0, e)
+    assert bs.bs_norm(e, out).item() == 0.0
+    out.fill_(7.0)
+    assert bs.bs_dot(e, e, out).item() == 0.0
+    out.fill_(7.0)
+    assert bs.bs_cg_update(0.5, e, e, e, e, out).item() == 0.0
+    assert not math.copysign(1.0, out.item()) < 0
+
+
+def test_copy_special_values(env):
+    bs, orc, torch, d = env
+    raw = np.array([0x7FF8_0000_DEAD_BEEF, 0x8000_0000_0000_0000, 0x7FF0_0000_0000_0000, 1, 0xFFF4_0000_0000_0001],
+                   dtype=np.uint64)
+    a = np.tile(raw, 1001).view(np.float64)
+    y = torch.empty(a.size, dtype=torch.float64, device=d)
+    bs.bs_copy(dev(torch, d, a), y)
+    assert host(y).tobytes() == a.tobytes()
+
+
+def test_axpy_beta_zero_reads_y(env):
+    bs, orc, torch, d = env
+    n = 5000
+    x = bs_inputs.uniform_pm1(5, n)
+    yv = bs_inputs.uniform_pm1(6, n)
+    yv[[0, 17, 4999]] = [np.inf, np.nan, -np.inf]
+    y = dev(torch, d, yv)
+    bs.bs_axpy(2.0, dev(torch, d, x), 0.0, y)
+    assert_bits(host(y), orc.axpy(2.0, x, 0.0, yv), "axpy beta=0")
+
+
+def test_reductions_integer_data_bit_exact(env):
+    """Integer-valued data sum exactly in any order: the GPU must match bits."""
+    bs, orc, torch, d = env
+    n = 5_000_011
+    x = bs_inputs.small_ints(7, n, -30, 30)
+    y = bs_inputs.small_ints(8, n, -30, 30)
+    assert bs.bs_dot(dev(torch, d, x), dev(torch, d, y)).item() == float(
+        np.dot(x.astype(np.int64), y.astype(np.int64)))
+    s = int(np.dot(x.astype(np.int64), x.astype(np.int64)))
+    assert bs.bs_norm(dev(torch, d, x)).item() == math.sqrt(s)
+    assert bs.bs_norm(dev(torch, d, np.ones(1 << 22))).item() == 2048.0
+
+
+def test_reductions_deterministic(env):
+    bs, orc, torch, d = env
+    n = 11_390_625
+    x = dev(torch, d, bs_inputs.uniform_pm1(9, n))
+    y = dev(torch, d, bs_inputs.uniform_pm1(10, n))
+    a = [bs.bs_dot(x, y).item() for _ in range(3)]
+    b = [bs.bs_norm(x).item() for _ in range(3)]
+    assert len(set(a)) == 1 and len(set(b)) == 1
+
+
+@pytest.mark.parametrize("k", list(range(10, 29)))
+def test_sweep_sizes(env, k):
+    """The 2^10 .. 2^28 sweep: every op, whole vectors against the oracle."""
+    bs, orc, torch, d = env
+    n = 1 << k
+    name = "c3_sweep"
+    v = bs_inputs.vectors(name, n, "xpqr")
+    x, p, q, r = (dev(torch, d, v[c]) for c in "xpqr")
+    y = torch.empty_like(x)
+    bs.bs_copy(x, y)
+    assert torch.equal(y, x)
+    del y
+    assert_rel(bs.bs_norm(x).item(), orc.norm(v["x"]), f"norm 2^{k}")
+    assert_rel(bs.bs_dot(x, p).item(), orc.dot(v["x"], v["p"]), f"dot 2^{k}")
+    rr = bs.bs_cg_update(0.37, p, q, x, r).item()
+    ox, orr_, orr = orc.cg_update(0.37, v["p"], v["q"], v["x"], v["r"])
+    assert_bits(host(x), ox, f"cg x 2^{k}")
+    assert_bits(host(r), orr_, f"cg r 2^{k}")
+    assert_rel(rr, orr, f"cg rr 2^{k}")
+    bs.bs_axpy(0.37, p, 1.0, q)
+    assert_bits(host(q), orc.axpy(0.37, v["p"], 1.0, v["q"]), f"axpy 2^{k}")
+
+
+# ----------------------------------------------------- scatter / gather ----
+
+MESHES = {
+    "c1_box8_N3": (8, 3),
+    "c2_box32_N7": (32, 7),
+    "c4_shuffled40_N5": (40, 5),
+    "c5_box24_N15": (24, 15),
+}
+
+
+def mesh_case(env, name):
+    bs, orc, torch, d = env
+    E, N = MESHES[name]
+    ep, npm = bs_inputs.mesh_perms(name, E, N)
+    l2g = bs.bs_mesh_box_l2g(E, E, E, N, ep, npm)
+    ng = bs.bs_mesh_box_count(E, E, E, N)[1]
+    off, ids = bs.bs_index_g2l(l2g, ng)
+    ol2g, ong = orc.mesh_box(E, E, E, N, ep, npm)
+    assert ong == ng
+    return l2g, off, ids, ol2g, ng
+
+
+@pytest.mark.parametrize("name", list(MESHES))
+def test_scatter_gather_mesh(env, name):
+    bs, orc, torch, d = env
+    l2g, off, ids, ol2g, ng = mesh_case(env, name)
+    nl = l2g.size
+    b = bs_inputs.base_seed(name)
+    vgv = bs_inputs.uniform_pm1(b + 1, ng)
+    vlv = bs_inputs.uniform_pm1(b + 9, nl)
+    # scatter
+    vl = torch.empty(nl, dtype=torch.float64, device=d)
+    bs.bs_scatter(dev(torch, d, l2g), dev(torch, d, vgv), vl)
+    assert_bits(host(vl), orc.scatter(ol2g, vgv), f"scatter {name}")
+    # gather, both kernels
+    want = orc.gather(ol2g, vlv, ng)
+    doff, dids, dvl = dev(torch, d, off), dev(torch, d, ids), dev(torch, d, vlv)
+    vg = torch.full((ng,), np.nan, dtype=torch.float64, device=d)
+    bs.bs_gather(doff, dids, dvl, vg)
+    assert_bits(host(vg), want, f"gather rows {name}")
+    for npb in (512, 2048, 4096):
+        plan = bs.bs_gather_plan(off, npb)
+        vg.fill_(np.nan)
+        bs.bs_gather(doff, dids, dvl, vg, dev(torch, d, plan))
+        assert_bits(host(vg), want, f"gather lds {name} npb={npb}")
+
+
+def test_gather_multiplicity_and_identity(env):
+    """gather(1_L) is the node multiplicity; scatter(g) returns l2g."""
+    bs, orc, torch, d = env
+    l2g, off, ids, ol2g, ng = mesh_case(env, "c2_box32_N7")
+    m = np.diff(off).astype(np.float64)
+    vg = torch.empty(ng, dtype=torch.float64, device=d)
+    bs.bs_gather(dev(torch, d, off), dev(torch, d, ids), torch.ones(l2g.size, dtype=torch.float64, device=d), vg)
+    assert_bits(host(vg), m, "gather(ones)")
+    vl = torch.empty(l2g.size, dtype=torch.float64, device=d)
+    bs.bs_scatter(dev(torch, d, l2g), torch.arange(ng, dtype=torch.float64, device=d), vl)
+    assert_bits(host(vl), l2g.astype(np.float64), "scatter(arange)")
+
+
+def test_masked_scatter_gather(env):
+    bs, orc, torch, d = env
+    E, N = 6, 4
+    l2g = bs.bs_mesh_box_l2g(E, E, E, N).copy()
+    ng = bs.bs_mesh_box_count(E, E, E, N)[1]
+    ol2g, _ = orc.mesh_box(E, E, E, N)
+    mask = bs_inputs.splitmix64(77, l2g.size) % np.uint64(5) == 0
+    l2g[mask] = -1
+    ol2g = ol2g.copy()
+    ol2g[mask] = -3
+    off, ids = bs.bs_index_g2l(l2g, ng)
+    vgv = bs_inputs.uniform_pm1(78, ng)
+    vl = torch.full((l2g.size,), np.nan, dtype=torch.float64, device=d)
+    bs.bs_scatter(dev(torch, d, l2g), dev(torch, d, vgv), vl)
+    got = host(vl)
+    assert_bits(got, orc.scatter(ol2g, vgv), "masked scatter")
+    assert not np.any(np.signbit(got[mask]))
+    vlv = bs_inputs.uniform_pm1(79, l2g.size)
+    want = orc.gather(ol2g, vlv, ng)
+    for plan in (None, bs.bs_gather_plan(off, 1024)):
+        vg = torch.full((ng,), np.nan, dtype=torch.float64, device=d)
+        bs.bs_gather(dev(torch, d, off), dev(torch, d, ids), dev(torch, d, vlv), vg,
+                     None if plan is None else dev(torch, d, plan))
+        assert_bits(host(vg), want, "masked gather")
+
+
+def test_gather_order_and_signed_zero(env):
+    """Ascending local order from +0.0: (2^53, 1, 1, -2^53) sums to 0 (ties to
+    even twice), rows of -0.0 give +0.0, empty rows give +0.0."""
+    bs, orc, torch, d = env
+    l2g = np.array([0, 2, 0, 2, 0, 0, 3, 3], dtype=np.int32)
+    vlv = np.array([2.0 ** 53, -0.0, 1.0, -0.0, 1.0, -2.0 ** 53, 5.0, -5.0])
+    ng = 5
+    off, ids = bs.bs_index_g2l(l2g, ng)
+    want = orc.gather(l2g, vlv, ng)
+    assert list(want) == [0.0, 0.0, 0.0, 0.0, 0.0]
+    for plan in (None, bs.bs_gather_plan(off, 3), bs.bs_gather_plan(off, 4096)):
+        vg = torch.full((ng,), np.nan, dtype=torch.float64, device=d)
+        bs.bs_gather(dev(torch, d, off), dev(torch, d, ids), dev(torch, d, vlv), vg,
+                     None if plan is None else dev(torch, d, plan))
+        assert_bits(host(vg), want, "order witness")
+
+
+def test_gather_long_row_fallback(env):
+    """A node with more entries than the LDS stage holds takes the direct path."""
+    bs, orc, torch, d = env
+    nl = 10_000
+    l2g = np.zeros(nl, dtype=np.int32)
+    l2g[::3] = 1
+    l2g[1::7] = 2
+    ng = 3
+    vlv = bs_inputs.uniform_pm1(80, nl)
+    off, ids = bs.bs_index_g2l(l2g, ng)
+    want = orc.gather(l2g, vlv, ng)
+    for plan in (None, bs.bs_gather_plan(off, 4096), bs.bs_gather_plan(off, 1)):
+        vg = torch.empty(ng, dtype=torch.float64, device=d)
+        bs.bs_gather(dev(torch, d, off), dev(torch, d, ids), dev(torch, d, vlv), vg,
+                     None if plan is None else dev(torch, d, plan))
+        assert_bits(host(vg), want, "long rows")
+
+
+def test_scatter_ragged_and_misaligned(env):
+    bs, orc, torch, d = env
+    for nl in [1, 3, 5, 1023, 1025, 4097]:
+        ng = 50
+        l2g = (bs_inputs.splitmix64(81, nl) % np.uint64(ng)).astype(np.int32)
+        vgv = bs_inputs.uniform_pm1(82, ng)
+        want = orc.scatter(l2g, vgv)
+        for o in (0, 1):
+            ibuf = torch.zeros(nl + 4, dtype=torch.int32, device=d)
+            ibuf[o:o + nl] = dev(torch, d, l2g)
+            obuf = torch.zeros(nl + 4, dtype=torch.float64, device=d)
+            bs.bs_scatter(ibuf[o:o + nl], dev(torch, d, vgv), obuf[o:o + nl])
+            assert_bits(host(obuf[o:o + nl]), want, f"scatter nl={nl} o={o}")
+
+
+def test_errors_enqueue_nothing(env):
+    bs, orc, torch, d = env
+    L, h = bs._lib(), bs.context().handle
+    x = torch.zeros(10, dtype=torch.float64, device=d)
+    raw = x.data_ptr()
+    assert L.bs_copy(h, -1, raw, raw, None) == bs.BS_EINVAL
+    assert L.bs_copy(h, 4, raw + 4, raw, None) == bs.BS_EALIGN
+    assert L.bs_axpy(h, 4, 1.0, raw, 1.0, None, None) == bs.BS_EINVAL
+    assert L.bs_scatter(h, 1 << 31, raw, raw, raw, None) == bs.BS_ERANGE
+    assert L.bs_dot(h, 4, raw, raw, None, None) == bs.BS_EINVAL
+    assert L.bs_gather(h, 4, raw, raw, raw, raw, raw, 0, None) == bs.BS_EINVAL
+    with pytest.raises(TypeError):
+        bs.bs_copy(x.float(), x.float())
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(x).item() == 0
+
+
+# ------------------------------------------------- CG streaming sequence ----
+
+def test_cg_sequence_matches_oracle(env):
+    """Four CG iterations on Z^T Z through the library vs the oracle."""
+    bs, orc, torch, d = env
+    E, N = 8, 3
+    l2g = bs.bs_mesh_box_l2g(E, E, E, N)
+    ng = bs.bs_mesh_box_count(E, E, E, N)[1]
+    off, ids = bs.bs_index_g2l(l2g, ng)
+    ol2g, _ = orc.mesh_box(E, E, E, N)
+    b = bs_inputs.uniform_pm1(1001, ng)
+    ox, orr_, ohist = orc.cg_sequence(ol2g, ng, b, 4)
+    dl2g, doff, dids = dev(torch, d, l2g), dev(torch, d, off), dev(torch, d, ids)
+    x = torch.zeros(ng, dtype=torch.float64, device=d)
+    r = dev(torch, d, b)
+    p = dev(torch, d, b)
+    q = torch.empty_like(p)
+    pl = torch.empty(l2g.size, dtype=torch.float64, device=d)
+    rr = bs.bs_dot(r, r).item()
+    hist = [rr]
+    for _ in range(4):
+        bs.bs_scatter(dl2g, p, pl)
+        bs.bs_gather(doff, dids, pl, q)
+        alpha = rr / bs.bs_dot(p, q).item()
+        rr_new = bs.bs_cg_update(alpha, p, q, x, r).item()
+        bs.bs_axpy(1.0, r, rr_new / rr, p)
+        rr = rr_new
+        hist.append(rr)
+    for h, oh in zip(hist[:2], ohist[:2]):
+        assert_rel(h, oh, "rr")
+    assert math.sqrt(hist[-1] / hist[0]) < 1e-13
+    assert np.allclose(host(x), ox, rtol=1e-12, atol=1e-14)
