@@ -1,0 +1,464 @@
+"""Benchmark of the seven Benchmark Streaming (BS) operations on one MI355X.
+
+One step is one pass of the whole path over the 32^3-element, order-7 box
+mesh (N_G = 11,390,625 global nodes, N_L = 16,777,216 local entries), fp64:
+BS1 copy, BS2 AXPY (alpha 0.37, beta 1), BS3 norm, BS4 dot and BS5 fused CG
+update on global-length vectors, BS7 scatter through I_l->g and BS6 gather
+through the CSR form of I_g->l. Each operation works on arrays of its own,
+so between two touches of the same array the step streams ~1.6 GB through
+the 256 MB last-level cache: every operation reads cold data from HBM.
+
+The figure of merit is effective bandwidth, algorithmic bytes over time
+("Portable high-order finite element kernels I", arXiv 2009.10917, where
+time is taken on the host around the launches). Algorithmic bytes per
+operation count every array once, index tables included:
+  copy 16n, AXPY 24n, norm 8n, dot 16n, fused update 48n,
+  scatter 12 N_L + 8 N_G, gather 12 N_L + 12 N_G + 4.
+
+Printed: one JSON line (value = bytes of a step / host-timed seconds of a
+step, whole job), with per-operation times from HIP events recorded on the
+launch stream during the same timed steps, the roofline of the dominant
+kernel, and the CPU oracle timed on a bounded sample of the same step.
+Optional: --sweep fits the latency-plus-bandwidth model T(B) = T0 + B/W_max
+(eq. 8) over n = 2^10 .. 2^28 and reports B_0.8 = 4 T0 W_max (eq. 10);
+--workloads times the shuffled 40^3 order-5 and 24^3 order-15 meshes and
+the CG streaming sequence. Their results go to --out (JSON), not stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import bs_inputs  # noqa: E402
+
+PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+METRIC = "effective GB/s and % of HBM peak per BS op (fp64, N=7 hex mesh, 1 GPU)"
+OPS = ["copy", "axpy", "norm", "dot", "cg_update", "scatter", "gather"]
+KERNEL_NAME = {  # op -> first-stage kernel as rocprofv3 names it (namespace and arguments stripped)
+    "copy": "k_copy<1>", "axpy": "k_axpy<1>", "norm": "k_dot<2, true>", "dot": "k_dot<2, false>",
+    "cg_update": "k_cg_update<4>", "scatter": "k_scatter", "gather": "k_gather_plan",
+}
+GATHER_NPB = 1024
+
+
+def op_bytes(op, n=0, nl=0, ng=0):
+    return {
+        "copy": 16 * n, "axpy": 24 * n, "norm": 8 * n, "dot": 16 * n, "cg_update": 48 * n,
+        "scatter": 12 * nl + 8 * ng, "gather": 12 * nl + 12 * ng + 4,
+    }[op]
+
+
+def kernel_source_sha():
+    path = os.path.join(ROOT, "cg_streaming_vector_amd", "csrc", "bs_kernels.hip")
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+class Mesh:
+    """Device tables and vectors of one mesh workload, one set per operation."""
+
+    def __init__(self, bs, torch, dev, name, E, N, gather_lds):
+        ep, npm = bs_inputs.mesh_perms(name, E, N)
+        self.name, self.E, self.N = name, E, N
+        self.nl, self.ng = bs.bs_mesh_box_count(E, E, E, N)
+        l2g = bs.bs_mesh_box_l2g(E, E, E, N, ep, npm)
+        off, ids = bs.bs_index_g2l(l2g, self.ng)
+        plan = bs.bs_gather_plan(off, GATHER_NPB)
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+        f64 = lambda n: torch.empty(n, dtype=torch.float64, device=dev)  # noqa: E731
+        v = bs_inputs.vectors(name, self.ng)
+        b = bs_inputs.base_seed(name)
+        self.l2g, self.off, self.ids, self.plan = t(l2g), t(off), t(ids), t(plan)
+        self.gather_lds = gather_lds
+        n = self.ng
+        # per-operation arrays (distinct, so no operation finds another's data in cache)
+        self.copy_x, self.copy_y = t(v["x"]), f64(n)
+        self.axpy_x, self.axpy_y = t(v["p"]), t(v["y"])
+        self.norm_x = t(v["q"])
+        self.dot_x, self.dot_y = t(v["r"]), t(v["x"])
+        self.cg_p, self.cg_q, self.cg_x, self.cg_r = t(v["p"]), t(v["q"]), t(v["x"]), t(v["r"])
+        self.sc_vg, self.sc_vl = t(v["y"]), f64(self.nl)
+        self.ga_vl, self.ga_vg = t(bs_inputs.uniform_pm1(b + 9, self.nl)), f64(n)
+        self.out = torch.zeros(4, dtype=torch.float64, device=dev)
+        del v
+
+    DEVICE_ARRAYS = ["l2g", "off", "ids", "plan", "copy_x", "copy_y", "axpy_x", "axpy_y", "norm_x", "dot_x",
+                     "dot_y", "cg_p", "cg_q", "cg_x", "cg_r", "sc_vg", "sc_vl", "ga_vl", "ga_vg", "out"]
+
+    def clone(self):
+        """Another set of the same device arrays (fresh memory, same values)."""
+        m = object.__new__(Mesh)
+        m.__dict__.update({k: v for k, v in self.__dict__.items() if k not in self.DEVICE_ARRAYS})
+        for k in self.DEVICE_ARRAYS:
+            setattr(m, k, getattr(self, k).clone())
+        return m
+
+    def launchers(self, bs, stream):
+        """op -> zero-argument callable issuing that op through the C ABI."""
+        L, h = bs._lib(), bs.context().handle
+        n, nl, ng = self.ng, self.nl, self.ng
+        P = lambda t: t.data_ptr()  # noqa: E731
+        o = P(self.out)
+        plan = P(self.plan) if self.gather_lds else None
+        nb = self.plan.numel() - 1 if self.gather_lds else 0
+        a = dict(
+            copy=(L.bs_copy, (h, n, P(self.copy_x), P(self.copy_y), stream)),
+            axpy=(L.bs_axpy, (h, n, 0.37, P(self.axpy_x), 1.0, P(self.axpy_y), stream)),
+            norm=(L.bs_norm, (h, n, P(self.norm_x), o, stream)),
+            dot=(L.bs_dot, (h, n, P(self.dot_x), P(self.dot_y), o + 8, stream)),
+            cg_update=(L.bs_cg_update, (h, n, 0.37, P(self.cg_p), P(self.cg_q), P(self.cg_x), P(self.cg_r),
+                                        o + 16, stream)),
+            scatter=(L.bs_scatter, (h, nl, P(self.l2g), P(self.sc_vg), P(self.sc_vl), stream)),
+            gather=(L.bs_gather, (h, ng, P(self.off), P(self.ids), P(self.ga_vl), P(self.ga_vg), plan, nb,
+                                  stream)),
+        )
+
+        def mk(fn, args, op):
+            def call():
+                s = fn(*args)
+                if s != 0:
+                    raise RuntimeError(f"bs_{op} returned {s}")
+            return call
+        return {op: mk(fn, args, op) for op, (fn, args) in a.items()}
+
+    def bytes(self, op):
+        return op_bytes(op, self.ng, self.nl, self.ng)
+
+
+def time_ops_rotated(torch, sets_launch, ops, reps):
+    """Average time per launch of each op, launched `reps` times back to back,
+    cycling through the arrays of len(sets_launch) distinct sets so that no
+    launch finds its operands in cache; HIP events on the launch stream
+    bracket each op's loop."""
+    stream = torch.cuda.current_stream()
+    R = len(sets_launch)
+    out = {}
+    for op in ops:
+        for i in range(R):
+            sets_launch[i][op]()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            sets_launch[i % R][op]()
+        e1.record(stream)
+        e1.synchronize()
+        out[op] = e0.elapsed_time(e1) * 1e-3 / reps
+    return out
+
+
+def traffic_for(kernel, launches_bytes):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if the
+    kernel source has not changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic_c2.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except ValueError:
+        return None
+    if d.get("kernel_source_sha256") != kernel_source_sha():
+        return None
+    k = d.get("kernels", {}).get(kernel)
+    if not k:
+        return None
+    return float(k["hbm_bytes_per_launch"])
+
+
+def cpu_baseline(mesh_host, budget_s=12.0):
+    """The oracle, as it stands, on the same step (host arrays), repeated
+    until about budget_s seconds; returns GB/s over the algorithmic bytes."""
+    import oracle
+    h = mesh_host
+    n = h["ng"]
+    nb = sum(op_bytes(op, n, h["nl"], n) for op in OPS)
+    reps, t = 0, 0.0
+    while t < budget_s and reps < 1000:
+        t0 = time.perf_counter()
+        oracle.copy(h["x"])
+        oracle.axpy(0.37, h["p"], 1.0, h["y"])
+        oracle.norm(h["q"])
+        oracle.dot(h["r"], h["x"])
+        oracle.cg_update(0.37, h["p"], h["q"], h["x"], h["r"])
+        oracle.scatter(h["l2g"], h["y"])
+        oracle.gather(h["l2g"], h["vl"], n)
+        t += time.perf_counter() - t0
+        reps += 1
+    return {"value": round(nb * reps / t / 1e9, 3), "unit": "GB/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"{reps} full step(s) of the 32^3 order-7 mesh (all 7 ops, oracle tables), "
+                      f"{t:.1f} s of CPU time"}
+
+
+def sweep(bs, torch, dev, reps_min=50):
+    """c3: each vector op over n = 2^10 .. 2^28, fitted to T(B) = T0 + B/W_max."""
+    L, h = bs._lib(), bs.context().handle
+    stream = torch.cuda.current_stream().cuda_stream
+    res = {op: [] for op in ["copy", "axpy", "norm", "dot", "cg_update"]}
+    for k in range(10, 29):
+        n = 1 << k
+        per = 48 * n
+        R = max(2, int(np.ceil(2 ** 30 / per)))  # rotate sets: >= 1 GiB of footprint
+        R = min(R, 64)
+        sets = [[torch.empty(n, dtype=torch.float64, device=dev).uniform_(-1, 1) for _ in range(4)]
+                for _ in range(R)]
+        out = torch.zeros(4, dtype=torch.float64, device=dev)
+        o = out.data_ptr()
+        for op in res:
+            def one(i):
+                a, b, c, d = (t.data_ptr() for t in sets[i % R])
+                if op == "copy":
+                    return L.bs_copy(h, n, a, b, stream)
+                if op == "axpy":
+                    return L.bs_axpy(h, n, 0.37, a, 1.0, b, stream)
+                if op == "norm":
+                    return L.bs_norm(h, n, a, o, stream)
+                if op == "dot":
+                    return L.bs_dot(h, n, a, b, o, stream)
+                return L.bs_cg_update(h, n, 0.37, a, b, c, d, o, stream)
+            reps = max(reps_min, R)
+            for i in range(min(reps, 8)):
+                one(i)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(reps):
+                if one(i) != 0:
+                    raise RuntimeError(op)
+            torch.cuda.synchronize()
+            T = (time.perf_counter() - t0) / reps
+            res[op].append((op_bytes(op, n), T))
+        del sets
+        torch.cuda.empty_cache()
+    from cg_streaming_vector_amd.model import fit_streaming_model
+    out = {}
+    for op, pts in res.items():
+        B = np.array([p[0] for p in pts], dtype=np.float64)
+        T = np.array([p[1] for p in pts], dtype=np.float64)
+        f = fit_streaming_model(B, T)
+        out[op] = {"points": [[int(b), t] for b, t in pts], **f}
+    return out
+
+
+def workloads(bs, torch, dev, gather_lds, steps=30):
+    """The shuffled 40^3 order-5 mesh (scatter, gather) and the 24^3 order-15
+    mesh (all 7 ops, and the CG streaming sequence)."""
+    out = {}
+    for name, E, N, ops in [("c4_shuffled40_N5", 40, 5, ["scatter", "gather"]),
+                            ("c5_box24_N15", 24, 15, OPS)]:
+        m = Mesh(bs, torch, dev, name, E, N, gather_lds)
+        stream = torch.cuda.current_stream().cuda_stream
+        R = 3 if name.startswith("c5") else 5
+        sets = [m] + [m.clone() for _ in range(R - 1)]
+        per_op = time_ops_rotated(torch, [x.launchers(bs, stream) for x in sets], ops, 3 * R)
+        del sets
+        res = {op: {"bytes": m.bytes(op), "us": round(per_op[op] * 1e6, 2),
+                    "GBps": round(m.bytes(op) / per_op[op] / 1e9, 1),
+                    "pct_peak": round(100 * m.bytes(op) / per_op[op] / 1e9 / PEAK_GBPS, 1)} for op in ops}
+        out[name] = res
+        if name == "c5_box24_N15":
+            out["cg_sequence_c5"] = cg_sequence(bs, torch, dev, m)
+        del m
+        torch.cuda.empty_cache()
+    return out
+
+
+def cg_sequence(bs, torch, dev, m, iters=100):
+    """CG-iteration streaming sequence on Z^T Z: scatter, gather, dot, fused
+    update, AXPY. (i) fixed scalars, no readback, `iters` iterations; (ii) true
+    CG, 4 iterations, reading alpha and beta back to the host."""
+    L, h = bs._lib(), bs.context().handle
+    st = torch.cuda.current_stream().cuda_stream
+    ng, nl = m.ng, m.nl
+    P = lambda t: t.data_ptr()  # noqa: E731
+    b = m.cg_r
+    x, r, p = torch.zeros_like(b), b.clone(), b.clone()
+    q, pl = torch.empty_like(b), m.sc_vl
+    o = torch.zeros(2, dtype=torch.float64, device=dev)
+    plan = P(m.plan) if m.gather_lds else None
+    nb = m.plan.numel() - 1 if m.gather_lds else 0
+
+    def it(alpha, beta):
+        assert L.bs_scatter(h, nl, P(m.l2g), P(p), P(pl), st) == 0
+        assert L.bs_gather(h, ng, P(m.off), P(m.ids), P(pl), P(q), plan, nb, st) == 0
+        assert L.bs_dot(h, ng, P(p), P(q), P(o), st) == 0
+        assert L.bs_cg_update(h, ng, alpha, P(p), P(q), P(x), P(r), P(o) + 8, st) == 0
+        assert L.bs_axpy(h, ng, 1.0, P(r), beta, P(p), st) == 0
+
+    per_iter = 24 * nl + 108 * ng
+    for _ in range(3):
+        it(1e-3, 0.5)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(iters):
+        it(1e-3, 0.5)
+    torch.cuda.synchronize()
+    T = (time.perf_counter() - t0) / iters
+    # true CG with readbacks
+    x.zero_()
+    r.copy_(b)
+    p.copy_(b)
+    assert L.bs_dot(h, ng, P(r), P(r), P(o) + 8, st) == 0
+    rr0 = rr = o[1].item()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(4):
+        assert L.bs_scatter(h, nl, P(m.l2g), P(p), P(pl), st) == 0
+        assert L.bs_gather(h, ng, P(m.off), P(m.ids), P(pl), P(q), plan, nb, st) == 0
+        assert L.bs_dot(h, ng, P(p), P(q), P(o), st) == 0
+        alpha = rr / o[0].item()
+        assert L.bs_cg_update(h, ng, alpha, P(p), P(q), P(x), P(r), P(o) + 8, st) == 0
+        rr_new = o[1].item()
+        assert L.bs_axpy(h, ng, 1.0, P(r), rr_new / rr, P(p), st) == 0
+        rr = rr_new
+    torch.cuda.synchronize()
+    Tcg = (time.perf_counter() - t0) / 4
+    return {"bytes_per_iter": per_iter, "fixed_scalars_us_per_iter": round(T * 1e6, 1),
+            "fixed_scalars_GBps": round(per_iter / T / 1e9, 1),
+            "true_cg_us_per_iter": round(Tcg * 1e6, 1), "true_cg_GBps": round(per_iter / Tcg / 1e9, 1),
+            "true_cg_rel_residual_after_4": float(np.sqrt(rr / rr0))}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--gather", choices=["rows", "lds"], default="lds")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rotate", type=int, default=12, help="array sets cycled in the per-op loops")
+    ap.add_argument("--per-op-reps", type=int, default=96)
+    ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--workloads", action="store_true")
+    ap.add_argument("--out", default=None)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the BS operations here run on a single MI355X; "
+              "how they would shard is described in the design notes. Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import cg_streaming_vector_amd as bs
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a HIP device")
+    dev = torch.device("cuda:0")
+    bs._lib()
+    ctx = bs.context(0)
+
+    name, E, N = "c2_box32_N7", 32, 7
+    mesh = Mesh(bs, torch, dev, name, E, N, gather_lds=(args.gather == "lds"))
+    stream = torch.cuda.current_stream().cuda_stream
+    launch = mesh.launchers(bs, stream)
+    step_bytes = sum(mesh.bytes(op) for op in OPS)
+
+    # per operation: back-to-back launches over ROT sets of distinct arrays
+    # (ROT x the smallest operation's bytes > 1 GB, beyond the 256 MB cache)
+    sets = [mesh] + [mesh.clone() for _ in range(args.rotate - 1)]
+    sets_launch = [m.launchers(bs, stream) for m in sets]
+    per_op = time_ops_rotated(torch, sets_launch, OPS, args.per_op_reps)
+    dom = max(OPS, key=lambda op: per_op[op])
+    del sets_launch, sets
+    torch.cuda.empty_cache()
+
+    # timed region: host clock around K steps; HIP events on the launch
+    # stream around the dominant kernel in every step
+    for _ in range(args.warmup):
+        for op in OPS:
+            launch[op]()
+    torch.cuda.synchronize()
+    cur = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        for op in OPS:
+            if op == dom:
+                ev[k][0].record(cur)
+            launch[op]()
+            if op == dom:
+                ev[k][1].record(cur)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    dom_live = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    ms_step = dt / args.steps * 1e3
+    value = step_bytes / (dt / args.steps) / 1e9
+
+    ops_out = {}
+    for op in OPS:
+        t = per_op[op]
+        gbps = mesh.bytes(op) / t / 1e9
+        ops_out[op] = {"bytes": mesh.bytes(op), "us": round(t * 1e6, 2), "GBps": round(gbps, 1),
+                       "pct_peak": round(100 * gbps / PEAK_GBPS, 1)}
+    achieved = mesh.bytes(dom) / dom_live / 1e9
+    traffic = traffic_for(KERNEL_NAME[dom], mesh.bytes(dom))
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
+                "kernel": KERNEL_NAME[dom], "bytes_per_launch": mesh.bytes(dom),
+                "us_per_launch": round(dom_live * 1e6, 2)}
+
+    # the runtime's own device-to-device copy at this size, on rotated buffers
+    R = args.rotate
+    src = [mesh.copy_x.clone() for _ in range(R)]
+    dst = [torch.empty_like(mesh.copy_x) for _ in range(R)]
+    for i in range(R):
+        dst[i].copy_(src[i])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(cur)
+    for i in range(args.per_op_reps):
+        dst[i % R].copy_(src[i % R])
+    e1.record(cur)
+    e1.synchronize()
+    rt_copy = 16 * mesh.ng / (e0.elapsed_time(e1) * 1e-3 / args.per_op_reps) / 1e9
+    del src, dst
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64",
+        "data": "synthetic (seeded SplitMix64 uniform[-1,1) vectors, structured box mesh)",
+        "config": {"workload": "box mesh 32^3 elements, order N=7, lexicographic numbering; "
+                               "all 7 BS ops per step", "elements": E ** 3, "order": N,
+                   "n_global": mesh.ng, "n_local": mesh.nl, "step_bytes": step_bytes,
+                   "gather_kernel": args.gather, "cu_count": ctx.info()["cu_count"]},
+        "pct_peak": round(100 * value / PEAK_GBPS, 1),
+        "per_op": ops_out,
+        "runtime_copy_GBps": round(rt_copy, 1),
+        "roofline": roofline,
+    }
+
+    extra = {}
+    if args.sweep:
+        extra["sweep"] = sweep(bs, torch, dev)
+    if args.workloads:
+        del launch
+        extra["workloads"] = workloads(bs, torch, dev, args.gather == "lds")
+
+    if not args.no_cpu_baseline:
+        import oracle
+        del launch
+        host = {"ng": mesh.ng, "nl": mesh.nl}
+        v = bs_inputs.vectors(name, mesh.ng)
+        host.update(v)
+        ol2g, _ = oracle.mesh_box(E, E, E, N)
+        host["l2g"] = ol2g
+        host["vl"] = bs_inputs.uniform_pm1(bs_inputs.base_seed(name) + 9, mesh.nl)
+        line["cpu_baseline"] = cpu_baseline(host)
+    else:
+        line["cpu_baseline"] = None
+
+    if args.out:
+        with open(args.out, "w") as f:
+            json.dump({"bench": line, **extra}, f, indent=1)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

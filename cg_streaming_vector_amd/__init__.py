@@ -307,7 +307,7 @@ def bs_index_g2l(l2g, n_global):
     return off, ids[:int(off[-1])]
 
 
-def bs_gather_plan(off, nodes_per_block=2048):
+def bs_gather_plan(off, nodes_per_block=1024):
     """blockStarts for the LDS-staged gather (int32 numpy array)."""
     off = _host_i32(off, "off")
     ng = off.size - 1

@@ -114,17 +114,19 @@ int bs_gather_plan(int64_t n_global, const int32_t *off, int nodes_per_block, in
                    int64_t *n_blocks)
 {
     if (n_global < 0 || !off || !block_starts || !n_blocks) return BS_EINVAL;
-    if (nodes_per_block < 1 || nodes_per_block > 4096) return BS_EINVAL;
+    if (nodes_per_block < 1 || nodes_per_block > 1024) return BS_EINVAL;
     if (n_global >= INT32_MAX) return BS_ERANGE;
-    // greedy: extend the block row by row while its entry count stays within
-    // nodes_per_block; a row longer than that gets a block of its own
+    // greedy: extend the block row by row while it holds at most
+    // nodes_per_block rows and nodes_per_block entries; a row longer than
+    // that gets a block of its own
     int64_t nb = 0;
     int64_t g = 0;
     block_starts[0] = 0;
     while (g < n_global) {
         const int64_t start = off[g];
         int64_t end = g + 1;
-        while (end < n_global && (int64_t)off[end + 1] - start <= nodes_per_block) ++end;
+        while (end < n_global && end - g < nodes_per_block && (int64_t)off[end + 1] - start <= nodes_per_block)
+            ++end;
         block_starts[++nb] = (int32_t)end;
         g = end;
     }

@@ -5,17 +5,22 @@
 // BS3 norm, BS4 inner product, BS5 fused CG update, BS6 gather and BS7
 // scatter. All are bound by HBM bandwidth (at most 0.25 flop per byte), so the
 // kernels are written for bytes in flight, not for arithmetic:
-//  - 128-bit (two-double) loads and stores, several per lane in flight before
-//    any is consumed, coalesced across the 64-lane wavefront;
-//  - grid-stride loops over a grid sized to the compute-unit count for the
-//    vector ops, so the reduction partials are few and their order fixed;
-//  - reductions: per-lane accumulation, then a wavefront butterfly through
-//    cross-lane shuffles, then the block's wavefronts through LDS, one partial
-//    per block, and the last block to finish (a completion counter, no
-//    atomics on values) sums the partials in a fixed order;
-//  - scatter and gather remap block indices so that each of the 8 XCDs walks
-//    one contiguous eighth of the index table, keeping the reuse of shared
-//    nodes inside one XCD's L2.
+//  - 128-bit (two-double) non-temporal loads and stores for every contiguous
+//    stream, all loads of a lane issued before any is consumed, coalesced
+//    across the 64-lane wavefront;
+//  - grid-stride loops over a grid sized from the compute-unit count, with
+//    the unroll depth and blocks per CU chosen per operation by measurement;
+//  - reductions: per-lane accumulation, a wavefront butterfly through
+//    cross-lane shuffles, the block's wavefronts through LDS, one partial per
+//    block, then a one-block second kernel that sums the partials in a fixed
+//    order. No atomics anywhere, so results repeat bit for bit;
+//  - scatter: each lane owns pairs of consecutive local entries, loads their
+//    two indices as one 8-byte word and stores the two values as one 16-byte
+//    word, 16 pairs per lane in flight;
+//  - gather: the balanced blockStarts scheme of the paper, each block staging
+//    at most 1024 CSR entries of v_L in LDS with coalesced index loads, then
+//    one lane per global node summing its entries from LDS in ascending order;
+//    without a plan, one lane per node with all of its loads issued up front.
 // No MFMA: nothing here is a dense contraction.
 //
 // Bit-exactness: the file is compiled with -ffp-contract=off and the pragma
@@ -38,15 +43,29 @@ namespace {
 
 constexpr int kBlock = 256;          // threads per block: 4 wavefronts
 constexpr int kWave = 64;            // gfx950 wavefront width
-constexpr int kUnroll = 4;           // 16-byte loads per lane per array per iteration
-constexpr int kBlocksPerCU = 8;      // grid of the vector ops: CUs * this
-constexpr int kMaxPartials = 16384;  // reduction scratch (blocks of one launch)
-constexpr int kXcds = 8;             // MI355X: 8 XCDs of 32 CUs, round-robin dispatch
-constexpr int kScatterPerLane = 4;   // local entries per lane in the scatter kernel
-constexpr int kGatherLds = 4096;     // entries a gather block may stage in LDS
+constexpr int kMaxPartials = 16384;  // reduction scratch (blocks of one first-stage launch)
+
+// Launch shape of a vector kernel: 16-byte loads per lane per array per loop
+// iteration, and blocks per compute unit (0: one tile per block, no loop).
+struct VecShape {
+    int unroll;
+    int blocks_per_cu;
+};
+// Chosen by a sweep of unroll {1,2,4,8} x blocks/CU {flat,2,4,8,16} x block
+// size {256,512,1024} x non-temporal on/off on cold data (vectors of 11.4M and
+// 67M doubles, buffers rotated through > 2 GB so no operand is cache-resident).
+constexpr VecShape kCopyShape{1, 0};
+constexpr VecShape kAxpyShape{1, 2};
+constexpr VecShape kDotShape{2, 2};
+constexpr VecShape kCgShape{4, 2};
+
+constexpr int kScatterPairs = 16;  // index pairs per lane in the scatter kernel
+constexpr int kGatherCap = 1024;   // CSR entries and rows a gather block stages in LDS
+constexpr int kGatherRowM = 4;     // entries per row loaded up front (row kernel)
+constexpr int kGatherRowR = 2;     // rows per lane (row kernel)
 
 typedef double d2 __attribute__((ext_vector_type(2)));
-typedef int i4 __attribute__((ext_vector_type(4)));
+typedef int i2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ d2 ld2(const d2 *p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void st2(d2 *p, d2 v) { __builtin_nontemporal_store(v, p); }
@@ -77,28 +96,20 @@ __device__ __forceinline__ double block_sum(double v)
     return s;
 }
 
-// Stores the block's partial, and in the last block to finish sums all
-// partials in index order (then a fixed tree) and writes the result. The
-// counter is left at zero for the next launch on the same context.
-__device__ __forceinline__ void finish_reduction(double part, double *partials,
-                                                 unsigned *counter, double *out, bool take_sqrt)
+// Second stage of every reduction: one block sums the nb per-block partials
+// in a fixed order (each lane a strided run, then the block tree) and writes
+// the result, or its square root. nb == 0 stores +0.0. The kernel boundary
+// between the two stages makes the partials visible across XCDs; a
+// single-kernel "last block" finish would need an agent-scope release per
+// block, which on this multi-XCD part writes back and invalidates L2 for
+// every block and measured several times slower than the second launch.
+__global__ __launch_bounds__(kBlock) void k_finish(const double *__restrict__ partials, int nb,
+                                                   double *__restrict__ out, bool take_sqrt)
 {
-    __shared__ bool is_last;
-    if (threadIdx.x == 0) {
-        __hip_atomic_store(&partials[blockIdx.x], part, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        unsigned done = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        is_last = (done == gridDim.x - 1);
-    }
-    __syncthreads();
-    if (!is_last) return;
     double s = 0.0;
-    for (unsigned i = threadIdx.x; i < gridDim.x; i += kBlock)
-        s += __hip_atomic_load(&partials[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = threadIdx.x; i < nb; i += kBlock) s += partials[i];
     s = block_sum(s);
-    if (threadIdx.x == 0) {
-        *out = take_sqrt ? std::sqrt(s) : s;
-        __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (threadIdx.x == 0) *out = take_sqrt ? std::sqrt(s) : s;
 }
 
 // ------------------------------------------------------- vector layout ----
@@ -122,22 +133,23 @@ __host__ __device__ inline Split split_of(int64_t n, int64_t head)
 }
 
 // ------------------------------------------------------------ BS1 copy ----
+template <int U>
 __global__ __launch_bounds__(kBlock) void k_copy(Split sp, const double *__restrict__ x,
                                                  double *__restrict__ y)
 {
     const d2 *xv = reinterpret_cast<const d2 *>(x + sp.head);
     d2 *yv = reinterpret_cast<d2 *>(y + sp.head);
-    const int64_t stride = (int64_t)gridDim.x * kBlock * kUnroll;
-    int64_t i = (int64_t)blockIdx.x * kBlock * kUnroll + threadIdx.x;
-    for (; i + (kUnroll - 1) * kBlock < sp.n2; i += stride) {
-        d2 v[kUnroll];
+    const int64_t stride = (int64_t)gridDim.x * kBlock * U;
+    int64_t i = (int64_t)blockIdx.x * kBlock * U + threadIdx.x;
+    for (; i + (U - 1) * kBlock < sp.n2; i += stride) {
+        d2 v[U];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) v[u] = ld2(xv + i + u * kBlock);
+        for (int u = 0; u < U; ++u) v[u] = ld2(xv + i + u * kBlock);
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) st2(yv + i + u * kBlock, v[u]);
+        for (int u = 0; u < U; ++u) st2(yv + i + u * kBlock, v[u]);
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
+    for (int u = 0; u < U; ++u)
         if (i + u * kBlock < sp.n2) st2(yv + i + u * kBlock, ld2(xv + i + u * kBlock));
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         if (sp.head) y[0] = x[0];
@@ -154,25 +166,26 @@ __device__ __forceinline__ d2 axpy2(double a, d2 x, double b, d2 y)
     return r;
 }
 
+template <int U>
 __global__ __launch_bounds__(kBlock) void k_axpy(Split sp, double a, const double *x, double b,
                                                  double *y)
 {
     const d2 *xv = reinterpret_cast<const d2 *>(x + sp.head);
     d2 *yv = reinterpret_cast<d2 *>(y + sp.head);
-    const int64_t stride = (int64_t)gridDim.x * kBlock * kUnroll;
-    int64_t i = (int64_t)blockIdx.x * kBlock * kUnroll + threadIdx.x;
-    for (; i + (kUnroll - 1) * kBlock < sp.n2; i += stride) {
-        d2 vx[kUnroll], vy[kUnroll];
+    const int64_t stride = (int64_t)gridDim.x * kBlock * U;
+    int64_t i = (int64_t)blockIdx.x * kBlock * U + threadIdx.x;
+    for (; i + (U - 1) * kBlock < sp.n2; i += stride) {
+        d2 vx[U], vy[U];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
             vx[u] = ld2(xv + i + u * kBlock);
             vy[u] = ld2(yv + i + u * kBlock);
         }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) st2(yv + i + u * kBlock, axpy2(a, vx[u], b, vy[u]));
+        for (int u = 0; u < U; ++u) st2(yv + i + u * kBlock, axpy2(a, vx[u], b, vy[u]));
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
         const int64_t k = i + u * kBlock;
         if (k < sp.n2) st2(yv + k, axpy2(a, ld2(xv + k), b, ld2(yv + k)));
     }
@@ -183,31 +196,31 @@ __global__ __launch_bounds__(kBlock) void k_axpy(Split sp, double a, const doubl
 }
 
 // ------------------------------------------------- BS3 norm, BS4 dot ----
-// One kernel for both: with y == nullptr it sums x[i]^2 and takes the root.
-template <bool kSquare>
+// First stage of both: with kSquare it sums x[i]^2 (y is ignored).
+template <int U, bool kSquare>
 __global__ __launch_bounds__(kBlock) void k_dot(Split sp, const double *x, const double *y,
-                                                double *partials, unsigned *counter, double *out)
+                                                double *partials)
 {
     const d2 *xv = reinterpret_cast<const d2 *>(x + sp.head);
     const d2 *yv = reinterpret_cast<const d2 *>((kSquare ? x : y) + sp.head);
-    const int64_t stride = (int64_t)gridDim.x * kBlock * kUnroll;
-    int64_t i = (int64_t)blockIdx.x * kBlock * kUnroll + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * kBlock * U;
+    int64_t i = (int64_t)blockIdx.x * kBlock * U + threadIdx.x;
     double acc0 = 0.0, acc1 = 0.0;
-    for (; i + (kUnroll - 1) * kBlock < sp.n2; i += stride) {
-        d2 vx[kUnroll], vy[kUnroll];
+    for (; i + (U - 1) * kBlock < sp.n2; i += stride) {
+        d2 vx[U], vy[U];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
             vx[u] = ld2(xv + i + u * kBlock);
             vy[u] = kSquare ? vx[u] : ld2(yv + i + u * kBlock);
         }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
             acc0 = __builtin_fma(vx[u].x, vy[u].x, acc0);
             acc1 = __builtin_fma(vx[u].y, vy[u].y, acc1);
         }
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
         const int64_t k = i + u * kBlock;
         if (k < sp.n2) {
             const d2 a = ld2(xv + k);
@@ -222,58 +235,58 @@ __global__ __launch_bounds__(kBlock) void k_dot(Split sp, const double *x, const
         if (sp.tail >= 0) acc1 = __builtin_fma(x[sp.tail], yy[sp.tail], acc1);
     }
     const double part = block_sum(acc0 + acc1);
-    finish_reduction(part, partials, counter, out, kSquare);
+    if (threadIdx.x == 0) partials[blockIdx.x] = part;
 }
 
 // -------------------------------------------------- BS5 fused CG update ----
+__device__ __forceinline__ void cg2(double a, d2 p, d2 q, d2 &x, d2 &r)
+{
+    x.x = x.x + a * p.x;
+    x.y = x.y + a * p.y;
+    r.x = r.x - a * q.x;
+    r.y = r.y - a * q.y;
+}
+
+template <int U>
 __global__ __launch_bounds__(kBlock) void k_cg_update(Split sp, double a, const double *p,
                                                       const double *q, double *x, double *r,
-                                                      double *partials, unsigned *counter,
-                                                      double *out)
+                                                      double *partials)
 {
     const d2 *pv = reinterpret_cast<const d2 *>(p + sp.head);
     const d2 *qv = reinterpret_cast<const d2 *>(q + sp.head);
     d2 *xv = reinterpret_cast<d2 *>(x + sp.head);
     d2 *rv = reinterpret_cast<d2 *>(r + sp.head);
-    const int64_t stride = (int64_t)gridDim.x * kBlock * kUnroll;
-    int64_t i = (int64_t)blockIdx.x * kBlock * kUnroll + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * kBlock * U;
+    int64_t i = (int64_t)blockIdx.x * kBlock * U + threadIdx.x;
     double acc0 = 0.0, acc1 = 0.0;
-    for (; i + (kUnroll - 1) * kBlock < sp.n2; i += stride) {
-        d2 vp[kUnroll], vq[kUnroll], vx[kUnroll], vr[kUnroll];
+    for (; i + (U - 1) * kBlock < sp.n2; i += stride) {
+        d2 vp[U], vq[U], vx[U], vr[U];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
             vp[u] = ld2(pv + i + u * kBlock);
             vq[u] = ld2(qv + i + u * kBlock);
             vx[u] = ld2(xv + i + u * kBlock);
             vr[u] = ld2(rv + i + u * kBlock);
         }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            d2 nx, nr;
-            nx.x = vx[u].x + a * vp[u].x;
-            nx.y = vx[u].y + a * vp[u].y;
-            nr.x = vr[u].x - a * vq[u].x;
-            nr.y = vr[u].y - a * vq[u].y;
-            st2(xv + i + u * kBlock, nx);
-            st2(rv + i + u * kBlock, nr);
-            acc0 = __builtin_fma(nr.x, nr.x, acc0);
-            acc1 = __builtin_fma(nr.y, nr.y, acc1);
+        for (int u = 0; u < U; ++u) {
+            cg2(a, vp[u], vq[u], vx[u], vr[u]);
+            st2(xv + i + u * kBlock, vx[u]);
+            st2(rv + i + u * kBlock, vr[u]);
+            acc0 = __builtin_fma(vr[u].x, vr[u].x, acc0);
+            acc1 = __builtin_fma(vr[u].y, vr[u].y, acc1);
         }
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
         const int64_t k = i + u * kBlock;
         if (k < sp.n2) {
-            const d2 vp1 = ld2(pv + k), vq1 = ld2(qv + k), vx1 = ld2(xv + k), vr1 = ld2(rv + k);
-            d2 nx, nr;
-            nx.x = vx1.x + a * vp1.x;
-            nx.y = vx1.y + a * vp1.y;
-            nr.x = vr1.x - a * vq1.x;
-            nr.y = vr1.y - a * vq1.y;
-            st2(xv + k, nx);
-            st2(rv + k, nr);
-            acc0 = __builtin_fma(nr.x, nr.x, acc0);
-            acc1 = __builtin_fma(nr.y, nr.y, acc1);
+            d2 vx1 = ld2(xv + k), vr1 = ld2(rv + k);
+            cg2(a, ld2(pv + k), ld2(qv + k), vx1, vr1);
+            st2(xv + k, vx1);
+            st2(rv + k, vr1);
+            acc0 = __builtin_fma(vr1.x, vr1.x, acc0);
+            acc1 = __builtin_fma(vr1.y, vr1.y, acc1);
         }
     }
     if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -292,55 +305,48 @@ __global__ __launch_bounds__(kBlock) void k_cg_update(Split sp, double a, const 
         }
     }
     const double part = block_sum(acc0 + acc1);
-    finish_reduction(part, partials, counter, out, false);
-}
-
-// n == 0 reductions still store +0.0 (no memset: a kernel keeps it capturable).
-__global__ void k_store_zero(double *out) { *out = 0.0; }
-
-// ------------------------------------------------------ XCD-aware order ----
-// Workgroups are dispatched round-robin over the XCDs: block b runs on XCD
-// b % 8. Map the first 8*floor(nb/8) blocks so that XCD x takes the tiles
-// x*q .. x*q+q-1 in order (q = floor(nb/8)); the remainder keeps its index.
-__device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t nb)
-{
-    const int64_t q = nb / kXcds;
-    if (b >= q * kXcds) return b;
-    return (b % kXcds) * q + b / kXcds;
+    if (threadIdx.x == 0) partials[blockIdx.x] = part;
 }
 
 // --------------------------------------------------------- BS7 scatter ----
-// Each lane handles kScatterPerLane consecutive local entries: one 16-byte
-// index load, four reads of v_G, two 16-byte stores. Tiles are kBlock lanes.
+// Lane t of block b owns the index pairs b*P + t + kBlock*u (u < kScatterPairs,
+// P = kBlock*kScatterPairs pairs per block), i.e. local entries 2*pair and
+// 2*pair+1: one 8-byte index load, two reads of v_G, one 16-byte store each.
+// All index loads of the lane are issued before the reads they feed, and all
+// reads before the stores. The last, partial tile goes entry by entry.
 __global__ __launch_bounds__(kBlock) void k_scatter(int64_t nl, const int32_t *__restrict__ l2g,
                                                     const double *__restrict__ vg,
                                                     double *__restrict__ vl)
 {
-    const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
-    const int64_t i0 = (tile * kBlock + threadIdx.x) * kScatterPerLane;
-    if (i0 + kScatterPerLane <= nl) {
-        const i4 id = __builtin_nontemporal_load(reinterpret_cast<const i4 *>(l2g + i0));
-        d2 a, b;
-        a.x = id.x >= 0 ? vg[id.x] : 0.0;
-        a.y = id.y >= 0 ? vg[id.y] : 0.0;
-        b.x = id.z >= 0 ? vg[id.z] : 0.0;
-        b.y = id.w >= 0 ? vg[id.w] : 0.0;
-        st2(reinterpret_cast<d2 *>(vl + i0), a);
-        st2(reinterpret_cast<d2 *>(vl + i0 + 2), b);
+    constexpr int64_t kTile = 2LL * kBlock * kScatterPairs;  // entries per block
+    const int64_t base = (int64_t)blockIdx.x * kTile;
+    if (base + kTile <= nl) {
+        const i2 *ip = reinterpret_cast<const i2 *>(l2g + base) + threadIdx.x;
+        d2 *op = reinterpret_cast<d2 *>(vl + base) + threadIdx.x;
+        i2 id[kScatterPairs];
+#pragma unroll
+        for (int u = 0; u < kScatterPairs; ++u) id[u] = __builtin_nontemporal_load(ip + u * kBlock);
+        d2 v[kScatterPairs];
+#pragma unroll
+        for (int u = 0; u < kScatterPairs; ++u) {
+            v[u].x = id[u].x >= 0 ? vg[id[u].x] : 0.0;
+            v[u].y = id[u].y >= 0 ? vg[id[u].y] : 0.0;
+        }
+#pragma unroll
+        for (int u = 0; u < kScatterPairs; ++u) st2(op + u * kBlock, v[u]);
     } else {
-        for (int64_t i = i0; i < nl; ++i) {
+        for (int64_t i = base + threadIdx.x; i < nl; i += kBlock) {
             const int32_t g = l2g[i];
             vl[i] = g >= 0 ? vg[g] : 0.0;
         }
     }
 }
 
-// Fallback for index or value pointers without 16-byte alignment.
+// Fallback for index or value pointers without 8/16-byte alignment.
 __global__ __launch_bounds__(kBlock) void k_scatter_scalar(int64_t nl, const int32_t *l2g,
                                                            const double *vg, double *vl)
 {
-    const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
-    const int64_t i = tile * kBlock + threadIdx.x;
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
     if (i < nl) {
         const int32_t g = l2g[i];
         vl[i] = g >= 0 ? vg[g] : 0.0;
@@ -348,53 +354,140 @@ __global__ __launch_bounds__(kBlock) void k_scatter_scalar(int64_t nl, const int
 }
 
 // ---------------------------------------------------------- BS6 gather ----
-// Row-per-lane: lane g walks ids[off[g] .. off[g+1]) and sums from +0.0.
+// Row kernel (no plan): lane t of block b owns rows b*kBlock*R + t + kBlock*r
+// (r < R). It loads both offsets of every row, then the first M ids of every
+// row, then the v_L values they name, before summing any: three dependent
+// rounds of loads per block instead of two per entry. Rows longer than M
+// finish entry by entry. Each sum runs left to right from +0.0.
 __global__ __launch_bounds__(kBlock) void k_gather_rows(int64_t ng, const int32_t *__restrict__ off,
                                                         const int32_t *__restrict__ ids,
                                                         const double *__restrict__ vl,
                                                         double *__restrict__ vg)
 {
-    const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
-    const int64_t g = tile * kBlock + threadIdx.x;
-    if (g >= ng) return;
-    const int32_t a = off[g], b = off[g + 1];
-    double s = 0.0;
-    for (int32_t j = a; j < b; ++j) s = s + vl[ids[j]];
-    __builtin_nontemporal_store(s, vg + g);
+    constexpr int M = kGatherRowM, R = kGatherRowR;
+    const int64_t g0 = (int64_t)blockIdx.x * kBlock * R + threadIdx.x;
+    int32_t a[R], b[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t g = g0 + (int64_t)r * kBlock;
+        a[r] = g < ng ? off[g] : 0;
+        b[r] = g < ng ? off[g + 1] : 0;
+    }
+    int32_t id[R][M];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int k = 0; k < M; ++k) id[r][k] = (a[r] + k < b[r]) ? __builtin_nontemporal_load(ids + a[r] + k) : -1;
+    double v[R][M];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int k = 0; k < M; ++k) v[r][k] = id[r][k] >= 0 ? vl[id[r][k]] : 0.0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t g = g0 + (int64_t)r * kBlock;
+        if (g >= ng) continue;
+        double s = 0.0;
+#pragma unroll
+        for (int k = 0; k < M; ++k)
+            if (a[r] + k < b[r]) s = s + v[r][k];
+        for (int32_t j = a[r] + M; j < b[r]; ++j) s = s + vl[ids[j]];
+        __builtin_nontemporal_store(s, vg + g);
+    }
 }
 
-// LDS-staged, after the blockStarts kernel of the paper: block b owns rows
-// bs[b] .. bs[b+1]); it first reads the rows' CSR entries with consecutive
-// lanes on consecutive entries and stages v_L[ids[j]] in LDS, then each lane
-// sums its rows from LDS in ascending entry order. A block holding more than
-// kGatherLds entries (a single very long row) reads from global memory.
-__global__ __launch_bounds__(kBlock) void k_gather_lds(const int32_t *__restrict__ bstart,
-                                                       const int32_t *__restrict__ off,
-                                                       const int32_t *__restrict__ ids,
-                                                       const double *__restrict__ vl,
-                                                       double *__restrict__ vg)
+// LDS-staged kernel after the blockStarts scheme of the paper: block b owns
+// rows bs[b] .. bs[b+1]), which bs_gather_plan caps at kGatherCap rows and
+// kGatherCap entries (a single longer row gets a block of its own). The block
+// stages the rows' offsets in LDS, reads the rows' CSR ids with consecutive
+// lanes on consecutive entries, fetches the named v_L values, all issued
+// before any is stored, stages them in LDS, and then each lane sums its rows
+// from LDS in ascending entry order. Blocks over capacity read global memory.
+__global__ __launch_bounds__(kBlock) void k_gather_plan(const int32_t *__restrict__ bstart,
+                                                        const int32_t *__restrict__ off,
+                                                        const int32_t *__restrict__ ids,
+                                                        const double *__restrict__ vl,
+                                                        double *__restrict__ vg)
 {
-    __shared__ double stage[kGatherLds];
-    const int64_t blk = xcd_tile(blockIdx.x, gridDim.x);
-    const int32_t r0 = bstart[blk], r1 = bstart[blk + 1];
-    const int32_t e0 = off[r0], e1 = off[r1];
-    const int32_t ne = e1 - e0;
-    if (ne <= kGatherLds) {
-        for (int32_t t = threadIdx.x; t < ne; t += kBlock) stage[t] = vl[ids[e0 + t]];
+    constexpr int K = kGatherCap / kBlock;  // entries per lane
+    __shared__ int32_t so[kGatherCap + 1];
+    __shared__ double stage[kGatherCap];
+    const int32_t r0 = bstart[blockIdx.x], r1 = bstart[blockIdx.x + 1];
+    const int32_t nr = r1 - r0;
+    if (nr <= kGatherCap) {
+        for (int32_t t = threadIdx.x; t <= nr; t += kBlock) so[t] = off[r0 + t];
         __syncthreads();
-        for (int32_t g = r0 + threadIdx.x; g < r1; g += kBlock) {
-            const int32_t a = off[g] - e0, b = off[g + 1] - e0;
-            double s = 0.0;
-            for (int32_t j = a; j < b; ++j) s = s + stage[j];
-            __builtin_nontemporal_store(s, vg + g);
-        }
-    } else {
-        for (int32_t g = r0 + threadIdx.x; g < r1; g += kBlock) {
-            double s = 0.0;
-            for (int32_t j = off[g]; j < off[g + 1]; ++j) s = s + vl[ids[j]];
-            vg[g] = s;
+        const int32_t e0 = so[0], ne = so[nr] - e0;
+        if (ne <= kGatherCap) {
+            int32_t id[K];
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const int32_t t = threadIdx.x + k * kBlock;
+                id[k] = t < ne ? __builtin_nontemporal_load(ids + e0 + t) : -1;
+            }
+            double v[K];
+#pragma unroll
+            for (int k = 0; k < K; ++k) v[k] = id[k] >= 0 ? vl[id[k]] : 0.0;
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const int32_t t = threadIdx.x + k * kBlock;
+                if (t < ne) stage[t] = v[k];
+            }
+            __syncthreads();
+            for (int32_t r = threadIdx.x; r < nr; r += kBlock) {
+                const int32_t a = so[r] - e0, b = so[r + 1] - e0;
+                double s = 0.0;
+                for (int32_t j = a; j < b; ++j) s = s + stage[j];
+                __builtin_nontemporal_store(s, vg + r0 + r);
+            }
+            return;
         }
     }
+    for (int32_t g = r0 + threadIdx.x; g < r1; g += kBlock) {
+        double s = 0.0;
+        for (int32_t j = off[g]; j < off[g + 1]; ++j) s = s + vl[ids[j]];
+        vg[g] = s;
+    }
+}
+
+// Scalar (8-byte) versions of the vector ops for operands whose 16-byte
+// phases differ.
+__global__ __launch_bounds__(kBlock) void k_copy_scalar(int64_t n, const double *x, double *y)
+{
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += (int64_t)gridDim.x * kBlock)
+        y[i] = x[i];
+}
+
+__global__ __launch_bounds__(kBlock) void k_axpy_scalar(int64_t n, double a, const double *x,
+                                                        double b, double *y)
+{
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += (int64_t)gridDim.x * kBlock)
+        y[i] = a * x[i] + b * y[i];
+}
+
+__global__ __launch_bounds__(kBlock) void k_dot_scalar(int64_t n, const double *x, const double *y,
+                                                       double *partials)
+{
+    double acc = 0.0;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += (int64_t)gridDim.x * kBlock)
+        acc = __builtin_fma(x[i], y[i], acc);
+    const double part = block_sum(acc);
+    if (threadIdx.x == 0) partials[blockIdx.x] = part;
+}
+
+__global__ __launch_bounds__(kBlock) void k_cg_update_scalar(int64_t n, double a, const double *p,
+                                                             const double *q, double *x, double *r,
+                                                             double *partials)
+{
+    double acc = 0.0;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += (int64_t)gridDim.x * kBlock) {
+        x[i] = x[i] + a * p[i];
+        const double nr = r[i] - a * q[i];
+        r[i] = nr;
+        acc = __builtin_fma(nr, nr, acc);
+    }
+    const double part = block_sum(acc);
+    if (threadIdx.x == 0) partials[blockIdx.x] = part;
 }
 
 }  // namespace
@@ -405,26 +498,32 @@ struct bs_ctx {
     int device;
     int cus;
     int max_partials;
-    double *partials;
-    unsigned *counter;
+    double *partials;  // first-stage reduction results, one per block
 };
 
 namespace {
 
 inline bool misaligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
-inline int launch_status()
+inline int launch_status() { return hipGetLastError() == hipSuccess ? BS_OK : BS_EHIP; }
+
+// Grid of a vector kernel with shape s over n2 pairs: the tiles needed, at
+// most CUs * blocks_per_cu (when that is set) and never above the partials
+// the context holds.
+inline unsigned vector_grid(const bs_ctx *c, int64_t n2, VecShape s)
 {
-    return hipGetLastError() == hipSuccess ? BS_OK : BS_EHIP;
+    const int64_t per = (int64_t)kBlock * s.unroll;
+    int64_t g = (n2 + per - 1) / per;
+    if (s.blocks_per_cu > 0 && g > (int64_t)c->cus * s.blocks_per_cu) g = (int64_t)c->cus * s.blocks_per_cu;
+    if (g > c->max_partials) g = c->max_partials;
+    if (g < 1) g = 1;
+    return (unsigned)g;
 }
 
-// Grid of the grid-stride vector kernels: enough tiles to cover n2 pairs, at
-// most CUs * kBlocksPerCU blocks (which also bounds the reduction partials).
-inline unsigned vector_grid(const bs_ctx *c, int64_t n2)
+inline unsigned scalar_grid(const bs_ctx *c, int64_t n)
 {
-    const int64_t per = (int64_t)kBlock * kUnroll;
-    int64_t g = (n2 + per - 1) / per;
-    const int64_t cap = (int64_t)c->cus * kBlocksPerCU;
+    int64_t g = (n + kBlock - 1) / kBlock;
+    const int64_t cap = (int64_t)c->cus * 8;
     if (g > cap) g = cap;
     if (g > c->max_partials) g = c->max_partials;
     if (g < 1) g = 1;
@@ -442,61 +541,43 @@ inline bool common_head(const void *const *ptrs, int k, int64_t *head)
     return true;
 }
 
-// Scalar (8-byte) versions for operands whose 16-byte phases differ.
-__global__ __launch_bounds__(kBlock) void k_copy_scalar(int64_t n, const double *x, double *y)
-{
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += (int64_t)gridDim.x * kBlock)
-        y[i] = x[i];
-}
-
-__global__ __launch_bounds__(kBlock) void k_axpy_scalar(int64_t n, double a, const double *x,
-                                                        double b, double *y)
-{
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += (int64_t)gridDim.x * kBlock)
-        y[i] = a * x[i] + b * y[i];
-}
-
-template <bool kSquare>
-__global__ __launch_bounds__(kBlock) void k_dot_scalar(int64_t n, const double *x, const double *y,
-                                                       double *partials, unsigned *counter, double *out)
-{
-    double acc = 0.0;
-    const double *yy = kSquare ? x : y;
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += (int64_t)gridDim.x * kBlock)
-        acc = __builtin_fma(x[i], yy[i], acc);
-    finish_reduction(block_sum(acc), partials, counter, out, kSquare);
-}
-
-__global__ __launch_bounds__(kBlock) void k_cg_update_scalar(int64_t n, double a, const double *p,
-                                                             const double *q, double *x, double *r,
-                                                             double *partials, unsigned *counter,
-                                                             double *out)
-{
-    double acc = 0.0;
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += (int64_t)gridDim.x * kBlock) {
-        x[i] = x[i] + a * p[i];
-        const double nr = r[i] - a * q[i];
-        r[i] = nr;
-        acc = __builtin_fma(nr, nr, acc);
-    }
-    finish_reduction(block_sum(acc), partials, counter, out, false);
-}
-
-inline unsigned scalar_grid(const bs_ctx *c, int64_t n)
-{
-    int64_t g = (n + kBlock - 1) / kBlock;
-    const int64_t cap = (int64_t)c->cus * kBlocksPerCU;
-    if (g > cap) g = cap;
-    if (g > c->max_partials) g = c->max_partials;
-    if (g < 1) g = 1;
-    return (unsigned)g;
-}
-
 inline int check_ctx(const bs_ctx *c)
 {
     if (!c) return BS_EINVAL;
-    if (hipSetDevice(c->device) != hipSuccess) return BS_EHIP;
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return BS_EHIP;
+    if (cur != c->device && hipSetDevice(c->device) != hipSuccess) return BS_EHIP;
     return BS_OK;
+}
+
+int finish_launch(bs_ctx *c, unsigned nb, double *out, bool take_sqrt, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_finish, dim3(1), dim3(kBlock), 0, st, c->partials, (int)nb, out, take_sqrt);
+    return launch_status();
+}
+
+int reduce_launch(bs_ctx *c, int64_t n, const double *x, const double *y, double *out, bool square,
+                  hipStream_t st)
+{
+    if (n == 0) return finish_launch(c, 0, out, false, st);
+    const void *ptrs[2] = {x, square ? x : y};
+    int64_t head;
+    unsigned nb;
+    if (common_head(ptrs, 2, &head)) {
+        const Split sp = split_of(n, head);
+        nb = vector_grid(c, sp.n2, kDotShape);
+        if (square)
+            hipLaunchKernelGGL((k_dot<kDotShape.unroll, true>), dim3(nb), dim3(kBlock), 0, st, sp, x, x,
+                               c->partials);
+        else
+            hipLaunchKernelGGL((k_dot<kDotShape.unroll, false>), dim3(nb), dim3(kBlock), 0, st, sp, x, y,
+                               c->partials);
+    } else {
+        nb = scalar_grid(c, n);
+        hipLaunchKernelGGL(k_dot_scalar, dim3(nb), dim3(kBlock), 0, st, n, x, y, c->partials);
+    }
+    if (hipGetLastError() != hipSuccess) return BS_EHIP;
+    return finish_launch(c, nb, out, square, st);
 }
 
 }  // namespace
@@ -516,7 +597,7 @@ const char *bs_strerror(int status)
     }
 }
 
-int bs_version(void) { return 100; }
+int bs_version(void) { return 200; }
 
 int bs_ctx_create(int device, bs_ctx **out)
 {
@@ -534,18 +615,9 @@ int bs_ctx_create(int device, bs_ctx **out)
     c->cus = cus;
     c->max_partials = kMaxPartials;
     c->partials = nullptr;
-    c->counter = nullptr;
-    if (hipMalloc(&c->partials, sizeof(double) * kMaxPartials) != hipSuccess ||
-        hipMalloc(&c->counter, sizeof(unsigned)) != hipSuccess) {
-        if (c->partials) (void)hipFree(c->partials);
+    if (hipMalloc(&c->partials, sizeof(double) * kMaxPartials) != hipSuccess) {
         delete c;
         return BS_ENOMEM;
-    }
-    if (hipMemset(c->counter, 0, sizeof(unsigned)) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
-        (void)hipFree(c->partials);
-        (void)hipFree(c->counter);
-        delete c;
-        return BS_EHIP;
     }
     *out = c;
     return BS_OK;
@@ -557,7 +629,6 @@ void bs_ctx_destroy(bs_ctx *c)
     if (hipSetDevice(c->device) == hipSuccess) {
         (void)hipDeviceSynchronize();
         (void)hipFree(c->partials);
-        (void)hipFree(c->counter);
     }
     delete c;
 }
@@ -582,7 +653,8 @@ int bs_copy(bs_ctx *c, int64_t n, const double *x, double *y, void *stream)
     int64_t head;
     if (common_head(ptrs, 2, &head)) {
         const Split sp = split_of(n, head);
-        hipLaunchKernelGGL(k_copy, dim3(vector_grid(c, sp.n2)), dim3(kBlock), 0, st, sp, x, y);
+        hipLaunchKernelGGL(k_copy<kCopyShape.unroll>, dim3(vector_grid(c, sp.n2, kCopyShape)), dim3(kBlock), 0,
+                           st, sp, x, y);
     } else {
         hipLaunchKernelGGL(k_copy_scalar, dim3(scalar_grid(c, n)), dim3(kBlock), 0, st, n, x, y);
     }
@@ -600,32 +672,10 @@ int bs_axpy(bs_ctx *c, int64_t n, double alpha, const double *x, double beta, do
     int64_t head;
     if (common_head(ptrs, 2, &head)) {
         const Split sp = split_of(n, head);
-        hipLaunchKernelGGL(k_axpy, dim3(vector_grid(c, sp.n2)), dim3(kBlock), 0, st, sp, alpha, x, beta, y);
+        hipLaunchKernelGGL(k_axpy<kAxpyShape.unroll>, dim3(vector_grid(c, sp.n2, kAxpyShape)), dim3(kBlock), 0,
+                           st, sp, alpha, x, beta, y);
     } else {
         hipLaunchKernelGGL(k_axpy_scalar, dim3(scalar_grid(c, n)), dim3(kBlock), 0, st, n, alpha, x, beta, y);
-    }
-    return launch_status();
-}
-
-static int reduce_launch(bs_ctx *c, int64_t n, const double *x, const double *y, double *out,
-                         bool square, hipStream_t st)
-{
-    if (n == 0) {
-        hipLaunchKernelGGL(k_store_zero, dim3(1), dim3(1), 0, st, out);
-        return launch_status();
-    }
-    const void *ptrs[2] = {x, square ? x : y};
-    int64_t head;
-    if (common_head(ptrs, 2, &head)) {
-        const Split sp = split_of(n, head);
-        const dim3 grid(vector_grid(c, sp.n2));
-        if (square)
-            hipLaunchKernelGGL(k_dot<true>, grid, dim3(kBlock), 0, st, sp, x, x, c->partials, c->counter, out);
-        else
-            hipLaunchKernelGGL(k_dot<false>, grid, dim3(kBlock), 0, st, sp, x, y, c->partials, c->counter, out);
-    } else {
-        const dim3 grid(scalar_grid(c, n));
-        hipLaunchKernelGGL(k_dot_scalar<false>, grid, dim3(kBlock), 0, st, n, x, y, c->partials, c->counter, out);
     }
     return launch_status();
 }
@@ -655,21 +705,22 @@ int bs_cg_update(bs_ctx *c, int64_t n, double alpha, const double *p, const doub
         misaligned(rr, 8))
         return BS_EALIGN;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (n == 0) {
-        hipLaunchKernelGGL(k_store_zero, dim3(1), dim3(1), 0, st, rr);
-        return launch_status();
-    }
+    if (n == 0) return finish_launch(c, 0, rr, false, st);
     const void *ptrs[4] = {p, q, x, r};
     int64_t head;
+    unsigned nb;
     if (common_head(ptrs, 4, &head)) {
         const Split sp = split_of(n, head);
-        hipLaunchKernelGGL(k_cg_update, dim3(vector_grid(c, sp.n2)), dim3(kBlock), 0, st, sp, alpha, p, q, x,
-                           r, c->partials, c->counter, rr);
+        nb = vector_grid(c, sp.n2, kCgShape);
+        hipLaunchKernelGGL(k_cg_update<kCgShape.unroll>, dim3(nb), dim3(kBlock), 0, st, sp, alpha, p, q, x, r,
+                           c->partials);
     } else {
-        hipLaunchKernelGGL(k_cg_update_scalar, dim3(scalar_grid(c, n)), dim3(kBlock), 0, st, n, alpha, p, q,
-                           x, r, c->partials, c->counter, rr);
+        nb = scalar_grid(c, n);
+        hipLaunchKernelGGL(k_cg_update_scalar, dim3(nb), dim3(kBlock), 0, st, n, alpha, p, q, x, r,
+                           c->partials);
     }
-    return launch_status();
+    if (hipGetLastError() != hipSuccess) return BS_EHIP;
+    return finish_launch(c, nb, rr, false, st);
 }
 
 int bs_scatter(bs_ctx *c, int64_t n_local, const int32_t *l2g, const double *v_global, double *v_local,
@@ -681,8 +732,8 @@ int bs_scatter(bs_ctx *c, int64_t n_local, const int32_t *l2g, const double *v_g
     if (n_local == 0) return BS_OK;
     if (misaligned(l2g, 4) || misaligned(v_global, 8) || misaligned(v_local, 8)) return BS_EALIGN;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (!misaligned(l2g, 16) && !misaligned(v_local, 16)) {
-        const int64_t per = (int64_t)kBlock * kScatterPerLane;
+    if (!misaligned(l2g, 8) && !misaligned(v_local, 16)) {
+        const int64_t per = 2LL * kBlock * kScatterPairs;
         const int64_t nb = (n_local + per - 1) / per;
         hipLaunchKernelGGL(k_scatter, dim3((unsigned)nb), dim3(kBlock), 0, st, n_local, l2g, v_global, v_local);
     } else {
@@ -705,10 +756,11 @@ int bs_gather(bs_ctx *c, int64_t n_global, const int32_t *off, const int32_t *id
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (block_starts) {
         if (n_blocks < 1 || n_blocks > n_global || misaligned(block_starts, 4)) return BS_EINVAL;
-        hipLaunchKernelGGL(k_gather_lds, dim3((unsigned)n_blocks), dim3(kBlock), 0, st, block_starts, off, ids,
+        hipLaunchKernelGGL(k_gather_plan, dim3((unsigned)n_blocks), dim3(kBlock), 0, st, block_starts, off, ids,
                            v_local, v_global);
     } else {
-        const int64_t nb = (n_global + kBlock - 1) / kBlock;
+        const int64_t per = (int64_t)kBlock * kGatherRowR;
+        const int64_t nb = (n_global + per - 1) / per;
         hipLaunchKernelGGL(k_gather_rows, dim3((unsigned)nb), dim3(kBlock), 0, st, n_global, off, ids, v_local,
                            v_global);
     }

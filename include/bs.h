@@ -55,8 +55,8 @@ const char *bs_strerror(int status);
 int bs_version(void);
 
 /* Create a context on HIP device `device`: queries its compute-unit count and
- * allocates the reduction scratch (partials and a completion counter) on that
- * device. *out receives the context; the caller releases it with
+ * allocates the reduction scratch (one partial sum per block of a first-stage
+ * launch) on that device. *out receives the context; the caller releases it with
  * bs_ctx_destroy. Errors: BS_EINVAL (out NULL), BS_EHIP (no such device),
  * BS_ENOMEM. */
 int bs_ctx_create(int device, bs_ctx **out);
@@ -121,8 +121,10 @@ int bs_scatter(bs_ctx *ctx, int64_t n_local, const int32_t *l2g, const double *v
  * ascending local index. off int32[n_global+1], ids int32[off[n_global]],
  * v_local double[> max id], v_global double[n_global]. block_starts NULL
  * selects the row-per-lane kernel; otherwise int32[n_blocks+1] from
- * bs_gather_plan selects the LDS-staged kernel (same bits). n_global or the
- * entry count beyond INT32_MAX is BS_ERANGE. */
+ * bs_gather_plan selects the LDS-staged kernel (same bits). Neither the CSR
+ * nor the plan is range-checked on the device: pass tables built by
+ * bs_index_g2l and bs_gather_plan (or equally well formed). n_global >=
+ * INT32_MAX is BS_ERANGE. */
 int bs_gather(bs_ctx *ctx, int64_t n_global, const int32_t *off, const int32_t *ids,
               const double *v_local, double *v_global, const int32_t *block_starts,
               int64_t n_blocks, void *stream);
@@ -160,12 +162,14 @@ int bs_index_g2l(int64_t n_local, int64_t n_global, const int32_t *l2g, int32_t 
                  int32_t *ids);
 
 /* blockStarts of the LDS-staged gather (arXiv 2009.10917, implementation
- * section, BS6): rows are cut into consecutive blocks holding about
- * nodes_per_block CSR entries each (never more, unless a single row is
- * longer), so each thread block reads and writes about the same amount.
- * block_starts receives n_blocks+1 row indices (capacity n_global+1 suffices),
- * block_starts[0] = 0 and block_starts[n_blocks] = n_global. nodes_per_block
- * must be in [1, 4096] (BS_EINVAL). */
+ * section, BS6): rows are cut into consecutive blocks so that each thread
+ * block reads and writes about the same amount: greedily, a block takes rows
+ * while it holds at most nodes_per_block rows and at most nodes_per_block CSR
+ * entries (a single longer row gets a block of its own). block_starts
+ * receives n_blocks+1 row indices (capacity n_global+1 suffices),
+ * block_starts[0] = 0 and block_starts[n_blocks] = n_global.
+ * nodes_per_block must be in [1, 1024] (BS_EINVAL): the gather kernel stages
+ * up to 1024 entries per block in LDS. */
 int bs_gather_plan(int64_t n_global, const int32_t *off, int nodes_per_block,
                    int32_t *block_starts, int64_t *n_blocks);
 

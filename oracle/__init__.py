@@ -49,6 +49,8 @@ def lib():
         if not os.path.exists(_LIB):
             build()
         L = ctypes.CDLL(_LIB)
+        L.or_threads.argtypes = []
+        L.or_threads.restype = ctypes.c_int
         L.or_copy.argtypes = [_c_int64, _ptr, _ptr]
         L.or_copy.restype = None
         L.or_axpy.argtypes = [_c_int64, _c_double, _ptr, _c_double, _ptr]
@@ -85,6 +87,11 @@ def _i32(a):
 
 def _nptr(a):
     return None if a is None else _i32(a)
+
+
+def threads():
+    """OpenMP threads the oracle's parallel loops use."""
+    return lib().or_threads()
 
 
 # --------------------------------------------------------------- BS1..BS7 --

@@ -32,11 +32,18 @@
  * GPU is held to.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 #define OR_CHUNK 65536
+
+/* Threads the parallel loops below use. */
+int or_threads(void)
+{
+    return omp_get_max_threads();
+}
 
 /* ---------------------------------------------------------------- BS1 --- */
 /* y = x as a bit copy: NaN payloads and signed zeros are preserved. */

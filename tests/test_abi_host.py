@@ -157,7 +157,7 @@ def test_g2l_rejects_out_of_range(bs):
     bs.bs_validate_l2g(np.array([-1, 2], dtype=np.int32), 3)
 
 
-@pytest.mark.parametrize("npb", [1, 8, 256, 512, 2048, 4096])
+@pytest.mark.parametrize("npb", [1, 8, 256, 512, 1000, 1024])
 def test_gather_plan(bs, npb):
     l2g = bs.bs_mesh_box_l2g(6, 5, 4, 3)
     ng = bs.bs_mesh_box_count(6, 5, 4, 3)[1]
@@ -169,9 +169,17 @@ def test_gather_plan(bs, npb):
     rows = np.diff(plan)
     # never above the target unless the block is one long row
     assert np.all((ent <= npb) | (rows == 1))
-    # greedy: adding the next row would have exceeded the target
+    assert np.all(rows <= npb)
+    # greedy: adding the next row would have exceeded a cap
     nxt = off[np.minimum(plan[1:-1] + 1, ng)] - off[plan[:-2]]
-    assert np.all(nxt > npb)
+    assert np.all((nxt > npb) | (rows[:-1] == npb))
+
+
+def test_gather_plan_caps_rows(bs):
+    # empty rows (fully masked nodes) still count against the row cap
+    off = np.zeros(3001, dtype=np.int32)
+    plan = bs.bs_gather_plan(off, 1024)
+    assert list(plan) == [0, 1024, 2048, 3000]
 
 
 def test_gather_plan_long_rows(bs):
@@ -182,4 +190,4 @@ def test_gather_plan_long_rows(bs):
     with pytest.raises(bs.BSError):
         bs.bs_gather_plan(off, 0)
     with pytest.raises(bs.BSError):
-        bs.bs_gather_plan(off, 5000)
+        bs.bs_gather_plan(off, 1025)

@@ -222,7 +222,7 @@ def test_scatter_gather_mesh(env, name):
     vg = torch.full((ng,), np.nan, dtype=torch.float64, device=d)
     bs.bs_gather(doff, dids, dvl, vg)
     assert_bits(host(vg), want, f"gather rows {name}")
-    for npb in (512, 2048, 4096):
+    for npb in (256, 512, 1024):
         plan = bs.bs_gather_plan(off, npb)
         vg.fill_(np.nan)
         bs.bs_gather(doff, dids, dvl, vg, dev(torch, d, plan))
@@ -278,7 +278,7 @@ def test_gather_order_and_signed_zero(env):
     off, ids = bs.bs_index_g2l(l2g, ng)
     want = orc.gather(l2g, vlv, ng)
     assert list(want) == [0.0, 0.0, 0.0, 0.0, 0.0]
-    for plan in (None, bs.bs_gather_plan(off, 3), bs.bs_gather_plan(off, 4096)):
+    for plan in (None, bs.bs_gather_plan(off, 3), bs.bs_gather_plan(off, 1024)):
         vg = torch.full((ng,), np.nan, dtype=torch.float64, device=d)
         bs.bs_gather(dev(torch, d, off), dev(torch, d, ids), dev(torch, d, vlv), vg,
                      None if plan is None else dev(torch, d, plan))
@@ -296,16 +296,35 @@ def test_gather_long_row_fallback(env):
     vlv = bs_inputs.uniform_pm1(80, nl)
     off, ids = bs.bs_index_g2l(l2g, ng)
     want = orc.gather(l2g, vlv, ng)
-    for plan in (None, bs.bs_gather_plan(off, 4096), bs.bs_gather_plan(off, 1)):
+    for plan in (None, bs.bs_gather_plan(off, 1024), bs.bs_gather_plan(off, 1)):
         vg = torch.empty(ng, dtype=torch.float64, device=d)
         bs.bs_gather(dev(torch, d, off), dev(torch, d, ids), dev(torch, d, vlv), vg,
                      None if plan is None else dev(torch, d, plan))
         assert_bits(host(vg), want, "long rows")
 
 
+def test_gather_plan_over_capacity_blocks(env):
+    """A hand-made plan whose blocks exceed the LDS capacity (rows or
+    entries) takes the global-memory path, with the same bits."""
+    bs, orc, torch, d = env
+    l2g = bs.bs_mesh_box_l2g(6, 6, 6, 3)
+    ng = bs.bs_mesh_box_count(6, 6, 6, 3)[1]
+    off, ids = bs.bs_index_g2l(l2g, ng)
+    ol2g, _ = orc.mesh_box(6, 6, 6, 3)
+    vlv = bs_inputs.uniform_pm1(85, l2g.size)
+    want = orc.gather(ol2g, vlv, ng)
+    plans = [np.array([0, ng], dtype=np.int32),
+             np.array([0, 700, 2100, 2101, ng], dtype=np.int32),
+             np.arange(0, ng + 1, dtype=np.int32)]
+    for plan in plans:
+        vg = torch.full((ng,), np.nan, dtype=torch.float64, device=d)
+        bs.bs_gather(dev(torch, d, off), dev(torch, d, ids), dev(torch, d, vlv), vg, dev(torch, d, plan))
+        assert_bits(host(vg), want, f"plan with {plan.size - 1} blocks")
+
+
 def test_scatter_ragged_and_misaligned(env):
     bs, orc, torch, d = env
-    for nl in [1, 3, 5, 1023, 1025, 4097]:
+    for nl in [1, 3, 5, 1023, 1025, 4097, 8191, 8192, 8193, 3 * 8192 + 77]:
         ng = 50
         l2g = (bs_inputs.splitmix64(81, nl) % np.uint64(ng)).astype(np.int32)
         vgv = bs_inputs.uniform_pm1(82, ng)
