@@ -45,7 +45,7 @@ PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 METRIC = "effective GB/s and % of HBM peak per BS op (fp64, N=7 hex mesh, 1 GPU)"
 OPS = ["copy", "axpy", "norm", "dot", "cg_update", "scatter", "gather"]
 KERNEL_NAME = {  # op -> first-stage kernel as rocprofv3 names it (namespace and arguments stripped)
-    "copy": "k_copy<1>", "axpy": "k_axpy<1>", "norm": "k_dot<2, true>", "dot": "k_dot<2, false>",
+    "copy": "k_copy<1>", "axpy": "k_axpy<1>", "norm": "k_dot<4, true>", "dot": "k_dot<4, false>",
     "cg_update": "k_cg_update<4>", "scatter": "k_scatter", "gather": "k_gather_plan",
 }
 GATHER_NPB = 1024
@@ -64,42 +64,60 @@ def kernel_source_sha():
 
 
 class Mesh:
-    """Device tables and vectors of one mesh workload, one set per operation."""
+    """Device tables and vectors of one mesh workload, one set per operation.
 
-    def __init__(self, bs, torch, dev, name, E, N, gather_lds):
+    With layout "arena" every array of the set comes from one allocation, in
+    the order below (each operation's arrays adjacent), on 2 MB boundaries;
+    with "torch" each array is a separate torch allocation."""
+
+    # (attribute, source) in arena order; source: host array name or ("empty", length kind)
+    ORDER = ["copy_x", "copy_y", "axpy_x", "axpy_y", "norm_x", "dot_x", "dot_y", "cg_p", "cg_q", "cg_x",
+             "cg_r", "l2g", "sc_vg", "sc_vl", "off", "ids", "plan", "ga_vl", "ga_vg", "out"]
+
+    def __init__(self, bs, torch, dev, name, E, N, gather_lds, layout="arena"):
         ep, npm = bs_inputs.mesh_perms(name, E, N)
         self.name, self.E, self.N = name, E, N
+        self.torch, self.dev, self.layout = torch, dev, layout
         self.nl, self.ng = bs.bs_mesh_box_count(E, E, E, N)
         l2g = bs.bs_mesh_box_l2g(E, E, E, N, ep, npm)
         off, ids = bs.bs_index_g2l(l2g, self.ng)
         plan = bs.bs_gather_plan(off, GATHER_NPB)
-        t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
-        f64 = lambda n: torch.empty(n, dtype=torch.float64, device=dev)  # noqa: E731
         v = bs_inputs.vectors(name, self.ng)
         b = bs_inputs.base_seed(name)
-        self.l2g, self.off, self.ids, self.plan = t(l2g), t(off), t(ids), t(plan)
         self.gather_lds = gather_lds
-        n = self.ng
+        n, nl = self.ng, self.nl
         # per-operation arrays (distinct, so no operation finds another's data in cache)
-        self.copy_x, self.copy_y = t(v["x"]), f64(n)
-        self.axpy_x, self.axpy_y = t(v["p"]), t(v["y"])
-        self.norm_x = t(v["q"])
-        self.dot_x, self.dot_y = t(v["r"]), t(v["x"])
-        self.cg_p, self.cg_q, self.cg_x, self.cg_r = t(v["p"]), t(v["q"]), t(v["x"]), t(v["r"])
-        self.sc_vg, self.sc_vl = t(v["y"]), f64(self.nl)
-        self.ga_vl, self.ga_vg = t(bs_inputs.uniform_pm1(b + 9, self.nl)), f64(n)
-        self.out = torch.zeros(4, dtype=torch.float64, device=dev)
-        del v
+        host = {"copy_x": v["x"], "copy_y": ("f64", n), "axpy_x": v["p"], "axpy_y": v["y"], "norm_x": v["q"],
+                "dot_x": v["r"], "dot_y": v["x"], "cg_p": v["p"], "cg_q": v["q"], "cg_x": v["x"], "cg_r": v["r"],
+                "l2g": l2g, "sc_vg": v["y"], "sc_vl": ("f64", nl), "off": off, "ids": ids, "plan": plan,
+                "ga_vl": bs_inputs.uniform_pm1(b + 9, nl), "ga_vg": ("f64", n), "out": np.zeros(4)}
+        self._materialize({k: (torch.from_numpy(np.ascontiguousarray(h)) if not isinstance(h, tuple) else h)
+                           for k, h in host.items()})
+        del v, host
 
-    DEVICE_ARRAYS = ["l2g", "off", "ids", "plan", "copy_x", "copy_y", "axpy_x", "axpy_y", "norm_x", "dot_x",
-                     "dot_y", "cg_p", "cg_q", "cg_x", "cg_r", "sc_vg", "sc_vl", "ga_vl", "ga_vg", "out"]
+    def _materialize(self, src):
+        """Place every array of ORDER on the device from src (tensors or ("f64", n))."""
+        torch = self.torch
+        def nbytes(x):
+            return x[1] * 8 if isinstance(x, tuple) else x.numel() * x.element_size()
+        if self.layout == "arena":
+            from cg_streaming_vector_amd.arena import Arena
+            arena = Arena(sum(Arena.slot(nbytes(src[k])) for k in self.ORDER), self.dev)
+            for k in self.ORDER:
+                x = src[k]
+                setattr(self, k, arena.empty(x[1], torch.float64) if isinstance(x, tuple) else arena.put(x))
+            self._arena = arena
+        else:
+            for k in self.ORDER:
+                x = src[k]
+                setattr(self, k, torch.empty(x[1], dtype=torch.float64, device=self.dev) if isinstance(x, tuple)
+                        else x.to(self.dev).clone())
 
     def clone(self):
         """Another set of the same device arrays (fresh memory, same values)."""
         m = object.__new__(Mesh)
-        m.__dict__.update({k: v for k, v in self.__dict__.items() if k not in self.DEVICE_ARRAYS})
-        for k in self.DEVICE_ARRAYS:
-            setattr(m, k, getattr(self, k).clone())
+        m.__dict__.update({k: v for k, v in self.__dict__.items() if k not in self.ORDER and k != "_arena"})
+        m._materialize({k: getattr(self, k) for k in self.ORDER})
         return m
 
     def launchers(self, bs, stream):
@@ -335,6 +353,8 @@ def main():
     ap.add_argument("--gather", choices=["rows", "lds"], default="lds")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate", type=int, default=12, help="array sets cycled in the per-op loops")
+    ap.add_argument("--layout", choices=["arena", "torch"], default="arena",
+                    help="arena: each set's arrays packed in one allocation on 2 MB boundaries")
     ap.add_argument("--per-op-reps", type=int, default=96)
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--workloads", action="store_true")
@@ -354,7 +374,7 @@ def main():
     ctx = bs.context(0)
 
     name, E, N = "c2_box32_N7", 32, 7
-    mesh = Mesh(bs, torch, dev, name, E, N, gather_lds=(args.gather == "lds"))
+    mesh = Mesh(bs, torch, dev, name, E, N, gather_lds=(args.gather == "lds"), layout=args.layout)
     stream = torch.cuda.current_stream().cuda_stream
     launch = mesh.launchers(bs, stream)
     step_bytes = sum(mesh.bytes(op) for op in OPS)
@@ -427,7 +447,7 @@ def main():
         "config": {"workload": "box mesh 32^3 elements, order N=7, lexicographic numbering; "
                                "all 7 BS ops per step", "elements": E ** 3, "order": N,
                    "n_global": mesh.ng, "n_local": mesh.nl, "step_bytes": step_bytes,
-                   "gather_kernel": args.gather, "cu_count": ctx.info()["cu_count"]},
+                   "gather_kernel": args.gather, "layout": args.layout, "cu_count": ctx.info()["cu_count"]},
         "pct_peak": round(100 * value / PEAK_GBPS, 1),
         "per_op": ops_out,
         "runtime_copy_GBps": round(rt_copy, 1),

@@ -51,13 +51,16 @@ struct VecShape {
     int unroll;
     int blocks_per_cu;
 };
-// Chosen by a sweep of unroll {1,2,4,8} x blocks/CU {flat,2,4,8,16} x block
-// size {256,512,1024} x non-temporal on/off on cold data (vectors of 11.4M and
-// 67M doubles, buffers rotated through > 2 GB so no operand is cache-resident).
+// Chosen by sweeps of unroll {1,2,4,8,16} x blocks/CU {flat,1,2,4,8,16} x block
+// size {256,512,1024} x non-temporal on/off x occupancy hint on cold data
+// (vectors of 11.4M and 67M doubles, buffers rotated through > 2 GB so no
+// operand is cache-resident). Fewer blocks keep the lockstep window of all
+// streams narrow, which the multi-stream kernels prefer.
 constexpr VecShape kCopyShape{1, 0};
 constexpr VecShape kAxpyShape{1, 2};
-constexpr VecShape kDotShape{2, 2};
-constexpr VecShape kCgShape{4, 2};
+constexpr VecShape kDotShape{4, 1};
+constexpr VecShape kNormShape{4, 2};
+constexpr VecShape kCgShape{4, 1};
 
 constexpr int kScatterPairs = 16;  // index pairs per lane in the scatter kernel
 constexpr int kGatherCap = 1024;   // CSR entries and rows a gather block stages in LDS
@@ -196,10 +199,13 @@ __global__ __launch_bounds__(kBlock) void k_axpy(Split sp, double a, const doubl
 }
 
 // ------------------------------------------------- BS3 norm, BS4 dot ----
-// First stage of both: with kSquare it sums x[i]^2 (y is ignored).
+// First stage of both: with kSquare it sums x[i]^2 (y is ignored). The grid
+// holds one or two blocks per CU, so the kernel never needs more than two
+// waves per SIMD: the occupancy hint lets the compiler keep every load of a
+// lane in flight instead of trading registers for waves it will not get.
 template <int U, bool kSquare>
-__global__ __launch_bounds__(kBlock) void k_dot(Split sp, const double *x, const double *y,
-                                                double *partials)
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_dot(
+    Split sp, const double *__restrict__ x, const double *__restrict__ y, double *__restrict__ partials)
 {
     const d2 *xv = reinterpret_cast<const d2 *>(x + sp.head);
     const d2 *yv = reinterpret_cast<const d2 *>((kSquare ? x : y) + sp.head);
@@ -247,10 +253,14 @@ __device__ __forceinline__ void cg2(double a, d2 p, d2 q, d2 &x, d2 &r)
     r.y = r.y - a * q.y;
 }
 
+// p, q, x and r are distinct arrays (the ABI requires it), so the pointers are
+// restrict-qualified: without that the compiler may not move a store of x or r
+// past a later load and serialises the lane's loads, which at one block per
+// CU costs about a third of the bandwidth.
 template <int U>
-__global__ __launch_bounds__(kBlock) void k_cg_update(Split sp, double a, const double *p,
-                                                      const double *q, double *x, double *r,
-                                                      double *partials)
+__global__ __launch_bounds__(kBlock) void k_cg_update(Split sp, double a, const double *__restrict__ p,
+                                                      const double *__restrict__ q, double *__restrict__ x,
+                                                      double *__restrict__ r, double *__restrict__ partials)
 {
     const d2 *pv = reinterpret_cast<const d2 *>(p + sp.head);
     const d2 *qv = reinterpret_cast<const d2 *>(q + sp.head);
@@ -565,13 +575,15 @@ int reduce_launch(bs_ctx *c, int64_t n, const double *x, const double *y, double
     unsigned nb;
     if (common_head(ptrs, 2, &head)) {
         const Split sp = split_of(n, head);
-        nb = vector_grid(c, sp.n2, kDotShape);
-        if (square)
-            hipLaunchKernelGGL((k_dot<kDotShape.unroll, true>), dim3(nb), dim3(kBlock), 0, st, sp, x, x,
+        if (square) {
+            nb = vector_grid(c, sp.n2, kNormShape);
+            hipLaunchKernelGGL((k_dot<kNormShape.unroll, true>), dim3(nb), dim3(kBlock), 0, st, sp, x, x,
                                c->partials);
-        else
+        } else {
+            nb = vector_grid(c, sp.n2, kDotShape);
             hipLaunchKernelGGL((k_dot<kDotShape.unroll, false>), dim3(nb), dim3(kBlock), 0, st, sp, x, y,
                                c->partials);
+        }
     } else {
         nb = scalar_grid(c, n);
         hipLaunchKernelGGL(k_dot_scalar, dim3(nb), dim3(kBlock), 0, st, n, x, y, c->partials);
