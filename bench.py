@@ -44,9 +44,10 @@ import bs_inputs  # noqa: E402
 PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 METRIC = "effective GB/s and % of HBM peak per BS op (fp64, N=7 hex mesh, 1 GPU)"
 OPS = ["copy", "axpy", "norm", "dot", "cg_update", "scatter", "gather"]
-KERNEL_NAME = {  # op -> first-stage kernel as rocprofv3 names it (namespace and arguments stripped)
-    "copy": "k_copy<1>", "axpy": "k_axpy<1>", "norm": "k_dot<4, true>", "dot": "k_dot<4, false>",
-    "cg_update": "k_cg_update<4>", "scatter": "k_scatter", "gather": "k_gather_plan",
+KERNEL_NAME = {  # op -> its kernels as rocprofv3 names them (namespace and arguments stripped)
+    "copy": ["k_copy<1>"], "axpy": ["k_axpy<1>"], "norm": ["k_dot<4, true>", "k_finish"],
+    "dot": ["k_dot<4, false>", "k_finish"], "cg_update": ["k_cg_update<4>", "k_finish"],
+    "scatter": ["k_scatter"], "gather": ["k_gather_plan"],
 }
 GATHER_NPB = 1024
 
@@ -174,9 +175,10 @@ def time_ops_rotated(torch, sets_launch, ops, reps):
     return out
 
 
-def traffic_for(kernel, launches_bytes):
-    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if the
-    kernel source has not changed since it was taken."""
+def traffic_for(kernels):
+    """HBM bytes per launch of an operation (the sum over its kernels) from the
+    committed rocprofv3 --pmc summary, if the kernel source has not changed
+    since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "pmc_traffic_c2.json")
     if not os.path.exists(path):
         return None
@@ -186,10 +188,13 @@ def traffic_for(kernel, launches_bytes):
         return None
     if d.get("kernel_source_sha256") != kernel_source_sha():
         return None
-    k = d.get("kernels", {}).get(kernel)
-    if not k:
-        return None
-    return float(k["hbm_bytes_per_launch"])
+    total = 0.0
+    for kernel in kernels:
+        k = d.get("kernels", {}).get(kernel)
+        if not k or "hbm_bytes_per_launch" not in k:
+            return None
+        total += float(k["hbm_bytes_per_launch"])
+    return total
 
 
 def cpu_baseline(mesh_host, budget_s=12.0):
@@ -417,10 +422,10 @@ def main():
         ops_out[op] = {"bytes": mesh.bytes(op), "us": round(t * 1e6, 2), "GBps": round(gbps, 1),
                        "pct_peak": round(100 * gbps / PEAK_GBPS, 1)}
     achieved = mesh.bytes(dom) / dom_live / 1e9
-    traffic = traffic_for(KERNEL_NAME[dom], mesh.bytes(dom))
+    traffic = traffic_for(KERNEL_NAME[dom])
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
-                "kernel": KERNEL_NAME[dom], "bytes_per_launch": mesh.bytes(dom),
+                "op": dom, "kernel": " + ".join(KERNEL_NAME[dom]), "bytes_per_launch": mesh.bytes(dom),
                 "us_per_launch": round(dom_live * 1e6, 2)}
 
     # the runtime's own device-to-device copy at this size, on rotated buffers

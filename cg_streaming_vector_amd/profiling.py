@@ -62,7 +62,7 @@ def load_counter(path, counter):
     return out
 
 
-def summarize(stats_csv, fetch_csv, write_csv, copy_kernel, copy_doubles, source=None):
+def summarize(stats_csv, fetch_csv, write_csv, copy_kernel, copy_doubles, source=None, ops=None):
     stats = load_stats(stats_csv) if stats_csv else {}
     fetch = load_counter(fetch_csv, "FETCH_SIZE") if fetch_csv else {}
     write = load_counter(write_csv, "WRITE_SIZE") if write_csv else {}
@@ -89,6 +89,13 @@ def summarize(stats_csv, fetch_csv, write_csv, copy_kernel, copy_doubles, source
     out = {"calibration": {"copy_kernel": copy_kernel, "copy_doubles": copy_doubles,
                            "fetch_scale": f_scale, "write_scale": w_scale},
            "kernels": kernels}
+    if ops:
+        # an operation may be several kernels launched back to back (a
+        # reduction's first stage and its finish): sum their averages
+        out["ops"] = {}
+        for name, ks in ops.items():
+            if all(k in kernels and "avg_ns" in kernels[k] for k in ks):
+                out["ops"][name] = {"kernels": ks, "avg_ns": sum(kernels[k]["avg_ns"] for k in ks)}
     if source:
         out["kernel_source_sha256"] = hashlib.sha256(open(source, "rb").read()).hexdigest()
     return out
@@ -108,6 +115,10 @@ def to_markdown(summary, title, commands):
             f"{d['fetch_kib_median']:.0f}" if "fetch_kib_median" in d else "",
             f"{d['write_kib_median']:.0f}" if "write_kib_median" in d else "",
             f"{d['hbm_bytes_per_launch'] / 1e6:.2f}" if "hbm_bytes_per_launch" in d else ""))
+    if summary.get("ops"):
+        lines += ["", "| operation | kernels | avg us (sum) |", "|---|---|---|"]
+        for name, d in summary["ops"].items():
+            lines.append(f"| {name} | {' + '.join('`%s`' % k for k in d['kernels'])} | {d['avg_ns'] / 1e3:.2f} |")
     if "kernel_source_sha256" in summary:
         lines += ["", f"Kernel source sha256: `{summary['kernel_source_sha256']}`"]
     return "\n".join(lines) + "\n"
@@ -123,10 +134,12 @@ def main(argv=None):
     ap.add_argument("--source")
     ap.add_argument("--title", default="BS kernels")
     ap.add_argument("--command", action="append", default=[])
+    ap.add_argument("--op", action="append", default=[], help="NAME=kernel1+kernel2 (summed averages)")
     ap.add_argument("--json")
     ap.add_argument("--md")
     a = ap.parse_args(argv)
-    s = summarize(a.stats, a.fetch, a.write, a.copy_kernel, a.copy_doubles, a.source)
+    ops = {o.split("=", 1)[0]: o.split("=", 1)[1].split("+") for o in a.op}
+    s = summarize(a.stats, a.fetch, a.write, a.copy_kernel, a.copy_doubles, a.source, ops)
     if a.json:
         with open(a.json, "w") as f:
             json.dump(s, f, indent=1)
