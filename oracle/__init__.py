@@ -22,6 +22,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# A test may point the wrapper at a deliberately broken build of oracle.c to
+# show that the pins catch the mistake.
+_LIB = os.environ.get("BS_ORACLE_LIB", _LIB)
 
 _c_int64 = ctypes.c_int64
 _c_double = ctypes.c_double

@@ -106,6 +106,24 @@ def test_dot_exact_rational(orc, n):
     assert abs(Fraction(got) - want) <= Fraction(2) * abs(want) * Fraction(1, 2 ** 53) + Fraction(1, 2 ** 150)
 
 
+@pytest.mark.parametrize("n", [1000, 70001])
+def test_dot_ill_conditioned(orc, n):
+    """Random x, y plus one last pair (-RN(S), 1) with S the exact dot of the
+    rest: the exact result S - RN(S) is below one ulp of S while sum |x y| is
+    of order n, a condition number near 1e16. Dot2 (error-free products and
+    sums) still returns it to high relative accuracy; a plain or half-
+    compensated sum does not."""
+    x = bs_inputs.uniform_pm1(48, n)
+    y = bs_inputs.uniform_pm1(49, n)
+    S = exact_dot(x, y)
+    x = np.append(x, -float(S))
+    y = np.append(y, 1.0)
+    want = S - Fraction(float(S))
+    assert want != 0
+    got = orc.dot(x, y)
+    assert abs(Fraction(got) - want) <= abs(want) * Fraction(1, 10 ** 6)
+
+
 def test_dot_integer_vectors_exact(orc):
     n = 300_000
     x = bs_inputs.small_ints(43, n, -50, 50)
