@@ -518,14 +518,16 @@ inline bool misaligned(const void *p, uintptr_t a) { return (reinterpret_cast<ui
 inline int launch_status() { return hipGetLastError() == hipSuccess ? BS_OK : BS_EHIP; }
 
 // Grid of a vector kernel with shape s over n2 pairs: the tiles needed, at
-// most CUs * blocks_per_cu (when that is set) and never above the partials
-// the context holds.
-inline unsigned vector_grid(const bs_ctx *c, int64_t n2, VecShape s)
+// most CUs * blocks_per_cu (when that is set). A reduction's grid is also
+// bounded by the partials the context holds; any other grid by 2^22 blocks
+// (the kernels loop over whatever a smaller grid leaves).
+inline unsigned vector_grid(const bs_ctx *c, int64_t n2, VecShape s, bool reduction)
 {
     const int64_t per = (int64_t)kBlock * s.unroll;
     int64_t g = (n2 + per - 1) / per;
     if (s.blocks_per_cu > 0 && g > (int64_t)c->cus * s.blocks_per_cu) g = (int64_t)c->cus * s.blocks_per_cu;
-    if (g > c->max_partials) g = c->max_partials;
+    const int64_t cap = reduction ? (int64_t)c->max_partials : (int64_t)1 << 22;
+    if (g > cap) g = cap;
     if (g < 1) g = 1;
     return (unsigned)g;
 }
@@ -576,11 +578,11 @@ int reduce_launch(bs_ctx *c, int64_t n, const double *x, const double *y, double
     if (common_head(ptrs, 2, &head)) {
         const Split sp = split_of(n, head);
         if (square) {
-            nb = vector_grid(c, sp.n2, kNormShape);
+            nb = vector_grid(c, sp.n2, kNormShape, true);
             hipLaunchKernelGGL((k_dot<kNormShape.unroll, true>), dim3(nb), dim3(kBlock), 0, st, sp, x, x,
                                c->partials);
         } else {
-            nb = vector_grid(c, sp.n2, kDotShape);
+            nb = vector_grid(c, sp.n2, kDotShape, true);
             hipLaunchKernelGGL((k_dot<kDotShape.unroll, false>), dim3(nb), dim3(kBlock), 0, st, sp, x, y,
                                c->partials);
         }
@@ -658,14 +660,16 @@ int bs_copy(bs_ctx *c, int64_t n, const double *x, double *y, void *stream)
 {
     if (int s = check_ctx(c)) return s;
     if (n < 0 || (n > 0 && (!x || !y))) return BS_EINVAL;
-    if (n == 0) return BS_OK;
     if (misaligned(x, 8) || misaligned(y, 8)) return BS_EALIGN;
+    // a copy onto itself changes nothing (and keeps the kernel's restrict
+    // qualifiers honest)
+    if (n == 0 || x == y) return BS_OK;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const void *ptrs[2] = {x, y};
     int64_t head;
     if (common_head(ptrs, 2, &head)) {
         const Split sp = split_of(n, head);
-        hipLaunchKernelGGL(k_copy<kCopyShape.unroll>, dim3(vector_grid(c, sp.n2, kCopyShape)), dim3(kBlock), 0,
+        hipLaunchKernelGGL(k_copy<kCopyShape.unroll>, dim3(vector_grid(c, sp.n2, kCopyShape, false)), dim3(kBlock), 0,
                            st, sp, x, y);
     } else {
         hipLaunchKernelGGL(k_copy_scalar, dim3(scalar_grid(c, n)), dim3(kBlock), 0, st, n, x, y);
@@ -684,7 +688,7 @@ int bs_axpy(bs_ctx *c, int64_t n, double alpha, const double *x, double beta, do
     int64_t head;
     if (common_head(ptrs, 2, &head)) {
         const Split sp = split_of(n, head);
-        hipLaunchKernelGGL(k_axpy<kAxpyShape.unroll>, dim3(vector_grid(c, sp.n2, kAxpyShape)), dim3(kBlock), 0,
+        hipLaunchKernelGGL(k_axpy<kAxpyShape.unroll>, dim3(vector_grid(c, sp.n2, kAxpyShape, false)), dim3(kBlock), 0,
                            st, sp, alpha, x, beta, y);
     } else {
         hipLaunchKernelGGL(k_axpy_scalar, dim3(scalar_grid(c, n)), dim3(kBlock), 0, st, n, alpha, x, beta, y);
@@ -723,7 +727,7 @@ int bs_cg_update(bs_ctx *c, int64_t n, double alpha, const double *p, const doub
     unsigned nb;
     if (common_head(ptrs, 4, &head)) {
         const Split sp = split_of(n, head);
-        nb = vector_grid(c, sp.n2, kCgShape);
+        nb = vector_grid(c, sp.n2, kCgShape, true);
         hipLaunchKernelGGL(k_cg_update<kCgShape.unroll>, dim3(nb), dim3(kBlock), 0, st, sp, alpha, p, q, x, r,
                            c->partials);
     } else {

@@ -125,6 +125,17 @@ def test_copy_special_values(env):
     assert host(y).tobytes() == a.tobytes()
 
 
+def test_copy_and_axpy_in_place(env):
+    """x == y is allowed for copy (no change) and AXPY (y = (a y) + (b y))."""
+    bs, orc, torch, d = env
+    v = bs_inputs.uniform_pm1(12, 100_003)
+    t = dev(torch, d, v)
+    bs.bs_copy(t, t)
+    assert_bits(host(t), v, "copy in place")
+    bs.bs_axpy(0.37, t, 1.5, t)
+    assert_bits(host(t), orc.axpy(0.37, v, 1.5, v), "axpy in place")
+
+
 def test_axpy_beta_zero_reads_y(env):
     bs, orc, torch, d = env
     n = 5000
