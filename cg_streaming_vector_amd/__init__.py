@@ -59,6 +59,9 @@ SIGNATURES = {
     "bs_cg_update": ([_ptr, _i64, _dbl, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr], _int),
     "bs_scatter": ([_ptr, _i64, _ptr, _ptr, _ptr, _ptr], _int),
     "bs_gather": ([_ptr, _i64, _ptr, _ptr, _ptr, _ptr, _ptr, _i64, _ptr], _int),
+    "bs_gather_dot": ([_ptr, _i64, _ptr, _ptr, _ptr, _ptr, _ptr, _i64, _ptr, _ptr, _ptr], _int),
+    "bs_cg_solve": ([_ptr, _i64, _i64, _ptr, _ptr, _ptr, _ptr, _i64, _ptr, _ptr, _ptr, _ptr, _ptr, _int, _dbl,
+                     _ptr, _ptr], _int),
     "bs_mesh_box_count": ([_int, _int, _int, _int, ctypes.POINTER(_i64), ctypes.POINTER(_i64)], _int),
     "bs_mesh_box_l2g": ([_int, _int, _int, _int, _ptr, _ptr, _ptr], _int),
     "bs_validate_l2g": ([_i64, _i64, _ptr], _int),
@@ -266,6 +269,52 @@ def bs_gather(off, ids, v_local, v_global, block_starts=None, *, ctx=None, strea
     return v_global
 
 
+def bs_gather_dot(off, ids, v_local, v_global, w, block_starts=None, out=None, *, ctx=None, stream=None):
+    """BS6 with w . v_global in the same pass: returns the one-element out."""
+    import torch
+    ng = v_global.numel()
+    if off.numel() != ng + 1 or w.numel() != ng:
+        raise ValueError("off must hold n_global + 1 entries and w n_global")
+    ctx = _ctx_dev(v_global, ctx)
+    out = _scalar_out(out, v_global)
+    bp, nb = None, 0
+    if block_starts is not None:
+        bp = _dev_tensor(block_starts, torch.int32, "block_starts")
+        nb = block_starts.numel() - 1
+    _check(_lib().bs_gather_dot(ctx.handle, ng, _dev_tensor(off, torch.int32, "off"),
+                                _dev_tensor(ids, torch.int32, "ids"),
+                                _dev_tensor(v_local, torch.float64, "v_local"),
+                                _dev_tensor(v_global, torch.float64, "v_global"), bp, nb,
+                                _dev_tensor(w, torch.float64, "w"), out.data_ptr(),
+                                _stream(stream, v_global.device)), "bs_gather_dot")
+    return out
+
+
+def bs_cg_solve(l2g, off, ids, x, r, p, q, p_local, iters, tol=0.0, block_starts=None, rr_hist=None, *,
+                ctx=None, stream=None):
+    """Device-resident CG on Z^T Z: runs up to `iters` iterations on the
+    device (x, r, p updated in place); returns rr_hist (device, iters+1)."""
+    import torch
+    ng, nl = x.numel(), l2g.numel()
+    if not (r.numel() == p.numel() == q.numel() == ng) or p_local.numel() != nl or off.numel() != ng + 1:
+        raise ValueError("inconsistent sizes")
+    ctx = _ctx_dev(x, ctx)
+    if rr_hist is None:
+        rr_hist = torch.empty(int(iters) + 1, dtype=torch.float64, device=x.device)
+    bp, nb = None, 0
+    if block_starts is not None:
+        bp = _dev_tensor(block_starts, torch.int32, "block_starts")
+        nb = block_starts.numel() - 1
+    _check(_lib().bs_cg_solve(ctx.handle, ng, nl, _dev_tensor(l2g, torch.int32, "l2g"),
+                              _dev_tensor(off, torch.int32, "off"), _dev_tensor(ids, torch.int32, "ids"), bp, nb,
+                              _dev_tensor(x, torch.float64, "x"), _dev_tensor(r, torch.float64, "r"),
+                              _dev_tensor(p, torch.float64, "p"), _dev_tensor(q, torch.float64, "q"),
+                              _dev_tensor(p_local, torch.float64, "p_local"), int(iters), float(tol),
+                              _dev_tensor(rr_hist, torch.float64, "rr_hist"), _stream(stream, x.device)),
+           "bs_cg_solve")
+    return rr_hist
+
+
 # ------------------------------------------------------------ host tables --
 
 def _host_i32(a, name):
@@ -321,5 +370,6 @@ def bs_gather_plan(off, nodes_per_block=1024):
 __all__ = [
     "BSError", "Context", "context", "LIB_PATH", "SIGNATURES",
     "bs_copy", "bs_axpy", "bs_norm", "bs_dot", "bs_cg_update", "bs_scatter", "bs_gather",
+    "bs_gather_dot", "bs_cg_solve",
     "bs_mesh_box_count", "bs_mesh_box_l2g", "bs_validate_l2g", "bs_index_g2l", "bs_gather_plan",
 ]

@@ -41,9 +41,24 @@
 
 namespace {
 
-constexpr int kBlock = 256;          // threads per block: 4 wavefronts
-constexpr int kWave = 64;            // gfx950 wavefront width
-constexpr int kMaxPartials = 16384;  // reduction scratch (blocks of one first-stage launch)
+constexpr int kBlock = 256;            // threads per block: 4 wavefronts
+constexpr int kWave = 64;              // gfx950 wavefront width
+constexpr int kFinishBlock = 1024;     // threads of the one-block reduction finish
+constexpr int kMaxPartials = 1 << 20;  // reduction scratch (blocks of one first-stage launch)
+
+// Device-resident CG scalars, one small array per context.
+enum CgSlot { kRR = 0, kAlpha = 1, kBeta = 2, kDone = 3, kThreshold = 4, kCgSlots = 8 };
+
+// A coefficient given by value or read from device memory (set by an earlier
+// kernel on the same stream, so no host synchronisation is needed).
+struct Coef {
+    double v;
+    const double *p;
+    __device__ __forceinline__ double get() const { return p ? *p : v; }
+};
+
+// Kernels of a device-resident CG iteration return at once after convergence.
+__device__ __forceinline__ bool skipped(const double *cgs) { return cgs && cgs[kDone] != 0.0; }
 
 // Launch shape of a vector kernel: 16-byte loads per lane per array per loop
 // iteration, and blocks per compute unit (0: one tile per block, no loop).
@@ -106,13 +121,66 @@ __device__ __forceinline__ double block_sum(double v)
 // single-kernel "last block" finish would need an agent-scope release per
 // block, which on this multi-XCD part writes back and invalidates L2 for
 // every block and measured several times slower than the second launch.
-__global__ __launch_bounds__(kBlock) void k_finish(const double *__restrict__ partials, int nb,
-                                                   double *__restrict__ out, bool take_sqrt)
+// Sum of the partials over one kFinishBlock-thread block, valid in thread 0:
+// each lane a strided run in index order, then the wave butterfly, then the
+// 16 wave sums in order.
+__device__ __forceinline__ double finish_sum(const double *__restrict__ partials, int nb)
 {
+    __shared__ double wsum[kFinishBlock / kWave];
     double s = 0.0;
-    for (int i = threadIdx.x; i < nb; i += kBlock) s += partials[i];
-    s = block_sum(s);
+    for (int i = threadIdx.x; i < nb; i += kFinishBlock) s += partials[i];
+    s = wave_sum(s);
+    if ((threadIdx.x & (kWave - 1)) == 0) wsum[threadIdx.x / kWave] = s;
+    __syncthreads();
+    double t = 0.0;
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int i = 0; i < kFinishBlock / kWave; ++i) t += wsum[i];
+    }
+    return t;
+}
+
+__global__ __launch_bounds__(kFinishBlock) void k_finish(const double *__restrict__ partials, int nb,
+                                                         double *__restrict__ out, bool take_sqrt)
+{
+    const double s = finish_sum(partials, nb);
     if (threadIdx.x == 0) *out = take_sqrt ? std::sqrt(s) : s;
+}
+
+// Finishes of the device-resident CG iteration (unpreconditioned CG, the
+// vector operations of the BS paper's CG list):
+//  kStart: rr = r.r; history[0] = rr; convergence threshold tol2 * rr; the
+//          history entries after 0 are set to -1 (an iteration that runs
+//          overwrites its entry).
+//  kAlpha: alpha = rr / (p.q).
+//  kBeta:  rr' = r'.r'; beta = rr' / rr; rr = rr'; history[k+1] = rr';
+//          converged when rr' <= threshold (or rr' == 0).
+enum CgFinish { kStart = 0, kSetAlpha = 1, kSetBeta = 2 };
+
+__global__ __launch_bounds__(kFinishBlock) void k_cg_finish(const double *__restrict__ partials, int nb,
+                                                            double *__restrict__ cgs, double *__restrict__ hist,
+                                                            int k, int iters, double tol2, int mode)
+{
+    if (mode == kStart) {
+        for (int i = 1 + threadIdx.x; i <= iters; i += kFinishBlock) hist[i] = -1.0;
+    } else if (cgs[kDone] != 0.0) {
+        return;
+    }
+    const double s = finish_sum(partials, nb);
+    if (threadIdx.x != 0) return;
+    if (mode == kStart) {
+        cgs[kRR] = s;
+        cgs[kThreshold] = tol2 * s;
+        cgs[kDone] = (s == 0.0) ? 1.0 : 0.0;
+        hist[0] = s;
+    } else if (mode == kSetAlpha) {
+        cgs[kAlpha] = cgs[kRR] / s;
+    } else {
+        cgs[kBeta] = s / cgs[kRR];
+        cgs[kRR] = s;
+        hist[k + 1] = s;
+        if (s == 0.0 || s <= cgs[kThreshold]) cgs[kDone] = 1.0;
+    }
 }
 
 // ------------------------------------------------------- vector layout ----
@@ -169,10 +237,14 @@ __device__ __forceinline__ d2 axpy2(double a, d2 x, double b, d2 y)
     return r;
 }
 
+// The coefficients come by value (bs_axpy) or from device memory (the
+// p = r + beta p step of the device-resident CG iteration).
 template <int U>
-__global__ __launch_bounds__(kBlock) void k_axpy(Split sp, double a, const double *x, double b,
-                                                 double *y)
+__global__ __launch_bounds__(kBlock) void k_axpy(Split sp, Coef ca, const double *x, Coef cb, double *y,
+                                                 const double *cgs)
 {
+    if (skipped(cgs)) return;
+    const double a = ca.get(), b = cb.get();
     const d2 *xv = reinterpret_cast<const d2 *>(x + sp.head);
     d2 *yv = reinterpret_cast<d2 *>(y + sp.head);
     const int64_t stride = (int64_t)gridDim.x * kBlock * U;
@@ -258,10 +330,13 @@ __device__ __forceinline__ void cg2(double a, d2 p, d2 q, d2 &x, d2 &r)
 // past a later load and serialises the lane's loads, which at one block per
 // CU costs about a third of the bandwidth.
 template <int U>
-__global__ __launch_bounds__(kBlock) void k_cg_update(Split sp, double a, const double *__restrict__ p,
+__global__ __launch_bounds__(kBlock) void k_cg_update(Split sp, Coef ca, const double *__restrict__ p,
                                                       const double *__restrict__ q, double *__restrict__ x,
-                                                      double *__restrict__ r, double *__restrict__ partials)
+                                                      double *__restrict__ r, double *__restrict__ partials,
+                                                      const double *cgs)
 {
+    if (skipped(cgs)) return;
+    const double a = ca.get();
     const d2 *pv = reinterpret_cast<const d2 *>(p + sp.head);
     const d2 *qv = reinterpret_cast<const d2 *>(q + sp.head);
     d2 *xv = reinterpret_cast<d2 *>(x + sp.head);
@@ -326,8 +401,9 @@ __global__ __launch_bounds__(kBlock) void k_cg_update(Split sp, double a, const 
 // reads before the stores. The last, partial tile goes entry by entry.
 __global__ __launch_bounds__(kBlock) void k_scatter(int64_t nl, const int32_t *__restrict__ l2g,
                                                     const double *__restrict__ vg,
-                                                    double *__restrict__ vl)
+                                                    double *__restrict__ vl, const double *cgs)
 {
+    if (skipped(cgs)) return;
     constexpr int64_t kTile = 2LL * kBlock * kScatterPairs;  // entries per block
     const int64_t base = (int64_t)blockIdx.x * kTile;
     if (base + kTile <= nl) {
@@ -364,16 +440,24 @@ __global__ __launch_bounds__(kBlock) void k_scatter_scalar(int64_t nl, const int
 }
 
 // ---------------------------------------------------------- BS6 gather ----
+// Both gather kernels optionally fold a dot product into the same pass: with
+// kDot, each lane also accumulates v_G[g] * w[g] over its rows and the block
+// writes one partial (the p.q of a CG iteration, q = Z^T Z p, without a
+// second read of q). The gathered values are the same bits either way.
+
 // Row kernel (no plan): lane t of block b owns rows b*kBlock*R + t + kBlock*r
 // (r < R). It loads both offsets of every row, then the first M ids of every
 // row, then the v_L values they name, before summing any: three dependent
 // rounds of loads per block instead of two per entry. Rows longer than M
 // finish entry by entry. Each sum runs left to right from +0.0.
+template <bool kDot>
 __global__ __launch_bounds__(kBlock) void k_gather_rows(int64_t ng, const int32_t *__restrict__ off,
                                                         const int32_t *__restrict__ ids,
                                                         const double *__restrict__ vl,
-                                                        double *__restrict__ vg)
+                                                        double *__restrict__ vg, const double *__restrict__ w,
+                                                        double *__restrict__ partials, const double *cgs)
 {
+    if (skipped(cgs)) return;
     constexpr int M = kGatherRowM, R = kGatherRowR;
     const int64_t g0 = (int64_t)blockIdx.x * kBlock * R + threadIdx.x;
     int32_t a[R], b[R];
@@ -393,6 +477,7 @@ __global__ __launch_bounds__(kBlock) void k_gather_rows(int64_t ng, const int32_
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int k = 0; k < M; ++k) v[r][k] = id[r][k] >= 0 ? vl[id[r][k]] : 0.0;
+    double acc = 0.0;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int64_t g = g0 + (int64_t)r * kBlock;
@@ -403,6 +488,11 @@ __global__ __launch_bounds__(kBlock) void k_gather_rows(int64_t ng, const int32_
             if (a[r] + k < b[r]) s = s + v[r][k];
         for (int32_t j = a[r] + M; j < b[r]; ++j) s = s + vl[ids[j]];
         __builtin_nontemporal_store(s, vg + g);
+        if (kDot) acc = __builtin_fma(s, w[g], acc);
+    }
+    if (kDot) {
+        const double part = block_sum(acc);
+        if (threadIdx.x == 0) partials[blockIdx.x] = part;
     }
 }
 
@@ -413,22 +503,28 @@ __global__ __launch_bounds__(kBlock) void k_gather_rows(int64_t ng, const int32_
 // lanes on consecutive entries, fetches the named v_L values, all issued
 // before any is stored, stages them in LDS, and then each lane sums its rows
 // from LDS in ascending entry order. Blocks over capacity read global memory.
+template <bool kDot>
 __global__ __launch_bounds__(kBlock) void k_gather_plan(const int32_t *__restrict__ bstart,
                                                         const int32_t *__restrict__ off,
                                                         const int32_t *__restrict__ ids,
                                                         const double *__restrict__ vl,
-                                                        double *__restrict__ vg)
+                                                        double *__restrict__ vg, const double *__restrict__ w,
+                                                        double *__restrict__ partials, const double *cgs)
 {
+    if (skipped(cgs)) return;
     constexpr int K = kGatherCap / kBlock;  // entries per lane
     __shared__ int32_t so[kGatherCap + 1];
     __shared__ double stage[kGatherCap];
     const int32_t r0 = bstart[blockIdx.x], r1 = bstart[blockIdx.x + 1];
     const int32_t nr = r1 - r0;
+    double acc = 0.0;
+    bool staged = false;
     if (nr <= kGatherCap) {
         for (int32_t t = threadIdx.x; t <= nr; t += kBlock) so[t] = off[r0 + t];
         __syncthreads();
         const int32_t e0 = so[0], ne = so[nr] - e0;
         if (ne <= kGatherCap) {
+            staged = true;
             int32_t id[K];
 #pragma unroll
             for (int k = 0; k < K; ++k) {
@@ -449,14 +545,21 @@ __global__ __launch_bounds__(kBlock) void k_gather_plan(const int32_t *__restric
                 double s = 0.0;
                 for (int32_t j = a; j < b; ++j) s = s + stage[j];
                 __builtin_nontemporal_store(s, vg + r0 + r);
+                if (kDot) acc = __builtin_fma(s, w[r0 + r], acc);
             }
-            return;
         }
     }
-    for (int32_t g = r0 + threadIdx.x; g < r1; g += kBlock) {
-        double s = 0.0;
-        for (int32_t j = off[g]; j < off[g + 1]; ++j) s = s + vl[ids[j]];
-        vg[g] = s;
+    if (!staged) {
+        for (int32_t g = r0 + threadIdx.x; g < r1; g += kBlock) {
+            double s = 0.0;
+            for (int32_t j = off[g]; j < off[g + 1]; ++j) s = s + vl[ids[j]];
+            vg[g] = s;
+            if (kDot) acc = __builtin_fma(s, w[g], acc);
+        }
+    }
+    if (kDot) {
+        const double part = block_sum(acc);
+        if (threadIdx.x == 0) partials[blockIdx.x] = part;
     }
 }
 
@@ -509,6 +612,7 @@ struct bs_ctx {
     int cus;
     int max_partials;
     double *partials;  // first-stage reduction results, one per block
+    double *cgs;       // device-resident CG scalars (CgSlot)
 };
 
 namespace {
@@ -537,7 +641,6 @@ inline unsigned scalar_grid(const bs_ctx *c, int64_t n)
     int64_t g = (n + kBlock - 1) / kBlock;
     const int64_t cap = (int64_t)c->cus * 8;
     if (g > cap) g = cap;
-    if (g > c->max_partials) g = c->max_partials;
     if (g < 1) g = 1;
     return (unsigned)g;
 }
@@ -564,7 +667,32 @@ inline int check_ctx(const bs_ctx *c)
 
 int finish_launch(bs_ctx *c, unsigned nb, double *out, bool take_sqrt, hipStream_t st)
 {
-    hipLaunchKernelGGL(k_finish, dim3(1), dim3(kBlock), 0, st, c->partials, (int)nb, out, take_sqrt);
+    hipLaunchKernelGGL(k_finish, dim3(1), dim3(kFinishBlock), 0, st, c->partials, (int)nb, out, take_sqrt);
+    return launch_status();
+}
+
+// First stage of norm / dot into the context's partials; returns the block
+// count through *nb.
+int dot_stage(bs_ctx *c, int64_t n, const double *x, const double *y, bool square, hipStream_t st,
+              unsigned *nb)
+{
+    const void *ptrs[2] = {x, square ? x : y};
+    int64_t head;
+    if (common_head(ptrs, 2, &head)) {
+        const Split sp = split_of(n, head);
+        if (square) {
+            *nb = vector_grid(c, sp.n2, kNormShape, true);
+            hipLaunchKernelGGL((k_dot<kNormShape.unroll, true>), dim3(*nb), dim3(kBlock), 0, st, sp, x, x,
+                               c->partials);
+        } else {
+            *nb = vector_grid(c, sp.n2, kDotShape, true);
+            hipLaunchKernelGGL((k_dot<kDotShape.unroll, false>), dim3(*nb), dim3(kBlock), 0, st, sp, x, y,
+                               c->partials);
+        }
+    } else {
+        *nb = scalar_grid(c, n);
+        hipLaunchKernelGGL(k_dot_scalar, dim3(*nb), dim3(kBlock), 0, st, n, x, y, c->partials);
+    }
     return launch_status();
 }
 
@@ -572,26 +700,52 @@ int reduce_launch(bs_ctx *c, int64_t n, const double *x, const double *y, double
                   hipStream_t st)
 {
     if (n == 0) return finish_launch(c, 0, out, false, st);
-    const void *ptrs[2] = {x, square ? x : y};
-    int64_t head;
     unsigned nb;
-    if (common_head(ptrs, 2, &head)) {
-        const Split sp = split_of(n, head);
-        if (square) {
-            nb = vector_grid(c, sp.n2, kNormShape, true);
-            hipLaunchKernelGGL((k_dot<kNormShape.unroll, true>), dim3(nb), dim3(kBlock), 0, st, sp, x, x,
-                               c->partials);
-        } else {
-            nb = vector_grid(c, sp.n2, kDotShape, true);
-            hipLaunchKernelGGL((k_dot<kDotShape.unroll, false>), dim3(nb), dim3(kBlock), 0, st, sp, x, y,
-                               c->partials);
-        }
-    } else {
-        nb = scalar_grid(c, n);
-        hipLaunchKernelGGL(k_dot_scalar, dim3(nb), dim3(kBlock), 0, st, n, x, y, c->partials);
-    }
-    if (hipGetLastError() != hipSuccess) return BS_EHIP;
+    if (int s = dot_stage(c, n, x, y, square, st, &nb)) return s;
     return finish_launch(c, nb, out, square, st);
+}
+
+// Gather launch shared by bs_gather, bs_gather_dot and the CG iteration.
+int gather_launch(bs_ctx *c, int64_t ng, const int32_t *off, const int32_t *ids, const double *vl, double *vg,
+                  const int32_t *bstart, int64_t nblocks, const double *w, const double *cgs, hipStream_t st,
+                  unsigned *nb)
+{
+    if (bstart) {
+        *nb = (unsigned)nblocks;
+        if (w)
+            hipLaunchKernelGGL(k_gather_plan<true>, dim3(*nb), dim3(kBlock), 0, st, bstart, off, ids, vl, vg, w,
+                               c->partials, cgs);
+        else
+            hipLaunchKernelGGL(k_gather_plan<false>, dim3(*nb), dim3(kBlock), 0, st, bstart, off, ids, vl, vg,
+                               nullptr, nullptr, cgs);
+    } else {
+        const int64_t per = (int64_t)kBlock * kGatherRowR;
+        *nb = (unsigned)((ng + per - 1) / per);
+        if (w)
+            hipLaunchKernelGGL(k_gather_rows<true>, dim3(*nb), dim3(kBlock), 0, st, ng, off, ids, vl, vg, w,
+                               c->partials, cgs);
+        else
+            hipLaunchKernelGGL(k_gather_rows<false>, dim3(*nb), dim3(kBlock), 0, st, ng, off, ids, vl, vg,
+                               nullptr, nullptr, cgs);
+    }
+    return launch_status();
+}
+
+int gather_args(const bs_ctx *c, int64_t n_global, const int32_t *off, const int32_t *ids, const double *v_local,
+                double *v_global, const int32_t *block_starts, int64_t n_blocks, bool dot)
+{
+    if (n_global < 0 || (n_global > 0 && (!off || !ids || !v_local || !v_global))) return BS_EINVAL;
+    if (n_global >= INT32_MAX) return BS_ERANGE;
+    if (n_global > 0 && (misaligned(off, 4) || misaligned(ids, 4) || misaligned(v_local, 8) ||
+                         misaligned(v_global, 8)))
+        return BS_EALIGN;
+    if (block_starts && n_global > 0) {
+        if (n_blocks < 1 || n_blocks > n_global || misaligned(block_starts, 4)) return BS_EINVAL;
+    }
+    // the fused dot writes one partial per block
+    int64_t nb = block_starts ? n_blocks : (n_global + (int64_t)kBlock * kGatherRowR - 1) / ((int64_t)kBlock * kGatherRowR);
+    if (dot && nb > c->max_partials) return BS_ERANGE;
+    return BS_OK;
 }
 
 }  // namespace
@@ -611,7 +765,7 @@ const char *bs_strerror(int status)
     }
 }
 
-int bs_version(void) { return 200; }
+int bs_version(void) { return 300; }
 
 int bs_ctx_create(int device, bs_ctx **out)
 {
@@ -629,7 +783,10 @@ int bs_ctx_create(int device, bs_ctx **out)
     c->cus = cus;
     c->max_partials = kMaxPartials;
     c->partials = nullptr;
-    if (hipMalloc(&c->partials, sizeof(double) * kMaxPartials) != hipSuccess) {
+    c->cgs = nullptr;
+    if (hipMalloc(&c->partials, sizeof(double) * kMaxPartials) != hipSuccess ||
+        hipMalloc(&c->cgs, sizeof(double) * kCgSlots) != hipSuccess) {
+        if (c->partials) (void)hipFree(c->partials);
         delete c;
         return BS_ENOMEM;
     }
@@ -643,6 +800,7 @@ void bs_ctx_destroy(bs_ctx *c)
     if (hipSetDevice(c->device) == hipSuccess) {
         (void)hipDeviceSynchronize();
         (void)hipFree(c->partials);
+        (void)hipFree(c->cgs);
     }
     delete c;
 }
@@ -669,8 +827,8 @@ int bs_copy(bs_ctx *c, int64_t n, const double *x, double *y, void *stream)
     int64_t head;
     if (common_head(ptrs, 2, &head)) {
         const Split sp = split_of(n, head);
-        hipLaunchKernelGGL(k_copy<kCopyShape.unroll>, dim3(vector_grid(c, sp.n2, kCopyShape, false)), dim3(kBlock), 0,
-                           st, sp, x, y);
+        hipLaunchKernelGGL(k_copy<kCopyShape.unroll>, dim3(vector_grid(c, sp.n2, kCopyShape, false)), dim3(kBlock),
+                           0, st, sp, x, y);
     } else {
         hipLaunchKernelGGL(k_copy_scalar, dim3(scalar_grid(c, n)), dim3(kBlock), 0, st, n, x, y);
     }
@@ -688,8 +846,8 @@ int bs_axpy(bs_ctx *c, int64_t n, double alpha, const double *x, double beta, do
     int64_t head;
     if (common_head(ptrs, 2, &head)) {
         const Split sp = split_of(n, head);
-        hipLaunchKernelGGL(k_axpy<kAxpyShape.unroll>, dim3(vector_grid(c, sp.n2, kAxpyShape, false)), dim3(kBlock), 0,
-                           st, sp, alpha, x, beta, y);
+        hipLaunchKernelGGL(k_axpy<kAxpyShape.unroll>, dim3(vector_grid(c, sp.n2, kAxpyShape, false)), dim3(kBlock),
+                           0, st, sp, Coef{alpha, nullptr}, x, Coef{beta, nullptr}, y, nullptr);
     } else {
         hipLaunchKernelGGL(k_axpy_scalar, dim3(scalar_grid(c, n)), dim3(kBlock), 0, st, n, alpha, x, beta, y);
     }
@@ -728,8 +886,8 @@ int bs_cg_update(bs_ctx *c, int64_t n, double alpha, const double *p, const doub
     if (common_head(ptrs, 4, &head)) {
         const Split sp = split_of(n, head);
         nb = vector_grid(c, sp.n2, kCgShape, true);
-        hipLaunchKernelGGL(k_cg_update<kCgShape.unroll>, dim3(nb), dim3(kBlock), 0, st, sp, alpha, p, q, x, r,
-                           c->partials);
+        hipLaunchKernelGGL(k_cg_update<kCgShape.unroll>, dim3(nb), dim3(kBlock), 0, st, sp, Coef{alpha, nullptr}, p,
+                           q, x, r, c->partials, nullptr);
     } else {
         nb = scalar_grid(c, n);
         hipLaunchKernelGGL(k_cg_update_scalar, dim3(nb), dim3(kBlock), 0, st, n, alpha, p, q, x, r,
@@ -751,7 +909,8 @@ int bs_scatter(bs_ctx *c, int64_t n_local, const int32_t *l2g, const double *v_g
     if (!misaligned(l2g, 8) && !misaligned(v_local, 16)) {
         const int64_t per = 2LL * kBlock * kScatterPairs;
         const int64_t nb = (n_local + per - 1) / per;
-        hipLaunchKernelGGL(k_scatter, dim3((unsigned)nb), dim3(kBlock), 0, st, n_local, l2g, v_global, v_local);
+        hipLaunchKernelGGL(k_scatter, dim3((unsigned)nb), dim3(kBlock), 0, st, n_local, l2g, v_global, v_local,
+                           nullptr);
     } else {
         const int64_t nb = (n_local + kBlock - 1) / kBlock;
         hipLaunchKernelGGL(k_scatter_scalar, dim3((unsigned)nb), dim3(kBlock), 0, st, n_local, l2g, v_global,
@@ -764,23 +923,74 @@ int bs_gather(bs_ctx *c, int64_t n_global, const int32_t *off, const int32_t *id
               double *v_global, const int32_t *block_starts, int64_t n_blocks, void *stream)
 {
     if (int s = check_ctx(c)) return s;
-    if (n_global < 0 || (n_global > 0 && (!off || !ids || !v_local || !v_global))) return BS_EINVAL;
-    if (n_global >= INT32_MAX) return BS_ERANGE;
+    if (int s = gather_args(c, n_global, off, ids, v_local, v_global, block_starts, n_blocks, false)) return s;
     if (n_global == 0) return BS_OK;
-    if (misaligned(off, 4) || misaligned(ids, 4) || misaligned(v_local, 8) || misaligned(v_global, 8))
-        return BS_EALIGN;
+    unsigned nb;
+    return gather_launch(c, n_global, off, ids, v_local, v_global, block_starts, n_blocks, nullptr, nullptr,
+                         static_cast<hipStream_t>(stream), &nb);
+}
+
+int bs_gather_dot(bs_ctx *c, int64_t n_global, const int32_t *off, const int32_t *ids, const double *v_local,
+                  double *v_global, const int32_t *block_starts, int64_t n_blocks, const double *w,
+                  double *result, void *stream)
+{
+    if (int s = check_ctx(c)) return s;
+    if (!result || (n_global > 0 && !w)) return BS_EINVAL;
+    if (int s = gather_args(c, n_global, off, ids, v_local, v_global, block_starts, n_blocks, true)) return s;
+    if (misaligned(result, 8) || (n_global > 0 && misaligned(w, 8))) return BS_EALIGN;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (block_starts) {
-        if (n_blocks < 1 || n_blocks > n_global || misaligned(block_starts, 4)) return BS_EINVAL;
-        hipLaunchKernelGGL(k_gather_plan, dim3((unsigned)n_blocks), dim3(kBlock), 0, st, block_starts, off, ids,
-                           v_local, v_global);
-    } else {
-        const int64_t per = (int64_t)kBlock * kGatherRowR;
-        const int64_t nb = (n_global + per - 1) / per;
-        hipLaunchKernelGGL(k_gather_rows, dim3((unsigned)nb), dim3(kBlock), 0, st, n_global, off, ids, v_local,
-                           v_global);
+    if (n_global == 0) return finish_launch(c, 0, result, false, st);
+    unsigned nb;
+    if (int s = gather_launch(c, n_global, off, ids, v_local, v_global, block_starts, n_blocks, w, nullptr, st,
+                              &nb))
+        return s;
+    return finish_launch(c, nb, result, false, st);
+}
+
+int bs_cg_solve(bs_ctx *c, int64_t n_global, int64_t n_local, const int32_t *l2g, const int32_t *off,
+                const int32_t *ids, const int32_t *block_starts, int64_t n_blocks, double *x, double *r,
+                double *p, double *q, double *p_local, int iters, double tol, double *rr_hist, void *stream)
+{
+    if (int s = check_ctx(c)) return s;
+    if (n_global < 1 || n_local < 1 || iters < 0 || !(tol >= 0.0) || !l2g || !x || !r || !p || !q || !p_local ||
+        !rr_hist)
+        return BS_EINVAL;
+    if (n_local > INT32_MAX) return BS_ERANGE;
+    if (int s = gather_args(c, n_global, off, ids, p_local, q, block_starts, n_blocks, true)) return s;
+    const void *vec[6] = {x, r, p, q, p_local, rr_hist};
+    for (const void *v : vec)
+        if (misaligned(v, 16) && v != rr_hist) return BS_EALIGN;
+    if (misaligned(rr_hist, 8) || misaligned(l2g, 8)) return BS_EALIGN;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const Split sp = split_of(n_global, 0);
+    const double *cgs = c->cgs;
+    // rr0 = r.r, history, threshold
+    unsigned nb;
+    if (int s = dot_stage(c, n_global, r, r, true, st, &nb)) return s;
+    hipLaunchKernelGGL(k_cg_finish, dim3(1), dim3(kFinishBlock), 0, st, c->partials, (int)nb, c->cgs, rr_hist, 0,
+                       iters, tol * tol, (int)kStart);
+    const int64_t sc_per = 2LL * kBlock * kScatterPairs;
+    const unsigned sc_nb = (unsigned)((n_local + sc_per - 1) / sc_per);
+    const unsigned cg_nb = vector_grid(c, sp.n2, kCgShape, true);
+    const unsigned ax_nb = vector_grid(c, sp.n2, kAxpyShape, false);
+    for (int k = 0; k < iters; ++k) {
+        // q = Z^T Z p and p.q in the gather's pass; alpha = rr / p.q
+        hipLaunchKernelGGL(k_scatter, dim3(sc_nb), dim3(kBlock), 0, st, n_local, l2g, p, p_local, cgs);
+        if (int s = gather_launch(c, n_global, off, ids, p_local, q, block_starts, n_blocks, p, cgs, st, &nb))
+            return s;
+        hipLaunchKernelGGL(k_cg_finish, dim3(1), dim3(kFinishBlock), 0, st, c->partials, (int)nb, c->cgs,
+                           rr_hist, k, iters, 0.0, (int)kSetAlpha);
+        // x += alpha p, r -= alpha q, r.r; beta = rr' / rr
+        hipLaunchKernelGGL(k_cg_update<kCgShape.unroll>, dim3(cg_nb), dim3(kBlock), 0, st, sp,
+                           Coef{0.0, cgs + kAlpha}, p, q, x, r, c->partials, cgs);
+        hipLaunchKernelGGL(k_cg_finish, dim3(1), dim3(kFinishBlock), 0, st, c->partials, (int)cg_nb, c->cgs,
+                           rr_hist, k, iters, 0.0, (int)kSetBeta);
+        // p = (1 r) + (beta p)
+        hipLaunchKernelGGL(k_axpy<kAxpyShape.unroll>, dim3(ax_nb), dim3(kBlock), 0, st, sp, Coef{1.0, nullptr}, r,
+                           Coef{0.0, cgs + kBeta}, p, cgs);
+        if (hipGetLastError() != hipSuccess) return BS_EHIP;
     }
-    return launch_status();
+    return BS_OK;
 }
 
 }  // extern "C"

@@ -129,6 +129,39 @@ int bs_gather(bs_ctx *ctx, int64_t n_global, const int32_t *off, const int32_t *
               const double *v_local, double *v_global, const int32_t *block_starts,
               int64_t n_blocks, void *stream);
 
+/* BS6 gather with the inner product of the CG iteration folded into the same
+ * pass (arXiv 2009.10917, the CG vector-operation list: q = A p followed by
+ * p.q): v_global as bs_gather computes it (same bits), and *result =
+ * sum over g of v_global[g]*w[g] into the device double `result`, reduced in
+ * a fixed order (repeatable bits, relative 1e-12 of the exact value). w is
+ * double[n_global], distinct from v_global. Other arguments and errors as
+ * bs_gather; BS_ERANGE if the gather would use more blocks than the context
+ * holds partials (bs_ctx_info). */
+int bs_gather_dot(bs_ctx *ctx, int64_t n_global, const int32_t *off, const int32_t *ids,
+                  const double *v_local, double *v_global, const int32_t *block_starts,
+                  int64_t n_blocks, const double *w, double *result, void *stream);
+
+/* Device-resident unpreconditioned Conjugate Gradient on A = Z^T Z (the
+ * element operator taken as the identity: the streaming skeleton of the CG
+ * method whose vector operations the BS tests isolate, arXiv 2009.10917, CG
+ * vector-operation list and the fused update of the BS tests). Runs up to
+ * `iters` iterations on `stream` with no host synchronisation: alpha and beta
+ * are computed on the device. Each iteration: p_local = Z p (bs_scatter);
+ * q = Z^T p_local with p.q in the same pass (bs_gather_dot); alpha = rr/p.q;
+ * x += alpha p, r -= alpha q, rr' = r.r (bs_cg_update); beta = rr'/rr;
+ * p = (1 r) + (beta p) (bs_axpy). On entry x, r, p hold x0, r0 = b - A x0 and
+ * p0 = r0 (for x0 = 0: r = p = b). rr_hist (device double[iters+1]) receives
+ * r.r before the first iteration and after each; once rr <= tol^2 * rr0 (or
+ * rr == 0) the remaining iterations do nothing and their entries stay -1.
+ * x, r, p, q: distinct device double[n_global]; p_local: device
+ * double[n_local]; all 16-byte aligned (BS_EALIGN), l2g 8-byte aligned.
+ * l2g, off, ids, block_starts as bs_scatter / bs_gather. Uses the context's
+ * scratch: one solve at a time per context. */
+int bs_cg_solve(bs_ctx *ctx, int64_t n_global, int64_t n_local, const int32_t *l2g,
+                const int32_t *off, const int32_t *ids, const int32_t *block_starts,
+                int64_t n_blocks, double *x, double *r, double *p, double *q, double *p_local,
+                int iters, double tol, double *rr_hist, void *stream);
+
 /* ---------------------------------------------------- host-side tables --
  * These run on the host, need no GPU, and write caller-allocated host arrays.
  */

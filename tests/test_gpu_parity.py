@@ -397,3 +397,76 @@ def test_cg_sequence_matches_oracle(env):
         assert_rel(h, oh, "rr")
     assert math.sqrt(hist[-1] / hist[0]) < 1e-13
     assert np.allclose(host(x), ox, rtol=1e-12, atol=1e-14)
+
+
+# ----------------------------------------- gather + dot, device-resident CG ----
+
+@pytest.mark.parametrize("name", ["c1_box8_N3", "c2_box32_N7"])
+def test_gather_dot(env, name):
+    """bs_gather_dot: the gather's bits unchanged, w . v_G to 1e-12."""
+    bs, orc, torch, d = env
+    l2g, off, ids, ol2g, ng = mesh_case(env, name)
+    vlv = bs_inputs.uniform_pm1(86, l2g.size)
+    wv = bs_inputs.uniform_pm1(87, ng)
+    want = orc.gather(ol2g, vlv, ng)
+    want_dot = orc.dot(want, wv)
+    doff, dids, dvl, dw = dev(torch, d, off), dev(torch, d, ids), dev(torch, d, vlv), dev(torch, d, wv)
+    for plan in (None, bs.bs_gather_plan(off, 1024)):
+        vg = torch.full((ng,), np.nan, dtype=torch.float64, device=d)
+        got = bs.bs_gather_dot(doff, dids, dvl, vg, dw, None if plan is None else dev(torch, d, plan)).item()
+        assert_bits(host(vg), want, f"gather_dot values {name}")
+        assert_rel(got, want_dot, f"gather_dot {name}")
+
+
+def cg_setup(env, name):
+    bs, orc, torch, d = env
+    l2g, off, ids, ol2g, ng = mesh_case(env, name)
+    b = bs_inputs.uniform_pm1(bs_inputs.base_seed(name) + 3, ng)
+    t = {"l2g": dev(torch, d, l2g), "off": dev(torch, d, off), "ids": dev(torch, d, ids),
+         "plan": dev(torch, d, bs.bs_gather_plan(off, 1024)),
+         "x": torch.zeros(ng, dtype=torch.float64, device=d), "r": dev(torch, d, b), "p": dev(torch, d, b),
+         "q": torch.empty(ng, dtype=torch.float64, device=d),
+         "pl": torch.empty(l2g.size, dtype=torch.float64, device=d)}
+    return t, ol2g, ng, b
+
+
+@pytest.mark.parametrize("name", ["c1_box8_N3", "c2_box32_N7"])
+def test_cg_solve_matches_oracle(env, name):
+    """Four device-resident CG iterations on Z^T Z against the oracle's CG:
+    same residual history to 1e-12 while it is significant, same x, and
+    convergence (A = diag(m), m in {1,2,4,8}: at most 4 steps)."""
+    bs, orc, torch, d = env
+    t, ol2g, ng, b = cg_setup(env, name)
+    ox, orr_, ohist = orc.cg_sequence(ol2g, ng, b, 4)
+    for plan in (None, t["plan"]):
+        x, r, p = t["x"].clone(), t["r"].clone(), t["p"].clone()
+        hist = bs.bs_cg_solve(t["l2g"], t["off"], t["ids"], x, r, p, t["q"], t["pl"], 4, 0.0, plan)
+        h = host(hist)
+        assert_rel(h[0], ohist[0], "rr0")
+        assert_rel(h[1], ohist[1], "rr1")
+        assert math.sqrt(h[4] / h[0]) < 1e-13
+        m = np.diff(host(t["off"]))
+        assert np.allclose(host(x), ox, rtol=1e-12, atol=1e-14)
+        assert np.allclose(host(x), b / m, rtol=1e-12, atol=1e-14)
+
+
+def test_cg_solve_early_exit_and_zero_iterations(env):
+    """A tolerance stops the iteration on the device: later history entries
+    stay -1 and x no longer changes; iters = 0 only measures rr0."""
+    bs, orc, torch, d = env
+    t, ol2g, ng, b = cg_setup(env, "c1_box8_N3")
+    x, r, p = t["x"].clone(), t["r"].clone(), t["p"].clone()
+    hist = host(bs.bs_cg_solve(t["l2g"], t["off"], t["ids"], x, r, p, t["q"], t["pl"], 12, 1e-10, t["plan"]))
+    done = [i for i in range(1, 13) if hist[i] >= 0]
+    assert 1 <= len(done) <= 5 and done == list(range(1, len(done) + 1))
+    assert np.all(hist[len(done) + 1:] == -1.0)
+    assert math.sqrt(hist[len(done)] / hist[0]) <= 1e-10
+    x2, r2, p2 = t["x"].clone(), t["r"].clone(), t["p"].clone()
+    h0 = host(bs.bs_cg_solve(t["l2g"], t["off"], t["ids"], x2, r2, p2, t["q"], t["pl"], 0, 0.0, t["plan"]))
+    assert h0.size == 1 and abs(h0[0] - orc.dot(b, b)) <= 1e-12 * orc.dot(b, b)
+    assert torch.count_nonzero(x2).item() == 0
+    # a zero right-hand side is converged before the first step
+    z = torch.zeros_like(t["r"])
+    hz = host(bs.bs_cg_solve(t["l2g"], t["off"], t["ids"], z.clone(), z.clone(), z.clone(), t["q"], t["pl"], 3,
+                             0.0, t["plan"]))
+    assert list(hz) == [0.0, -1.0, -1.0, -1.0]
