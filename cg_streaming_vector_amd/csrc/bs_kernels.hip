@@ -77,7 +77,7 @@ constexpr VecShape kDotShape{4, 1};
 constexpr VecShape kNormShape{4, 2};
 constexpr VecShape kCgShape{4, 1};
 
-constexpr int kScatterPairs = 16;  // index pairs per lane in the scatter kernel
+constexpr int kScatterPairs = 32;  // index pairs per lane in the scatter kernel
 constexpr int kGatherCap = 1024;   // CSR entries and rows a gather block stages in LDS
 constexpr int kGatherRowM = 4;     // entries per row loaded up front (row kernel)
 constexpr int kGatherRowR = 2;     // rows per lane (row kernel)
@@ -398,7 +398,41 @@ __global__ __launch_bounds__(kBlock) void k_cg_update(Split sp, Coef ca, const d
 // P = kBlock*kScatterPairs pairs per block), i.e. local entries 2*pair and
 // 2*pair+1: one 8-byte index load, two reads of v_G, one 16-byte store each.
 // All index loads of the lane are issued before the reads they feed, and all
-// reads before the stores. The last, partial tile goes entry by entry.
+// reads before the stores. Full tiles take a path with no bounds tests (they
+// would cost the compiler its freedom to keep every load in flight); in the
+// last, partial tile a pair past the end is skipped and a pair cut by the end
+// goes as one 4-byte load and one 8-byte store.
+template <bool kFull>
+__device__ __forceinline__ void scatter_tile(int64_t base, int64_t nl, const int32_t *__restrict__ l2g,
+                                             const double *__restrict__ vg, double *__restrict__ vl)
+{
+    i2 id[kScatterPairs];
+#pragma unroll
+    for (int u = 0; u < kScatterPairs; ++u) {
+        const int64_t e = base + 2 * ((int64_t)u * kBlock + threadIdx.x);
+        if (kFull || e + 1 < nl) {
+            id[u] = __builtin_nontemporal_load(reinterpret_cast<const i2 *>(l2g + e));
+        } else {
+            id[u].x = e < nl ? l2g[e] : -1;
+            id[u].y = -1;
+        }
+    }
+    d2 v[kScatterPairs];
+#pragma unroll
+    for (int u = 0; u < kScatterPairs; ++u) {
+        v[u].x = id[u].x >= 0 ? vg[id[u].x] : 0.0;
+        v[u].y = id[u].y >= 0 ? vg[id[u].y] : 0.0;
+    }
+#pragma unroll
+    for (int u = 0; u < kScatterPairs; ++u) {
+        const int64_t e = base + 2 * ((int64_t)u * kBlock + threadIdx.x);
+        if (kFull || e + 1 < nl)
+            st2(reinterpret_cast<d2 *>(vl + e), v[u]);
+        else if (e < nl)
+            vl[e] = v[u].x;
+    }
+}
+
 __global__ __launch_bounds__(kBlock) void k_scatter(int64_t nl, const int32_t *__restrict__ l2g,
                                                     const double *__restrict__ vg,
                                                     double *__restrict__ vl, const double *cgs)
@@ -406,26 +440,10 @@ __global__ __launch_bounds__(kBlock) void k_scatter(int64_t nl, const int32_t *_
     if (skipped(cgs)) return;
     constexpr int64_t kTile = 2LL * kBlock * kScatterPairs;  // entries per block
     const int64_t base = (int64_t)blockIdx.x * kTile;
-    if (base + kTile <= nl) {
-        const i2 *ip = reinterpret_cast<const i2 *>(l2g + base) + threadIdx.x;
-        d2 *op = reinterpret_cast<d2 *>(vl + base) + threadIdx.x;
-        i2 id[kScatterPairs];
-#pragma unroll
-        for (int u = 0; u < kScatterPairs; ++u) id[u] = __builtin_nontemporal_load(ip + u * kBlock);
-        d2 v[kScatterPairs];
-#pragma unroll
-        for (int u = 0; u < kScatterPairs; ++u) {
-            v[u].x = id[u].x >= 0 ? vg[id[u].x] : 0.0;
-            v[u].y = id[u].y >= 0 ? vg[id[u].y] : 0.0;
-        }
-#pragma unroll
-        for (int u = 0; u < kScatterPairs; ++u) st2(op + u * kBlock, v[u]);
-    } else {
-        for (int64_t i = base + threadIdx.x; i < nl; i += kBlock) {
-            const int32_t g = l2g[i];
-            vl[i] = g >= 0 ? vg[g] : 0.0;
-        }
-    }
+    if (base + kTile <= nl)
+        scatter_tile<true>(base, nl, l2g, vg, vl);
+    else
+        scatter_tile<false>(base, nl, l2g, vg, vl);
 }
 
 // Fallback for index or value pointers without 8/16-byte alignment.

@@ -335,7 +335,7 @@ def test_gather_plan_over_capacity_blocks(env):
 
 def test_scatter_ragged_and_misaligned(env):
     bs, orc, torch, d = env
-    for nl in [1, 3, 5, 1023, 1025, 4097, 8191, 8192, 8193, 3 * 8192 + 77]:
+    for nl in [1, 3, 5, 1023, 1025, 4097, 8191, 8193, 16383, 16384, 16385, 3 * 16384 + 77, 5 * 16384 - 1]:
         ng = 50
         l2g = (bs_inputs.splitmix64(81, nl) % np.uint64(ng)).astype(np.int32)
         vgv = bs_inputs.uniform_pm1(82, ng)
