@@ -47,7 +47,7 @@ OPS = ["copy", "axpy", "norm", "dot", "cg_update", "scatter", "gather"]
 KERNEL_NAME = {  # op -> its kernels as rocprofv3 names them (namespace and arguments stripped)
     "copy": ["k_copy<1>"], "axpy": ["k_axpy<1>"], "norm": ["k_dot<4, true>", "k_finish"],
     "dot": ["k_dot<4, false>", "k_finish"], "cg_update": ["k_cg_update<4>", "k_finish"],
-    "scatter": ["k_scatter"], "gather": ["k_gather_plan"],
+    "scatter": ["k_scatter"], "gather": ["k_gather_plan<false>"],
 }
 GATHER_NPB = 1024
 
