@@ -16,13 +16,15 @@ operation count every array once, index tables included:
   scatter 12 N_L + 8 N_G, gather 12 N_L + 12 N_G + 4.
 
 Printed: one JSON line (value = bytes of a step / host-timed seconds of a
-step, whole job), with per-operation times from HIP events recorded on the
-launch stream during the same timed steps, the roofline of the dominant
-kernel, and the CPU oracle timed on a bounded sample of the same step.
-Optional: --sweep fits the latency-plus-bandwidth model T(B) = T0 + B/W_max
-(eq. 8) over n = 2^10 .. 2^28 and reports B_0.8 = 4 T0 W_max (eq. 10);
---workloads times the shuffled 40^3 order-5 and 24^3 order-15 meshes and
-the CG streaming sequence. Their results go to --out (JSON), not stdout.
+step, whole job), with per-operation times (HIP events around loops of
+back-to-back launches that cycle through distinct array sets, so every launch
+reads cold data), the roofline of the dominant operation (HIP events around
+it in every timed step), and the CPU oracle timed on a bounded sample of the
+same step. Optional: --sweep fits the latency-plus-bandwidth model
+T(B) = T0 + B/W_max (eq. 8) over n = 2^10 .. 2^28 and reports
+B_0.8 = 4 T0 W_max (eq. 10); --workloads times the shuffled 40^3 order-5 and
+24^3 order-15 meshes and the CG streaming sequence (host-driven and
+device-resident). Their results go to --out (JSON), not stdout.
 """
 from __future__ import annotations
 
