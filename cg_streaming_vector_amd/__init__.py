@@ -60,6 +60,9 @@ SIGNATURES = {
     "bs_scatter": ([_ptr, _i64, _ptr, _ptr, _ptr, _ptr], _int),
     "bs_gather": ([_ptr, _i64, _ptr, _ptr, _ptr, _ptr, _ptr, _i64, _ptr], _int),
     "bs_gather_dot": ([_ptr, _i64, _ptr, _ptr, _ptr, _ptr, _ptr, _i64, _ptr, _ptr, _ptr], _int),
+    "bs_scale": ([_ptr, _i64, _ptr, _ptr, _ptr, _ptr], _int),
+    "bs_gll": ([_int, _ptr, _ptr], _int),
+    "bs_mesh_box_mass": ([_int, _int, _int, _int, _ptr], _int),
     "bs_cg_solve": ([_ptr, _i64, _i64, _ptr, _ptr, _ptr, _ptr, _i64, _ptr, _ptr, _ptr, _ptr, _ptr, _int, _dbl,
                      _ptr, _ptr], _int),
     "bs_mesh_box_count": ([_int, _int, _int, _int, ctypes.POINTER(_i64), ctypes.POINTER(_i64)], _int),
@@ -269,6 +272,34 @@ def bs_gather(off, ids, v_local, v_global, block_starts=None, *, ctx=None, strea
     return v_global
 
 
+def bs_scale(x, d, y, *, ctx=None, stream=None):
+    """y = x / d elementwise (y may be x); returns y."""
+    import torch
+    if not (x.numel() == d.numel() == y.numel()):
+        raise ValueError("x, d, y differ in length")
+    ctx = _ctx_dev(x, ctx)
+    _check(_lib().bs_scale(ctx.handle, x.numel(), _dev_tensor(x, torch.float64, "x"),
+                           _dev_tensor(d, torch.float64, "d"), _dev_tensor(y, torch.float64, "y"),
+                           _stream(stream, x.device)), "bs_scale")
+    return y
+
+
+def bs_gll(order):
+    """(nodes, weights) of the GLL rule of degree `order` (numpy, host)."""
+    r = np.empty(int(order) + 1, dtype=np.float64)
+    w = np.empty(int(order) + 1, dtype=np.float64)
+    _check(_lib().bs_gll(int(order), r.ctypes.data, w.ctypes.data), "bs_gll")
+    return r, w
+
+
+def bs_mesh_box_mass(ex, ey, ez, order):
+    """Local lumped-mass weights of the unit-hexahedron box mesh (numpy)."""
+    nl, _ = bs_mesh_box_count(ex, ey, ez, order)
+    w = np.empty(nl, dtype=np.float64)
+    _check(_lib().bs_mesh_box_mass(ex, ey, ez, order, w.ctypes.data), "bs_mesh_box_mass")
+    return w
+
+
 def bs_gather_dot(off, ids, v_local, v_global, w, block_starts=None, out=None, *, ctx=None, stream=None):
     """BS6 with w . v_global in the same pass: returns the one-element out."""
     import torch
@@ -370,6 +401,6 @@ def bs_gather_plan(off, nodes_per_block=1024):
 __all__ = [
     "BSError", "Context", "context", "LIB_PATH", "SIGNATURES",
     "bs_copy", "bs_axpy", "bs_norm", "bs_dot", "bs_cg_update", "bs_scatter", "bs_gather",
-    "bs_gather_dot", "bs_cg_solve",
+    "bs_gather_dot", "bs_cg_solve", "bs_scale", "bs_gll", "bs_mesh_box_mass",
     "bs_mesh_box_count", "bs_mesh_box_l2g", "bs_validate_l2g", "bs_index_g2l", "bs_gather_plan",
 ]

@@ -13,6 +13,7 @@
 // axis, and the node (i,j,k) of element (cx,cy,cz) the lattice point
 // (cx*order + i, cy*order + j, cz*order + k): a closed form, no search.
 
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <vector>
@@ -77,6 +78,65 @@ int bs_mesh_box_l2g(int ex, int ey, int ez, int order, const int32_t *elem_perm,
             }
         }
     }
+    return BS_OK;
+}
+
+int bs_gll(int order, double *nodes, double *weights)
+{
+    if (order < 1 || !nodes || !weights) return BS_EINVAL;
+    const int n = order;
+    // Legendre P_n and P_{n-1} at t by the three-term recurrence
+    auto legendre = [n](double t, double &pn, double &pn1) {
+        double a = 1.0, b = t;
+        for (int k = 2; k <= n; ++k) {
+            const double c = ((2.0 * k - 1.0) * t * b - (k - 1.0) * a) / k;
+            a = b;
+            b = c;
+        }
+        pn = (n == 0) ? 1.0 : b;
+        pn1 = (n == 0) ? 0.0 : a;
+    };
+    // interior nodes: roots of q(t) = P_{n+1}(t) - P_{n-1}(t), which vanishes
+    // exactly at the GLL points (q = (2n+1)/(n(n+1)) (t^2-1) P_n'(t)); Newton
+    // with q'(t) = (2n+1) P_n(t), from the Chebyshev-Gauss-Lobatto points
+    nodes[0] = -1.0;
+    nodes[n] = 1.0;
+    for (int i = 1; i < n; ++i) {
+        double t = -std::cos(M_PI * i / n);
+        for (int it = 0; it < 60; ++it) {
+            double pn, pn1;
+            legendre(t, pn, pn1);
+            const double pn2 = ((2.0 * n + 1.0) * t * pn - n * pn1) / (n + 1.0);  // P_{n+1}
+            const double q = pn2 - pn1;
+            const double dq = (2.0 * n + 1.0) * pn;
+            const double step = q / dq;
+            t -= step;
+            if (std::fabs(step) <= 4e-16 * std::fabs(t) + 1e-300) break;
+        }
+        nodes[i] = t;
+    }
+    for (int i = 0; i <= n; ++i) {
+        double pn, pn1;
+        legendre(nodes[i], pn, pn1);
+        weights[i] = 2.0 / (n * (n + 1.0) * pn * pn);
+    }
+    return BS_OK;
+}
+
+int bs_mesh_box_mass(int ex, int ey, int ez, int order, double *w_local)
+{
+    int64_t nl, ng;
+    if (int s = bs_mesh_box_count(ex, ey, ez, order, &nl, &ng)) return s;
+    if (!w_local) return BS_EINVAL;
+    const int64_t nq = order + 1, Np = nq * nq * nq, K = (int64_t)ex * ey * ez;
+    std::vector<double> r(nq), w(nq), block(Np);
+    bs_gll(order, r.data(), w.data());
+    // one element's weights, w_i w_j w_k times the Jacobian 1/8 of the map
+    // from [-1,1]^3 onto a unit cube; every element of the box is a unit cube
+    for (int64_t k = 0; k < nq; ++k)
+        for (int64_t j = 0; j < nq; ++j)
+            for (int64_t i = 0; i < nq; ++i) block[i + nq * (j + nq * k)] = w[i] * w[j] * w[k] / 8.0;
+    for (int64_t e = 0; e < K; ++e) std::memcpy(w_local + e * Np, block.data(), sizeof(double) * Np);
     return BS_OK;
 }
 

@@ -270,6 +270,45 @@ __global__ __launch_bounds__(kBlock) void k_axpy(Split sp, Coef ca, const double
     }
 }
 
+// ------------------------------------------- pointwise scale y = x / d ----
+// The 1/m scaling by the lumped mass ("GPU accelerated spectral finite
+// elements on all-hex meshes", coarse-grid correction). Each quotient is one
+// correctly rounded IEEE division. y may be x (in place).
+template <int U>
+__global__ __launch_bounds__(kBlock) void k_scale(Split sp, const double *x, const double *d, double *y)
+{
+    const d2 *xv = reinterpret_cast<const d2 *>(x + sp.head);
+    const d2 *dv = reinterpret_cast<const d2 *>(d + sp.head);
+    d2 *yv = reinterpret_cast<d2 *>(y + sp.head);
+    const int64_t stride = (int64_t)gridDim.x * kBlock * U;
+    int64_t i = (int64_t)blockIdx.x * kBlock * U + threadIdx.x;
+    for (; i + (U - 1) * kBlock < sp.n2; i += stride) {
+        d2 vx[U], vd[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            vx[u] = ld2(xv + i + u * kBlock);
+            vd[u] = ld2(dv + i + u * kBlock);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) st2(yv + i + u * kBlock, vx[u] / vd[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t k = i + u * kBlock;
+        if (k < sp.n2) st2(yv + k, ld2(xv + k) / ld2(dv + k));
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (sp.head) y[0] = x[0] / d[0];
+        if (sp.tail >= 0) y[sp.tail] = x[sp.tail] / d[sp.tail];
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void k_scale_scalar(int64_t n, const double *x, const double *d, double *y)
+{
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += (int64_t)gridDim.x * kBlock)
+        y[i] = x[i] / d[i];
+}
+
 // ------------------------------------------------- BS3 norm, BS4 dot ----
 // First stage of both: with kSquare it sums x[i]^2 (y is ignored). The grid
 // holds one or two blocks per CU, so the kernel never needs more than two
@@ -868,6 +907,25 @@ int bs_axpy(bs_ctx *c, int64_t n, double alpha, const double *x, double beta, do
                            0, st, sp, Coef{alpha, nullptr}, x, Coef{beta, nullptr}, y, nullptr);
     } else {
         hipLaunchKernelGGL(k_axpy_scalar, dim3(scalar_grid(c, n)), dim3(kBlock), 0, st, n, alpha, x, beta, y);
+    }
+    return launch_status();
+}
+
+int bs_scale(bs_ctx *c, int64_t n, const double *x, const double *d, double *y, void *stream)
+{
+    if (int s = check_ctx(c)) return s;
+    if (n < 0 || (n > 0 && (!x || !d || !y))) return BS_EINVAL;
+    if (n == 0) return BS_OK;
+    if (misaligned(x, 8) || misaligned(d, 8) || misaligned(y, 8)) return BS_EALIGN;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const void *ptrs[3] = {x, d, y};
+    int64_t head;
+    if (common_head(ptrs, 3, &head)) {
+        const Split sp = split_of(n, head);
+        hipLaunchKernelGGL(k_scale<kAxpyShape.unroll>, dim3(vector_grid(c, sp.n2, kAxpyShape, false)), dim3(kBlock),
+                           0, st, sp, x, d, y);
+    } else {
+        hipLaunchKernelGGL(k_scale_scalar, dim3(scalar_grid(c, n)), dim3(kBlock), 0, st, n, x, d, y);
     }
     return launch_status();
 }

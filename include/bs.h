@@ -81,6 +81,13 @@ int bs_copy(bs_ctx *ctx, int64_t n, const double *x, double *y, void *stream);
 int bs_axpy(bs_ctx *ctx, int64_t n, double alpha, const double *x, double beta,
             double *y, void *stream);
 
+/* Pointwise scale y[i] = x[i] / d[i], one correctly rounded division each:
+ * the scaling of a global vector by the inverted (lumped, diagonal) mass
+ * matrix (arXiv 1506.05996, coarse-grid correction: y = r / m), the one
+ * streaming operation that a lumped-mass / Jacobi step adds to the BS set.
+ * x, d, y contiguous double[n]; y == x allowed. Bit-exact. */
+int bs_scale(bs_ctx *ctx, int64_t n, const double *x, const double *d, double *y, void *stream);
+
 /* BS3 norm (arXiv 2009.10917, CG vector-operation list and the two-kernel
  * reduction of the implementation section): *result = sqrt(sum x[i]^2), the
  * 2-norm, written to the device double `result`. The sum is reduced in a
@@ -182,6 +189,21 @@ int bs_mesh_box_count(int ex, int ey, int ez, int order, int64_t *n_local, int64
  * int32[n_local]. */
 int bs_mesh_box_l2g(int ex, int ey, int ez, int order, const int32_t *elem_perm,
                     const int32_t *node_perm, int32_t *l2g);
+
+/* Gauss-Lobatto-Legendre points and weights of degree `order` on [-1, 1]:
+ * nodes double[order+1] ascending (the end points and the roots of P_order'),
+ * weights double[order+1], w_i = 2 / (order (order+1) P_order(r_i)^2). These
+ * are the element nodes of arXiv 2009.10917 eqs. 1-2. BS_EINVAL for order < 1
+ * or a NULL output. */
+int bs_gll(int order, double *nodes, double *weights);
+
+/* Local lumped-mass weights of the box mesh of unit hexahedra: every element's
+ * node (i,j,k) gets w_i w_j w_k / 8 (GLL weights times the Jacobian of the map
+ * from [-1,1]^3 onto the unit cube), in the local layout of bs_mesh_box_l2g.
+ * The lumped global mass is their gather, m = Z^T w_L (arXiv 1506.05996,
+ * coarse-grid correction: m_N as the global components of the local weights).
+ * w_local receives double[n_local]. Errors as bs_mesh_box_count. */
+int bs_mesh_box_mass(int ex, int ey, int ez, int order, double *w_local);
 
 /* Check that every id is < n_global (negative ids are masks): BS_OK or
  * BS_EINVAL. */

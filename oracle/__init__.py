@@ -74,6 +74,12 @@ def lib():
         L.or_mesh_box.restype = _c_int64
         L.or_g2l.argtypes = [_c_int64, _c_int64, _ptr, _ptr, _ptr]
         L.or_g2l.restype = _c_int64
+        L.or_gll_weights.argtypes = [ctypes.c_int, _ptr]
+        L.or_gll_weights.restype = ctypes.c_int
+        L.or_mesh_box_mass.argtypes = [ctypes.c_int] * 4 + [_ptr]
+        L.or_mesh_box_mass.restype = ctypes.c_int
+        L.or_scale.argtypes = [_c_int64, _ptr, _ptr, _ptr]
+        L.or_scale.restype = None
         _lib = L
     return _lib
 
@@ -195,6 +201,32 @@ def g2l(l2g, n_global):
     if m < 0:
         raise ValueError("id out of range")
     return off, ids[:m].copy()
+
+
+def gll_weights(p):
+    """GLL quadrature weights of degree p on [-1, 1]."""
+    w = np.empty(p + 1, dtype=np.float64)
+    if lib().or_gll_weights(int(p), w.ctypes.data) != 0:
+        raise ValueError("order must be >= 1")
+    return w
+
+
+def mesh_box_mass(ex, ey, ez, p):
+    """Local lumped-mass weights of the unit-hexahedron box mesh."""
+    w = np.empty(ex * ey * ez * (p + 1) ** 3, dtype=np.float64)
+    if lib().or_mesh_box_mass(ex, ey, ez, p, w.ctypes.data) != 0:
+        raise ValueError("bad mesh arguments")
+    return w
+
+
+def scale(x, d):
+    """y = x / d elementwise, each quotient correctly rounded."""
+    x, px = _f64(x)
+    d, pd = _f64(d)
+    assert x.size == d.size
+    y = np.empty_like(x)
+    lib().or_scale(x.size, px, pd, y.ctypes.data)
+    return y
 
 
 def cg_sequence(l2g, n_global, b, iters):

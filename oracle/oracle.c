@@ -350,3 +350,51 @@ int64_t or_g2l(int64_t n_local, int64_t n_global, const int32_t *l2g,
     free(pr);
     return m;
 }
+
+/* ------------------------------------------------ lumped mass, 1/m scale --- */
+/* GLL quadrature weights on [-1, 1]: w_i = 2 / (p (p+1) P_p(r_i)^2) at the
+ * nodes of or_gll_nodes. Returns 0, or -1 if p < 1. */
+int or_gll_weights(int p, double *w)
+{
+    if (p < 1) return -1;
+    double *r = (double *)malloc((size_t)(p + 1) * sizeof(double));
+    if (!r) return -1;
+    or_gll_nodes(p, r);
+    for (int i = 0; i <= p; ++i) {
+        double P, Pm;
+        legendre(p, r[i], &P, &Pm);
+        w[i] = 2.0 / ((double)p * (p + 1.0) * P * P);
+    }
+    free(r);
+    return 0;
+}
+
+/* Local (diagonal) mass weights of the box mesh of unit hexahedra: node
+ * (i,j,k) of every element carries w_i w_j w_k / 8 (the GLL weights times
+ * the Jacobian of the map from [-1,1]^3 onto a unit cube). The lumped global
+ * mass is the gather of these weights, m = Z^T w_L ("GPU accelerated spectral
+ * finite elements on all-hex meshes", coarse-grid correction: the lumped mass
+ * as the global components of the local weights). */
+int or_mesh_box_mass(int ex, int ey, int ez, int p, double *w_local)
+{
+    if (ex < 1 || ey < 1 || ez < 1 || p < 1) return -1;
+    const int64_t nq = p + 1, Np = nq * nq * nq, K = (int64_t)ex * ey * ez;
+    double *w = (double *)malloc((size_t)nq * sizeof(double));
+    if (!w) return -1;
+    or_gll_weights(p, w);
+    for (int64_t e = 0; e < K; ++e)
+        for (int64_t k = 0; k < nq; ++k)
+            for (int64_t j = 0; j < nq; ++j)
+                for (int64_t i = 0; i < nq; ++i)
+                    w_local[e * Np + i + nq * (j + nq * k)] = w[i] * w[j] * w[k] / 8.0;
+    free(w);
+    return 0;
+}
+
+/* y[i] = x[i] / d[i], one correctly rounded division ("scaling by the
+ * inverted mass matrix", arXiv 1506.05996, coarse-grid correction). */
+void or_scale(int64_t n, const double *x, const double *d, double *y)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) y[i] = x[i] / d[i];
+}

@@ -185,6 +185,25 @@ def test_gather_plan_caps_rows(bs):
     assert list(plan) == [0, 1024, 2048, 3000]
 
 
+@pytest.mark.parametrize("p", [1, 2, 3, 4, 5, 7, 10, 15])
+def test_gll_matches_oracle(bs, orc, p):
+    """The library's GLL rule (Newton on P_{p+1} - P_{p-1}) and the oracle's
+    (Newton on P_p' itself) are written independently; they agree to a few
+    units in the last place."""
+    r, w = bs.bs_gll(p)
+    assert np.allclose(r, orc.gll_nodes(p), rtol=0, atol=4e-16)
+    assert np.allclose(w, orc.gll_weights(p), rtol=4e-15, atol=0)
+    assert r[0] == -1.0 and r[-1] == 1.0
+    with pytest.raises(bs.BSError):
+        bs.bs_gll(0)
+
+
+def test_box_mass_matches_oracle(bs, orc):
+    for dims, N in [((1, 1, 1), 1), ((3, 2, 4), 3), ((5, 5, 5), 7)]:
+        w = bs.bs_mesh_box_mass(*dims, N)
+        assert np.allclose(w, orc.mesh_box_mass(*dims, N), rtol=1e-14, atol=0)
+
+
 def test_gather_plan_long_rows(bs):
     # one node with 10 entries, the rest single
     off = np.array([0, 1, 11, 12, 13], dtype=np.int32)

@@ -418,6 +418,43 @@ def test_gather_dot(env, name):
         assert_rel(got, want_dot, f"gather_dot {name}")
 
 
+@pytest.mark.parametrize("n", [1, 2, 3, 1000, 4097, 1_000_003, 11_390_625])
+def test_scale_bit_exact(env, n):
+    """bs_scale: y = x / d, one correctly rounded division per entry."""
+    bs, orc, torch, d = env
+    x = bs_inputs.uniform_pm1(211, n)
+    dv = bs_inputs.uniform_pm1(212, n) + 1.5
+    y = torch.empty(n, dtype=torch.float64, device=d)
+    bs.bs_scale(dev(torch, d, x), dev(torch, d, dv), y)
+    assert_bits(host(y), orc.scale(x, dv), f"scale n={n}")
+    xt = dev(torch, d, x)
+    bs.bs_scale(xt, dev(torch, d, dv), xt)  # in place
+    assert_bits(host(xt), orc.scale(x, dv), f"scale in place n={n}")
+
+
+@pytest.mark.parametrize("name", ["c1_box8_N3", "c2_box32_N7"])
+def test_lumped_mass_and_inverse_scale(env, name):
+    """m = Z^T w_L through bs_gather, then y = r / m through bs_scale, bit for
+    bit against the oracle on the same weights; the library's own weights
+    agree with the oracle's to rounding and sum to the box volume."""
+    bs, orc, torch, d = env
+    l2g, off, ids, ol2g, ng = mesh_case(env, name)
+    E, N = MESHES[name]
+    ow = orc.mesh_box_mass(E, E, E, N)
+    lw = bs.bs_mesh_box_mass(E, E, E, N)
+    assert np.allclose(lw, ow, rtol=1e-14, atol=0)
+    want_m = orc.gather(ol2g, ow, ng)
+    m = torch.empty(ng, dtype=torch.float64, device=d)
+    bs.bs_gather(dev(torch, d, off), dev(torch, d, ids), dev(torch, d, ow), m,
+                 dev(torch, d, bs.bs_gather_plan(off, 1024)))
+    assert_bits(host(m), want_m, "lumped mass")
+    assert abs(host(m).sum() - E ** 3) <= 1e-11 * E ** 3
+    r = bs_inputs.uniform_pm1(213, ng)
+    y = torch.empty(ng, dtype=torch.float64, device=d)
+    bs.bs_scale(dev(torch, d, r), m, y)
+    assert_bits(host(y), orc.scale(r, want_m), "r / m")
+
+
 def cg_setup(env, name):
     bs, orc, torch, d = env
     l2g, off, ids, ol2g, ng = mesh_case(env, name)

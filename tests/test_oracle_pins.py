@@ -403,6 +403,56 @@ def test_gather_scatter_random_bound(orc):
     assert np.all(np.abs(got - m * v) <= (m - 1) * np.spacing(m * np.abs(v)))
 
 
+# ------------------------------------------------ lumped mass, 1/m scale ----
+
+def test_gll_weights_closed_forms(orc):
+    assert np.allclose(orc.gll_weights(1), [1, 1], rtol=0, atol=1e-15)
+    assert np.allclose(orc.gll_weights(2), [1 / 3, 4 / 3, 1 / 3], rtol=0, atol=1e-15)
+    assert np.allclose(orc.gll_weights(3), [1 / 6, 5 / 6, 5 / 6, 1 / 6], rtol=0, atol=1e-15)
+    assert np.allclose(orc.gll_weights(4), [1 / 10, 49 / 90, 32 / 45, 49 / 90, 1 / 10], rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("p", [1, 2, 5, 7, 15])
+def test_gll_quadrature_exactness(orc, p):
+    """GLL with p+1 points integrates every polynomial of degree <= 2p-1
+    exactly: sum_i w_i r_i^k = 2/(k+1) for even k, 0 for odd k; and it fails
+    for degree 2p (the end-point rule is not Gauss)."""
+    r, w = orc.gll_nodes(p), orc.gll_weights(p)
+    for k in range(2 * p):
+        want = 2.0 / (k + 1) if k % 2 == 0 else 0.0
+        assert abs(np.dot(w, r ** k) - want) < 1e-13, k
+    assert abs(np.dot(w, r ** (2 * p)) - 2.0 / (2 * p + 1)) > 1e-11
+
+
+@pytest.mark.parametrize("E,N", [(1, 3), (3, 2), (4, 7)])
+def test_lumped_mass(orc, E, N):
+    """m = Z^T w_L: positive, sums to the box volume E^3, and on one element
+    is the tensor product of the GLL weights over 8."""
+    l2g, ng = orc.mesh_box(E, E, E, N)
+    wl = orc.mesh_box_mass(E, E, E, N)
+    m = orc.gather(l2g, wl, ng)
+    assert np.all(m > 0)
+    assert abs(m.sum() - E ** 3) <= 1e-12 * E ** 3
+    if E == 1:
+        w = orc.gll_weights(N)
+        want = (w[None, None, :] * w[None, :, None] * w[:, None, None]).ravel() / 8
+        assert np.allclose(m, want, rtol=1e-15, atol=0)
+    # a node shared by two elements gets both elements' weights
+    w = orc.gll_weights(N)
+    if E > 1:
+        g = l2g[N]  # node (N,0,0) of element 0 is node (0,0,0) of element 1
+        assert m[g] == (w[N] * w[0] * w[0] / 8.0) + (w[0] * w[0] * w[0] / 8.0)
+
+
+def test_scale_exact_rounding(orc):
+    x = bs_inputs.uniform_pm1(201, 3000)
+    d = bs_inputs.uniform_pm1(202, 3000) + 2.0
+    y = orc.scale(x, d)
+    for i in range(3000):
+        assert y[i] == rn(Fraction(x[i]) / Fraction(d[i]))
+    assert np.array_equal(orc.scale(x, np.ones(3000)), x)
+
+
 # ------------------------------------------------------- CG on Z^T Z ------
 
 def test_cg_sequence_converges_in_four(orc):
