@@ -79,6 +79,8 @@ def lib():
         L.or_mesh_box_mass.argtypes = [ctypes.c_int] * 4 + [_ptr]
         L.or_mesh_box_mass.restype = ctypes.c_int
         L.or_scale.argtypes = [_c_int64, _ptr, _ptr, _ptr]
+        L.or_mesh_hex.argtypes = [_c_int64, ctypes.c_int, _c_int64, _ptr, _ptr]
+        L.or_mesh_hex.restype = _c_int64
         L.or_scale.restype = None
         _lib = L
     return _lib
@@ -252,3 +254,21 @@ def cg_sequence(l2g, n_global, b, iters):
         rr = rr_new
         hist.append(rr)
     return x, r, hist
+
+
+def mesh_hex(ev, p, n_vert=None):
+    """I_l->g of an unstructured hex mesh from its corner vertices.
+
+    ev: int32[E, 8], corner c = a + 2b + 4d of the reference cube. Global
+    nodes are the distinct points of the mesh (exact symbolic trilinear
+    weights over the vertices), numbered by first appearance.
+    Returns (l2g int32[E (p+1)^3], n_global)."""
+    ev = np.ascontiguousarray(ev, dtype=np.int32).reshape(-1, 8)
+    E = ev.shape[0]
+    if n_vert is None:
+        n_vert = int(ev.max()) + 1 if E else 0
+    l2g = np.empty(E * (p + 1) ** 3, dtype=np.int32)
+    ng = lib().or_mesh_hex(E, p, n_vert, ev.ctypes.data, l2g.ctypes.data)
+    if ng < 0:
+        raise ValueError("bad hex mesh")
+    return l2g, int(ng)

@@ -22,6 +22,10 @@
  *   or_gll_nodes  GLL points of degree p           (nodes of eqs. 1-2)
  *   or_mesh_box   I_l->g of a box hex mesh         (eqs. 1-3; arXiv 1506.05996, local-to-global table)
  *   or_g2l        CSR form of I_g->l               (arXiv 1506.05996, global-to-local table)
+ *   or_gll_weights, or_mesh_box_mass, or_scale   lumped mass and the 1/m scaling
+ *                 (arXiv 1506.05996, coarse-grid correction)
+ *   or_mesh_hex   I_l->g of an unstructured hex mesh given by corner vertices
+ *                 (unstructured mesh of the CEED formulation section; arXiv 1506.05996, local-to-global table)
  *
  * The reductions (dot, norm, the residual norm of the fused update) are
  * evaluated accurately with Dot2 of Ogita, Rump and Oishi ("Accurate sum and
@@ -397,4 +401,121 @@ void or_scale(int64_t n, const double *x, const double *d, double *y)
 {
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) y[i] = x[i] / d[i];
+}
+
+/* ------------------------------------------- unstructured hex meshes --- */
+/*
+ * I_l->g of an unstructured mesh of hexahedra ("Portable high-order finite
+ * element kernels I", the unstructured hexahedral mesh of the CEED
+ * formulation section; "GPU accelerated spectral finite elements on all-hex
+ * meshes", local-to-global table: one global number per GLL node of the
+ * mesh).
+ *
+ * Element e is given by its 8 corner vertices: corner c = a + 2b + 4d is the
+ * corner (a, b, d) in {0,1}^3 of the reference cube (x, y, z), so corner c is
+ * local node (a p, b p, d p) of the node order i + (p+1)(j + (p+1)k). Its
+ * vertex is ev[8e + c], an id in [0, n_vert).
+ *
+ * Local node (i,j,k) is the point sum_c phi_c X_{ev[8e+c]} of the trilinear
+ * map, phi_c the product over the three axes of (1 - r)/2 (bit 0) or
+ * (1 + r)/2 (bit 1) at the node's GLL coordinate. Two local nodes are the same
+ * global node exactly when they put the same weight on every vertex. The
+ * weights are kept exactly, as symbols: the factor of axis a is identified by
+ * m_a = i_a for bit 1 and p - i_a for bit 0, the node's GLL index counted
+ * from the far end of that axis. GLL points are distinct and symmetric
+ * (r_{p-i} = -r_i), so equal m give equal factors; m = 0 is the zero factor.
+ * A vertex's weight is the multiset of its three m (a product does not depend
+ * on the order of its factors), and a node's signature is the list of
+ * (vertex, sorted m triple) over its vertices with nonzero weight, sorted.
+ *
+ * Global ids number the distinct signatures in order of first appearance in
+ * local storage order. Returns the number of global nodes, or -1 on bad
+ * arguments (a vertex id out of range, an element with a repeated vertex) or
+ * no memory.
+ */
+#define OR_SIG 16   /* 8 (vertex, weight code) pairs */
+
+static const int32_t *or_sig_base;
+
+static int cmp_sig(const void *pa, const void *pb)
+{
+    const int32_t *a = or_sig_base + (int64_t)OR_SIG * *(const int64_t *)pa;
+    const int32_t *b = or_sig_base + (int64_t)OR_SIG * *(const int64_t *)pb;
+    for (int t = 0; t < OR_SIG; ++t)
+        if (a[t] != b[t]) return a[t] < b[t] ? -1 : 1;
+    return 0;
+}
+
+int64_t or_mesh_hex(int64_t n_elem, int p, int64_t n_vert, const int32_t *ev, int32_t *l2g)
+{
+    if (n_elem < 0 || p < 1 || n_vert < 0) return -1;
+    for (int64_t e = 0; e < n_elem; ++e)
+        for (int c = 0; c < 8; ++c) {
+            if (ev[8 * e + c] < 0 || ev[8 * e + c] >= n_vert) return -1;
+            for (int c2 = 0; c2 < c; ++c2)
+                if (ev[8 * e + c2] == ev[8 * e + c]) return -1;
+        }
+    const int64_t nq = p + 1, Np = nq * nq * nq, NL = n_elem * Np;
+    int32_t *sig = (int32_t *)malloc((size_t)(NL > 0 ? NL : 1) * OR_SIG * sizeof(int32_t));
+    int64_t *order = (int64_t *)malloc((size_t)(NL > 0 ? NL : 1) * sizeof(int64_t));
+    int64_t *cls = (int64_t *)malloc((size_t)(NL > 0 ? NL : 1) * sizeof(int64_t));
+    if (!sig || !order || !cls) goto fail;
+    for (int64_t e = 0; e < n_elem; ++e)
+        for (int64_t k = 0; k < nq; ++k)
+            for (int64_t j = 0; j < nq; ++j)
+                for (int64_t i = 0; i < nq; ++i) {
+                    const int64_t L = e * Np + i + nq * (j + nq * k);
+                    const int64_t idx[3] = {i, j, k};
+                    int32_t *s = sig + OR_SIG * L;
+                    int n = 0;
+                    for (int c = 0; c < 8; ++c) {
+                        int64_t m[3];
+                        int zero = 0;
+                        for (int a = 0; a < 3; ++a) {
+                            m[a] = ((c >> a) & 1) ? idx[a] : p - idx[a];
+                            if (m[a] == 0) zero = 1;
+                        }
+                        if (zero) continue;
+                        /* sort the three factors */
+                        for (int x = 0; x < 3; ++x)
+                            for (int y = x + 1; y < 3; ++y)
+                                if (m[y] < m[x]) { int64_t t = m[x]; m[x] = m[y]; m[y] = t; }
+                        s[2 * n] = ev[8 * e + c];
+                        s[2 * n + 1] = (int32_t)((m[0] * nq + m[1]) * nq + m[2]);
+                        ++n;
+                    }
+                    /* sort the (vertex, code) pairs by vertex: insertion sort */
+                    for (int x = 1; x < n; ++x)
+                        for (int y = x; y > 0 && s[2 * y] < s[2 * (y - 1)]; --y) {
+                            int32_t t0 = s[2 * y], t1 = s[2 * y + 1];
+                            s[2 * y] = s[2 * (y - 1)];
+                            s[2 * y + 1] = s[2 * (y - 1) + 1];
+                            s[2 * (y - 1)] = t0;
+                            s[2 * (y - 1) + 1] = t1;
+                        }
+                    for (int x = n; x < 8; ++x) s[2 * x] = s[2 * x + 1] = -1;
+                }
+    /* group equal signatures */
+    for (int64_t L = 0; L < NL; ++L) order[L] = L;
+    or_sig_base = sig;
+    qsort(order, (size_t)NL, sizeof(int64_t), cmp_sig);
+    int64_t ncls = 0;
+    for (int64_t t = 0; t < NL; ++t) {
+        if (t > 0 && cmp_sig(&order[t - 1], &order[t]) != 0) ++ncls;
+        cls[order[t]] = ncls;
+    }
+    if (NL > 0) ++ncls;
+    /* number the classes by first appearance */
+    int64_t *first = order;   /* reused: class -> global id */
+    for (int64_t t = 0; t < ncls; ++t) first[t] = -1;
+    int64_t NG = 0;
+    for (int64_t L = 0; L < NL; ++L) {
+        if (first[cls[L]] < 0) first[cls[L]] = NG++;
+        l2g[L] = (int32_t)first[cls[L]];
+    }
+    free(cls); free(order); free(sig);
+    return NG;
+fail:
+    free(cls); free(order); free(sig);
+    return -1;
 }

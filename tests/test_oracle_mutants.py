@@ -46,6 +46,13 @@ MUTANTS = [
      "box or scatter or gather"),
     ("g2l_descending", "if (a->g != b->g) return a->g < b->g ? -1 : 1;\n    return (a->i < b->i) ? -1 : (a->i > b->i);",
      "if (a->g != b->g) return a->g < b->g ? -1 : 1;\n    return (a->i > b->i) ? -1 : (a->i < b->i);", "g2l"),
+    ("hex_factors_in_axis_order", "if (m[y] < m[x])", "if (0 && m[y] < m[x])", "hex"),
+    ("hex_keeps_zero_weights", "if (zero) continue;", "(void)zero;", "hex"),
+    ("hex_factor_from_own_end", "m[a] = ((c >> a) & 1) ? idx[a] : p - idx[a];",
+     "m[a] = ((c >> a) & 1) ? p - idx[a] : idx[a];", "hex"),
+    ("hex_vertices_in_corner_order", "y > 0 && s[2 * y] < s[2 * (y - 1)]", "y > 0 && 0", "hex"),
+    ("hex_numbered_by_signature", "if (first[cls[L]] < 0) first[cls[L]] = NG++;",
+     "if (first[cls[L]] < 0) first[cls[L]] = NG++;\n        first[cls[L]] = cls[L];", "hex"),
 ]
 
 

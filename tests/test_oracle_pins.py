@@ -469,3 +469,174 @@ def test_cg_sequence_converges_in_four(orc):
     x1, _, h1 = orc.cg_sequence(l2g, ng, b1, 1)
     assert math.sqrt(h1[-1] / h1[0]) < 1e-15
     assert np.allclose(x1, b1 / m, rtol=1e-15, atol=0)
+
+
+# ------------------------------------------- unstructured hex meshes ------
+# A global numbering is fixed only up to renaming; the oracle numbers nodes by
+# first appearance, so every expected partition below is renamed the same way
+# before the arrays are compared.
+
+def first_touch(keys):
+    """Rename equal keys 0, 1, 2, ... in order of first appearance."""
+    keys = np.asarray(keys)
+    _, first, inv = np.unique(keys, return_index=True, return_inverse=True)
+    rank = np.empty(len(first), dtype=np.int64)
+    rank[np.argsort(first, kind="stable")] = np.arange(len(first))
+    return rank[inv.ravel()].astype(np.int32)
+
+
+def unrotate(l2g, sym, N):
+    """Undo bs_inputs.hex_orient on a local array: element e was presented in
+    the corner order of cube symmetry sym[e]; return the array in the
+    element's original node order."""
+    nq = N + 1
+    loc = np.asarray(l2g).reshape(-1, nq, nq, nq)  # [e, k, j, i]
+    out = np.empty_like(loc)
+    q = np.stack(np.meshgrid(np.arange(nq), np.arange(nq), np.arange(nq), indexing="ij"), -1)  # [k,j,i,(k,j,i)]
+    q = q[..., ::-1]  # (i, j, k)
+    for e in range(loc.shape[0]):
+        perm, flip, _ = bs_inputs.cube_symmetry(int(sym[e]))
+        o = np.empty_like(q)
+        for a in range(3):
+            o[..., perm[a]] = np.where((flip >> a) & 1, N - q[..., a], q[..., a])
+        out[e, o[..., 2], o[..., 1], o[..., 0]] = loc[e]
+    return out.ravel()
+
+
+def entity_count(ev, N):
+    """Global node count from the mesh's entities: vertices, then N-1 nodes
+    per edge, (N-1)^2 per face and (N-1)^3 per element."""
+    edges, faces = set(), set()
+    for h in ev:
+        for c in range(8):
+            for a in range(3):
+                if not (c >> a) & 1:
+                    edges.add(frozenset((h[c], h[c | 1 << a])))
+        for a in range(3):
+            for side in (0, 1):
+                faces.add(frozenset(h[c] for c in range(8) if (c >> a) & 1 == side))
+    V = len(set(np.asarray(ev).ravel()))
+    return V + (N - 1) * len(edges) + (N - 1) ** 2 * len(faces) + (N - 1) ** 3 * len(ev)
+
+
+@pytest.mark.parametrize("dims,N", [((1, 1, 1), 1), ((2, 3, 2), 3), ((4, 3, 2), 4), ((3, 3, 3), 7)])
+def test_hex_box_equals_box_positions(orc, dims, N):
+    """On the box lattice the corner-connectivity oracle finds exactly the
+    partition of the position-based box oracle, and the lattice count."""
+    ev, nv = bs_inputs.hex_box(*dims)
+    l2g, ng = orc.mesh_hex(ev, N, nv)
+    box, bng = orc.mesh_box(*dims, N)
+    assert ng == bng == math.prod(d * N + 1 for d in dims)
+    assert np.array_equal(l2g, first_touch(box))
+
+
+@pytest.mark.parametrize("N", [1, 2, 5])
+def test_hex_orientation_invariant(orc, N):
+    """Presenting every element in a random one of the 48 corner orders of the
+    cube renames its local nodes only: undoing the renaming gives the box's
+    partition back."""
+    ev, nv = bs_inputs.hex_box(3, 2, 3)
+    rot, sym = bs_inputs.hex_orient(ev, 501)
+    assert len(set(sym.tolist())) > 10
+    l2g, ng = orc.mesh_hex(rot, N, nv)
+    box, bng = orc.mesh_box(3, 2, 3, N)
+    assert ng == bng
+    assert np.array_equal(first_touch(unrotate(l2g, sym, N)), first_touch(box))
+
+
+def test_hex_vertex_names_do_not_matter(orc):
+    ev, nv = bs_inputs.hex_box(3, 3, 2)
+    rot, _ = bs_inputs.hex_orient(ev, 502)
+    ref, ng = orc.mesh_hex(rot, 4, nv)
+    ev2, nv2 = bs_inputs.hex_relabel(rot, nv, 503, spare=17)
+    l2g, ng2 = orc.mesh_hex(ev2, 4, nv2)
+    assert ng2 == ng and np.array_equal(l2g, ref)
+
+
+def lattice_keys(dims, N, periodic, twist):
+    """Brute force: node (i,j,k) of cell (cx,cy,cz) is the lattice point
+    (cx N + i, ...), wrapped on periodic axes (and reflected in y where the
+    twisted x axis wraps)."""
+    nx, ny, nz = dims
+    G = [d * N for d in dims]
+    keys = []
+    for cz in range(nz):
+        for cy in range(ny):
+            for cx in range(nx):
+                for k in range(N + 1):
+                    for j in range(N + 1):
+                        for i in range(N + 1):
+                            X, Y, Z = cx * N + i, cy * N + j, cz * N + k
+                            if periodic[0] and X == G[0]:
+                                X = 0
+                                if twist:
+                                    Y = G[1] - Y
+                            if periodic[1]:
+                                Y %= G[1]
+                            if periodic[2]:
+                                Z %= G[2]
+                            keys.append((Z * (G[1] + 1) + Y) * (G[0] + 1) + X)
+    return np.array(keys)
+
+
+@pytest.mark.parametrize("periodic,twist", [((True, False, False), False), ((True, True, True), False),
+                                            ((True, False, True), True)])
+@pytest.mark.parametrize("N", [2, 3])
+def test_hex_periodic_and_twisted(orc, periodic, twist, N):
+    dims = (3, 3, 4)
+    ev, nv = bs_inputs.hex_box(*dims, periodic=periodic, twist=twist)
+    rot, sym = bs_inputs.hex_orient(ev, 504)
+    l2g, ng = orc.mesh_hex(rot, N, nv)
+    want = first_touch(lattice_keys(dims, N, periodic, twist))
+    assert ng == want.max() + 1
+    assert ng == math.prod(d * N + (0 if p else 1) for d, p in zip(dims, periodic))
+    assert np.array_equal(first_touch(unrotate(l2g, sym, N)), want)
+
+
+def gll_points(N):
+    """GLL points from numpy's Legendre class: -1, the roots of P_N', +1."""
+    inner = np.polynomial.legendre.Legendre.basis(N).deriv().roots() if N > 1 else np.array([])
+    return np.concatenate([[-1.0], np.sort(inner.real), [1.0]])
+
+
+@pytest.mark.parametrize("N", [1, 3, 6])
+def test_hex_tet_split_by_physical_positions(orc, N):
+    """Unstructured mesh: maps every local node through its element's
+    trilinear map and clusters the physical points (distance < 1e-9); the
+    clusters are the oracle's global nodes. The count also matches the
+    entity formula."""
+    from scipy.sparse import coo_matrix
+    from scipy.sparse.csgraph import connected_components
+    from scipy.spatial import cKDTree
+
+    ev, nv, X = bs_inputs.hex_tet_split(2, 1, 2)
+    l2g, ng = orc.mesh_hex(ev, N, nv)
+    assert ng == entity_count(ev, N)
+    r = gll_points(N)
+    t = (1 + r) / 2
+    phi = np.stack([1 - t, t])  # [bit, node]
+    nq = N + 1
+    pts = np.zeros((len(ev), nq, nq, nq, 3))
+    for c in range(8):
+        a, b, d = c & 1, (c >> 1) & 1, (c >> 2) & 1
+        w = phi[d][:, None, None] * phi[b][None, :, None] * phi[a][None, None, :]  # [k, j, i]
+        pts += w[None, :, :, :, None] * X[ev[:, c]][:, None, None, None, :]
+    pts = pts.reshape(-1, 3)
+    pairs = cKDTree(pts).query_pairs(1e-9, output_type="ndarray")
+    n = len(pts)
+    g = coo_matrix((np.ones(len(pairs)), (pairs[:, 0], pairs[:, 1])), shape=(n, n))
+    ncomp, lab = connected_components(g, directed=False)
+    assert ncomp == ng
+    assert np.array_equal(l2g, first_touch(lab))
+
+
+def test_hex_rejects_bad_elements(orc):
+    ev, nv = bs_inputs.hex_box(2, 1, 1)
+    bad = ev.copy()
+    bad[1, 3] = bad[1, 0]
+    with pytest.raises(ValueError):
+        orc.mesh_hex(bad, 2, nv)
+    with pytest.raises(ValueError):
+        orc.mesh_hex(ev, 2, int(ev.max()))
+    l2g, ng = orc.mesh_hex(np.zeros((0, 8), np.int32), 3, 0)
+    assert l2g.size == 0 and ng == 0
