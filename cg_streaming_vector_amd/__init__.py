@@ -67,6 +67,7 @@ SIGNATURES = {
                      _ptr, _ptr], _int),
     "bs_mesh_box_count": ([_int, _int, _int, _int, ctypes.POINTER(_i64), ctypes.POINTER(_i64)], _int),
     "bs_mesh_box_l2g": ([_int, _int, _int, _int, _ptr, _ptr, _ptr], _int),
+    "bs_mesh_hex_l2g": ([_i64, _int, _i64, _ptr, _ptr, ctypes.POINTER(_i64)], _int),
     "bs_validate_l2g": ([_i64, _i64, _ptr], _int),
     "bs_index_g2l": ([_i64, _i64, _ptr, _ptr, _ptr], _int),
     "bs_gather_plan": ([_i64, _ptr, _int, _ptr, ctypes.POINTER(_i64)], _int),
@@ -372,6 +373,25 @@ def bs_mesh_box_l2g(ex, ey, ez, order, elem_perm=None, node_perm=None):
     return l2g
 
 
+def bs_mesh_hex_l2g(ev, order, n_vertices=None):
+    """I_l->g of an unstructured hex mesh from corner vertices ev (int32
+    [n_elements, 8]). Returns (l2g int32[n_elements (order+1)^3], n_global)."""
+    ev = _host_i32(ev, "ev")
+    if ev.size % 8:
+        raise ValueError("ev must hold 8 vertices per element")
+    E = ev.size // 8
+    if n_vertices is None:
+        n_vertices = int(ev.max()) + 1 if E else 0
+    nl = E * (int(order) + 1) ** 3
+    # a table too large for int32 ids is refused (BS_ERANGE) before anything
+    # is written, so a token buffer stands in for it
+    l2g = np.empty(nl if 0 <= nl <= 2 ** 31 - 1 else 1, dtype=np.int32)
+    ng = _i64()
+    _check(_lib().bs_mesh_hex_l2g(E, int(order), int(n_vertices), ev.ctypes.data, l2g.ctypes.data,
+                                  ctypes.byref(ng)), "bs_mesh_hex_l2g")
+    return l2g, ng.value
+
+
 def bs_validate_l2g(l2g, n_global):
     l2g = _host_i32(l2g, "l2g")
     _check(_lib().bs_validate_l2g(l2g.size, int(n_global), l2g.ctypes.data), "bs_validate_l2g")
@@ -402,5 +422,5 @@ __all__ = [
     "BSError", "Context", "context", "LIB_PATH", "SIGNATURES",
     "bs_copy", "bs_axpy", "bs_norm", "bs_dot", "bs_cg_update", "bs_scatter", "bs_gather",
     "bs_gather_dot", "bs_cg_solve", "bs_scale", "bs_gll", "bs_mesh_box_mass",
-    "bs_mesh_box_count", "bs_mesh_box_l2g", "bs_validate_l2g", "bs_index_g2l", "bs_gather_plan",
+    "bs_mesh_box_count", "bs_mesh_box_l2g", "bs_mesh_hex_l2g", "bs_validate_l2g", "bs_index_g2l", "bs_gather_plan",
 ]

@@ -12,10 +12,19 @@
 // On the box this makes the global node lattice (E*order + 1) points per
 // axis, and the node (i,j,k) of element (cx,cy,cz) the lattice point
 // (cx*order + i, cy*order + j, cz*order + k): a closed form, no search.
+//
+// On an unstructured mesh given by element corner vertices the same sharing
+// is found topologically: a node on a vertex, edge or face belongs to that
+// entity, whose nodes are laid out in a frame fixed by the entity's own
+// vertex ids (an edge counted from its smaller vertex, a face from its
+// smallest vertex towards the smaller neighbour), so every element that
+// holds the entity, in whatever orientation, names its nodes alike.
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <new>
 #include <vector>
 
 #include "bs.h"
@@ -30,6 +39,56 @@ bool is_permutation(const int32_t *p, int64_t n)
         seen[(size_t)p[i]] = 1;
     }
     return true;
+}
+
+// A face of an element seen from the mesh: its four vertices sorted, and the
+// vertex diagonally opposite the smallest one. Two elements share the face
+// when the sorted quadruples agree; they agree on its shape only if the
+// opposite vertex agrees too.
+struct FaceKey {
+    int32_t v[4];
+    int32_t opposite;
+    bool operator<(const FaceKey &o) const
+    {
+        for (int t = 0; t < 4; ++t)
+            if (v[t] != o.v[t]) return v[t] < o.v[t];
+        return opposite < o.opposite;
+    }
+    bool same_set(const FaceKey &o) const { return std::equal(v, v + 4, o.v); }
+};
+
+// Face of an element with the reference axis `a` fixed at `side`: its corner
+// at face position (u, w) along the two other axes a1 < a2.
+struct FaceFrame {
+    int a, a1, a2, side;
+    int corner(int u, int w) const { return (side << a) | (u << a1) | (w << a2); }
+};
+
+FaceFrame face_frame(int f)
+{
+    FaceFrame fr;
+    fr.a = f >> 1;
+    fr.side = f & 1;
+    fr.a1 = fr.a == 0 ? 1 : 0;
+    fr.a2 = fr.a == 2 ? 1 : 2;
+    return fr;
+}
+
+FaceKey face_key(const int32_t *v, int f)
+{
+    const FaceFrame fr = face_frame(f);
+    FaceKey k;
+    int32_t q[2][2];
+    for (int u = 0; u < 2; ++u)
+        for (int w = 0; w < 2; ++w) q[u][w] = v[fr.corner(u, w)];
+    int ua = 0, wa = 0;
+    for (int u = 0; u < 2; ++u)
+        for (int w = 0; w < 2; ++w)
+            if (q[u][w] < q[ua][wa]) ua = u, wa = w;
+    k.v[0] = q[0][0], k.v[1] = q[0][1], k.v[2] = q[1][0], k.v[3] = q[1][1];
+    std::sort(k.v, k.v + 4);
+    k.opposite = q[1 - ua][1 - wa];
+    return k;
 }
 
 }  // namespace
@@ -77,6 +136,132 @@ int bs_mesh_box_l2g(int ex, int ey, int ez, int order, const int32_t *elem_perm,
                 }
             }
         }
+    }
+    return BS_OK;
+}
+
+int bs_mesh_hex_l2g(int64_t n_elements, int order, int64_t n_vertices, const int32_t *ev, int32_t *l2g,
+                    int64_t *n_global)
+{
+    if (n_elements < 0 || order < 1 || n_vertices < 0 || !n_global) return BS_EINVAL;
+    if (n_elements > 0 && (!ev || !l2g)) return BS_EINVAL;
+    const int64_t N = order, nq = N + 1;
+    if (nq > 2048) return BS_ERANGE;
+    const int64_t Np = nq * nq * nq;
+    if (n_elements > INT32_MAX / Np || n_vertices > INT32_MAX) return BS_ERANGE;
+    const int64_t E = n_elements;
+    for (int64_t e = 0; e < E; ++e) {
+        const int32_t *v = ev + 8 * e;
+        for (int c = 0; c < 8; ++c) {
+            if (v[c] < 0 || v[c] >= n_vertices) return BS_EINVAL;
+            for (int c2 = 0; c2 < c; ++c2)
+                if (v[c2] == v[c]) return BS_EINVAL;
+        }
+    }
+    try {
+        // Entities shared between elements: edges by their two vertices,
+        // faces by their four. Sort and deduplicate the keys of all elements.
+        std::vector<uint64_t> edges;
+        edges.reserve((size_t)E * 12);
+        std::vector<FaceKey> faces;
+        faces.reserve((size_t)E * 6);
+        for (int64_t e = 0; e < E; ++e) {
+            const int32_t *v = ev + 8 * e;
+            for (int a = 0; a < 3; ++a)
+                for (int c = 0; c < 8; ++c) {
+                    if ((c >> a) & 1) continue;
+                    const uint32_t x = (uint32_t)v[c], y = (uint32_t)v[c | 1 << a];
+                    edges.push_back((uint64_t)std::min(x, y) << 32 | std::max(x, y));
+                }
+            for (int f = 0; f < 6; ++f) faces.push_back(face_key(v, f));
+        }
+        std::sort(edges.begin(), edges.end());
+        edges.erase(std::unique(edges.begin(), edges.end()), edges.end());
+        std::sort(faces.begin(), faces.end());
+        // a shared face must be the same quadrilateral in every element
+        for (size_t t = 1; t < faces.size(); ++t)
+            if (faces[t].same_set(faces[t - 1]) && faces[t].opposite != faces[t - 1].opposite) return BS_EINVAL;
+        faces.erase(std::unique(faces.begin(), faces.end(),
+                                [](const FaceKey &x, const FaceKey &y) { return x.same_set(y); }),
+                    faces.end());
+
+        // Provisional ids: the vertices, then N-1 nodes per edge, (N-1)^2 per
+        // face, (N-1)^3 per element, each entity's nodes in a frame fixed by
+        // its vertex ids so that every element sharing it agrees.
+        const int64_t m = N - 1;
+        const int64_t base_edge = n_vertices;
+        const int64_t base_face = base_edge + (int64_t)edges.size() * m;
+        const int64_t base_cell = base_face + (int64_t)faces.size() * m * m;
+        const int64_t n_raw = base_cell + E * m * m * m;
+        // final ids: provisional ids renamed in order of first appearance
+        std::vector<int32_t> rename((size_t)n_raw, -1);
+        int64_t ng = 0;
+        for (int64_t e = 0; e < E; ++e) {
+            const int32_t *v = ev + 8 * e;
+            int64_t eid[3][8], fid[6];
+            for (int a = 0; a < 3; ++a)
+                for (int c = 0; c < 8; ++c) {
+                    if ((c >> a) & 1) continue;
+                    const uint32_t x = (uint32_t)v[c], y = (uint32_t)v[c | 1 << a];
+                    const uint64_t key = (uint64_t)std::min(x, y) << 32 | std::max(x, y);
+                    eid[a][c] = std::lower_bound(edges.begin(), edges.end(), key) - edges.begin();
+                }
+            for (int f = 0; f < 6; ++f) {
+                const FaceKey k = face_key(v, f);
+                fid[f] = std::lower_bound(faces.begin(), faces.end(), k,
+                                          [](const FaceKey &x, const FaceKey &y) {
+                                              return std::lexicographical_compare(x.v, x.v + 4, y.v, y.v + 4);
+                                          }) -
+                         faces.begin();
+            }
+            int32_t *dst = l2g + e * Np;
+            for (int64_t k = 0; k < nq; ++k)
+                for (int64_t j = 0; j < nq; ++j)
+                    for (int64_t i = 0; i < nq; ++i) {
+                        const int64_t idx[3] = {i, j, k};
+                        int bnd[3], nb = 0;
+                        for (int a = 0; a < 3; ++a) {
+                            bnd[a] = idx[a] == 0 ? 0 : idx[a] == N ? 1 : -1;
+                            nb += bnd[a] >= 0;
+                        }
+                        int64_t raw;
+                        if (nb == 3) {
+                            raw = v[bnd[0] | bnd[1] << 1 | bnd[2] << 2];
+                        } else if (nb == 2) {
+                            // edge along the one interior axis, counted from its
+                            // end with the smaller vertex id
+                            const int a = bnd[0] < 0 ? 0 : bnd[1] < 0 ? 1 : 2;
+                            int c0 = 0;
+                            for (int b = 0; b < 3; ++b)
+                                if (b != a) c0 |= bnd[b] << b;
+                            const int c1 = c0 | 1 << a;
+                            const int64_t u = v[c0] < v[c1] ? idx[a] : N - idx[a];
+                            raw = base_edge + eid[a][c0] * m + (u - 1);
+                        } else if (nb == 1) {
+                            // face: origin at its smallest vertex, first axis
+                            // towards the smaller of that vertex's two neighbours
+                            const int a = bnd[0] >= 0 ? 0 : bnd[1] >= 0 ? 1 : 2;
+                            const FaceFrame fr = face_frame(2 * a + bnd[a]);
+                            int ua = 0, wa = 0;
+                            for (int u = 0; u < 2; ++u)
+                                for (int w = 0; w < 2; ++w)
+                                    if (v[fr.corner(u, w)] < v[fr.corner(ua, wa)]) ua = u, wa = w;
+                            const int64_t dp = ua ? N - idx[fr.a1] : idx[fr.a1];
+                            const int64_t dq = wa ? N - idx[fr.a2] : idx[fr.a2];
+                            const bool p_first = v[fr.corner(1 - ua, wa)] < v[fr.corner(ua, 1 - wa)];
+                            const int64_t x = p_first ? dp : dq, y = p_first ? dq : dp;
+                            raw = base_face + fid[2 * a + bnd[a]] * m * m + (y - 1) * m + (x - 1);
+                        } else {
+                            raw = base_cell + e * m * m * m + ((k - 1) * m + (j - 1)) * m + (i - 1);
+                        }
+                        int32_t &g = rename[(size_t)raw];
+                        if (g < 0) g = (int32_t)ng++;
+                        dst[i + nq * (j + nq * k)] = g;
+                    }
+        }
+        *n_global = ng;
+    } catch (const std::bad_alloc &) {
+        return BS_ENOMEM;
     }
     return BS_OK;
 }

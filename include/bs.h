@@ -190,6 +190,31 @@ int bs_mesh_box_count(int ex, int ey, int ez, int order, int64_t *n_local, int64
 int bs_mesh_box_l2g(int ex, int ey, int ez, int order, const int32_t *elem_perm,
                     const int32_t *node_perm, int32_t *l2g);
 
+/* I_l->g of an unstructured mesh of hexahedra given by corner vertices
+ * (arXiv 2009.10917, the unstructured hexahedral mesh of the CEED
+ * formulation section; arXiv 1506.05996, local-to-global table: one global
+ * number per GLL node of the mesh, so nodes on a shared vertex, edge or face
+ * get one id whatever the orientation of the elements that share it).
+ *   ev        int32[n_elements * 8], host: ev[8e + c] is the vertex at corner
+ *             c = a + 2b + 4d of element e, (a, b, d) in {0,1}^3 the corner of
+ *             the reference cube along (x, y, z) -- local node (a*order,
+ *             b*order, d*order). Ids in [0, n_vertices); unused ids allowed.
+ *   l2g       int32[n_elements * (order+1)^3], host, written: element by
+ *             element, node (i,j,k) at i + (order+1)(j + (order+1)k).
+ *   n_global  written: the number of global nodes. Ids are numbered in order
+ *             of first appearance in l2g.
+ * Entities are identified by their vertex sets: two elements share an edge
+ * when they share its two end vertices, a face when they share its four. A
+ * mesh in which distinct edges or faces have the same vertex set (a periodic
+ * direction of fewer than 3 elements) cannot be told apart and is shared.
+ * BS_EINVAL: bad sizes or NULL, a vertex id out of range, an element with a
+ * repeated vertex, or a face whose four vertices two elements connect in
+ * different cyclic orders (not a conforming mesh). BS_ERANGE: n_elements *
+ * (order+1)^3 above INT32_MAX or order > 2047. BS_ENOMEM: no host memory.
+ * Nothing is written to n_global on error; l2g may be partly written. */
+int bs_mesh_hex_l2g(int64_t n_elements, int order, int64_t n_vertices, const int32_t *ev,
+                    int32_t *l2g, int64_t *n_global);
+
 /* Gauss-Lobatto-Legendre points and weights of degree `order` on [-1, 1]:
  * nodes double[order+1] ascending (the end points and the roots of P_order'),
  * weights double[order+1], w_i = 2 / (order (order+1) P_order(r_i)^2). These

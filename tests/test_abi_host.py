@@ -213,3 +213,84 @@ def test_gather_plan_long_rows(bs):
         bs.bs_gather_plan(off, 0)
     with pytest.raises(bs.BSError):
         bs.bs_gather_plan(off, 1025)
+
+
+# ------------------------------------------- unstructured hex meshes ------
+
+def hex_meshes():
+    """(name, ev, n_vert) of every family the generators make."""
+    out = []
+    ev, nv = bs_inputs.hex_box(4, 3, 2)
+    out.append(("box", ev, nv))
+    out.append(("box_oriented", bs_inputs.hex_orient(ev, 601)[0], nv))
+    ev, nv = bs_inputs.hex_box(3, 4, 3, periodic=(True, True, True))
+    out.append(("torus_oriented", bs_inputs.hex_orient(ev, 602)[0], nv))
+    ev, nv = bs_inputs.hex_box(3, 3, 3, periodic=(True, False, True), twist=True)
+    out.append(("twisted_oriented", bs_inputs.hex_orient(ev, 603)[0], nv))
+    ev, nv, _ = bs_inputs.hex_tet_split(2, 2, 1)
+    ev, _ = bs_inputs.hex_orient(ev, 604)
+    ev, nv = bs_inputs.hex_relabel(ev, nv, 605, spare=11)
+    out.append(("tet_split_oriented_relabeled", ev, nv))
+    return out
+
+
+@pytest.mark.parametrize("N", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("mesh", hex_meshes(), ids=lambda m: m[0])
+def test_hex_l2g_matches_oracle(bs, orc, mesh, N):
+    """The library's topological builder (entity frames) and the oracle's
+    symbolic trilinear weights are independent; both number by first
+    appearance, so the tables must be identical."""
+    _, ev, nv = mesh
+    l2g, ng = bs.bs_mesh_hex_l2g(ev, N, nv)
+    ol2g, ong = orc.mesh_hex(ev, N, nv)
+    assert ng == ong
+    assert np.array_equal(l2g, ol2g)
+
+
+def test_hex_l2g_shuffled_elements(bs, orc):
+    ev, nv, _ = bs_inputs.hex_tet_split(2, 1, 2)
+    ev = ev[bs_inputs.permutation(606, len(ev))]
+    l2g, ng = bs.bs_mesh_hex_l2g(ev, 4, nv)
+    ol2g, ong = orc.mesh_hex(ev, 4, nv)
+    assert ng == ong and np.array_equal(l2g, ol2g)
+
+
+def test_hex_l2g_box_equals_box_builder(bs):
+    """Same partition as the closed-form box builder (renamed by first
+    appearance)."""
+    ev, nv = bs_inputs.hex_box(5, 4, 3)
+    l2g, ng = bs.bs_mesh_hex_l2g(ev, 4, nv)
+    box = bs.bs_mesh_box_l2g(5, 4, 3, 4)
+    assert ng == bs.bs_mesh_box_count(5, 4, 3, 4)[1]
+    _, first, inv = np.unique(box, return_index=True, return_inverse=True)
+    rank = np.empty(len(first), dtype=np.int64)
+    rank[np.argsort(first)] = np.arange(len(first))
+    assert np.array_equal(l2g, rank[inv.ravel()])
+
+
+def test_hex_l2g_errors(bs):
+    ev, nv = bs_inputs.hex_box(2, 1, 1)
+    with pytest.raises(bs.BSError) as e:
+        bs.bs_mesh_hex_l2g(ev, 0, nv)
+    assert e.value.status == bs.BS_EINVAL
+    bad = ev.copy()
+    bad[0, 5] = bad[0, 2]
+    with pytest.raises(bs.BSError):
+        bs.bs_mesh_hex_l2g(bad, 2, nv)
+    with pytest.raises(bs.BSError):
+        bs.bs_mesh_hex_l2g(ev, 2, int(ev.max()))  # a vertex id out of range
+    # the shared face x = 1 presented with two of its vertices swapped in the
+    # second element: same four vertices, different quadrilateral
+    twisted = ev.copy()
+    a, b = twisted[1, 0], twisted[1, 2]  # corners (0,0,0) and (0,1,0): an edge
+    twisted[1, 0], twisted[1, 2] = b, a
+    a, b = twisted[1, 2], twisted[1, 6]  # then (0,1,0) <-> (0,1,1)
+    twisted[1, 2], twisted[1, 6] = b, a
+    with pytest.raises(bs.BSError) as e:
+        bs.bs_mesh_hex_l2g(twisted, 2, nv)
+    assert e.value.status == bs.BS_EINVAL
+    with pytest.raises(bs.BSError) as e:
+        bs.bs_mesh_hex_l2g(np.zeros((1, 8), np.int32) + np.arange(8, dtype=np.int32), 3000, 8)
+    assert e.value.status == bs.BS_ERANGE
+    l2g, ng = bs.bs_mesh_hex_l2g(np.zeros((0, 8), np.int32), 3, 0)
+    assert l2g.size == 0 and ng == 0

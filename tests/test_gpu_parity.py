@@ -507,3 +507,74 @@ def test_cg_solve_early_exit_and_zero_iterations(env):
     hz = host(bs.bs_cg_solve(t["l2g"], t["off"], t["ids"], z.clone(), z.clone(), z.clone(), t["q"], t["pl"], 3,
                              0.0, t["plan"]))
     assert list(hz) == [0.0, -1.0, -1.0, -1.0]
+
+
+# ------------------------------------------------ unstructured hex meshes ----
+
+def unstructured_case(env, kind):
+    """A mesh with arbitrary element orientation: the library builds the
+    tables it runs on, the oracle builds its own from the same corners."""
+    bs, orc, torch, d = env
+    if kind == "tet_split":
+        ev, nv, _ = bs_inputs.hex_tet_split(6, 5, 6)  # 4320 hexahedra, not a lattice
+        N = 5
+    else:
+        ev, nv = bs_inputs.hex_box(16, 16, 12, periodic=(True, True, True))
+        N = 7
+    ev, _ = bs_inputs.hex_orient(ev, 701)
+    ev, nv = bs_inputs.hex_relabel(ev, nv, 702, spare=5)
+    ev = ev[bs_inputs.permutation(703, len(ev))]
+    l2g, ng = bs.bs_mesh_hex_l2g(ev, N, nv)
+    off, ids = bs.bs_index_g2l(l2g, ng)
+    ol2g, ong = orc.mesh_hex(ev, N, nv)
+    assert ong == ng
+    return l2g, off, ids, ol2g, ng
+
+
+@pytest.mark.parametrize("kind", ["tet_split", "torus"])
+def test_unstructured_scatter_gather(env, kind):
+    bs, orc, torch, d = env
+    l2g, off, ids, ol2g, ng = unstructured_case(env, kind)
+    vgv = bs_inputs.uniform_pm1(711, ng)
+    vlv = bs_inputs.uniform_pm1(712, l2g.size)
+    wv = bs_inputs.uniform_pm1(713, ng)
+    vl = torch.empty(l2g.size, dtype=torch.float64, device=d)
+    bs.bs_scatter(dev(torch, d, l2g), dev(torch, d, vgv), vl)
+    assert_bits(host(vl), orc.scatter(ol2g, vgv), f"scatter {kind}")
+    want = orc.gather(ol2g, vlv, ng)
+    doff, dids, dvl = dev(torch, d, off), dev(torch, d, ids), dev(torch, d, vlv)
+    for plan in (None, bs.bs_gather_plan(off, 1024), bs.bs_gather_plan(off, 300)):
+        dplan = None if plan is None else dev(torch, d, plan)
+        vg = torch.full((ng,), np.nan, dtype=torch.float64, device=d)
+        bs.bs_gather(doff, dids, dvl, vg, dplan)
+        assert_bits(host(vg), want, f"gather {kind}")
+        vg.fill_(np.nan)
+        got = bs.bs_gather_dot(doff, dids, dvl, vg, dev(torch, d, wv), dplan).item()
+        assert_bits(host(vg), want, f"gather_dot values {kind}")
+        assert_rel(got, orc.dot(want, wv), f"gather_dot {kind}")
+
+
+def test_unstructured_cg_solve(env):
+    """Device-resident CG on Z^T Z = diag(m) of the tet-split mesh, whose
+    multiplicities take many values: the residual history follows the
+    oracle's CG while it is significant, and the iteration reaches b / m
+    within one step per distinct multiplicity."""
+    bs, orc, torch, d = env
+    l2g, off, ids, ol2g, ng = unstructured_case(env, "tet_split")
+    m = np.diff(off)
+    iters = len(np.unique(m))
+    b = bs_inputs.uniform_pm1(721, ng)
+    ox, _, ohist = orc.cg_sequence(ol2g, ng, b, iters)
+    t = {k: dev(torch, d, v) for k, v in (("l2g", l2g), ("off", off), ("ids", ids),
+                                           ("plan", bs.bs_gather_plan(off, 1024)))}
+    x = torch.zeros(ng, dtype=torch.float64, device=d)
+    r, p = dev(torch, d, b), dev(torch, d, b)
+    q = torch.empty(ng, dtype=torch.float64, device=d)
+    pl = torch.empty(l2g.size, dtype=torch.float64, device=d)
+    h = host(bs.bs_cg_solve(t["l2g"], t["off"], t["ids"], x, r, p, q, pl, iters, 0.0, t["plan"]))
+    assert_rel(h[0], ohist[0], "rr0")
+    assert_rel(h[1], ohist[1], "rr1")
+    assert abs(h[2] - ohist[2]) <= 1e-9 * ohist[2]
+    assert math.sqrt(h[iters] / h[0]) < 1e-10
+    assert np.allclose(host(x), b / m, rtol=1e-9, atol=1e-12)
+    assert np.allclose(ox, b / m, rtol=1e-9, atol=1e-12)
