@@ -77,12 +77,18 @@ class Mesh:
     ORDER = ["copy_x", "copy_y", "axpy_x", "axpy_y", "norm_x", "dot_x", "dot_y", "cg_p", "cg_q", "cg_x",
              "cg_r", "l2g", "sc_vg", "sc_vl", "off", "ids", "plan", "ga_vl", "ga_vg", "out"]
 
-    def __init__(self, bs, torch, dev, name, E, N, gather_lds, layout="arena"):
-        ep, npm = bs_inputs.mesh_perms(name, E, N)
+    def __init__(self, bs, torch, dev, name, E, N, gather_lds, layout="arena", tables=None):
+        """A box of E^3 elements of order N, or, with tables = (l2g, n_global),
+        any mesh whose I_l->g is given."""
         self.name, self.E, self.N = name, E, N
         self.torch, self.dev, self.layout = torch, dev, layout
-        self.nl, self.ng = bs.bs_mesh_box_count(E, E, E, N)
-        l2g = bs.bs_mesh_box_l2g(E, E, E, N, ep, npm)
+        if tables is None:
+            ep, npm = bs_inputs.mesh_perms(name, E, N)
+            self.nl, self.ng = bs.bs_mesh_box_count(E, E, E, N)
+            l2g = bs.bs_mesh_box_l2g(E, E, E, N, ep, npm)
+        else:
+            l2g, self.ng = tables
+            self.nl = l2g.size
         off, ids = bs.bs_index_g2l(l2g, self.ng)
         plan = bs.bs_gather_plan(off, GATHER_NPB)
         v = bs_inputs.vectors(name, self.ng)
@@ -218,17 +224,29 @@ def cpu_baseline(mesh_host, budget_s=12.0):
         oracle.gather(h["l2g"], h["vl"], n)
         t += time.perf_counter() - t0
         reps += 1
+    model = "unknown CPU"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": round(nb * reps / t / 1e9, 3), "unit": "GB/s", "cores": oracle.threads(),
             "kind": "oracle",
             "sample": f"{reps} full step(s) of the 32^3 order-7 mesh (all 7 ops, oracle tables), "
-                      f"{t:.1f} s of CPU time"}
+                      f"{t:.1f} s of wall time on {oracle.threads()} OpenMP threads of {model}"}
 
 
-def sweep(bs, torch, dev, reps_min=50):
-    """c3: each vector op over n = 2^10 .. 2^28, fitted to T(B) = T0 + B/W_max."""
-    L, h = bs._lib(), bs.context().handle
+def sweep(bs, torch, dev, reps_min=100, min_seconds=0.05):
+    """c3: each vector op over n = 2^10 .. 2^28, fitted to T(B) = T0 + B/W_max.
+    The launches of each point are issued by the library's C++ loop
+    (bs_bench_loop), timed on the host around the whole run as the pages
+    time it; at least reps_min launches and min_seconds per point."""
     stream = torch.cuda.current_stream().cuda_stream
     res = {op: [] for op in ["copy", "axpy", "norm", "dot", "cg_update"]}
+    arity = {"copy": 2, "axpy": 2, "norm": 1, "dot": 2, "cg_update": 4}
+    out = torch.zeros(1, dtype=torch.float64, device=dev)
     for k in range(10, 29):
         n = 1 << k
         per = 48 * n
@@ -236,30 +254,12 @@ def sweep(bs, torch, dev, reps_min=50):
         R = min(R, 64)
         sets = [[torch.empty(n, dtype=torch.float64, device=dev).uniform_(-1, 1) for _ in range(4)]
                 for _ in range(R)]
-        out = torch.zeros(4, dtype=torch.float64, device=dev)
-        o = out.data_ptr()
         for op in res:
-            def one(i):
-                a, b, c, d = (t.data_ptr() for t in sets[i % R])
-                if op == "copy":
-                    return L.bs_copy(h, n, a, b, stream)
-                if op == "axpy":
-                    return L.bs_axpy(h, n, 0.37, a, 1.0, b, stream)
-                if op == "norm":
-                    return L.bs_norm(h, n, a, o, stream)
-                if op == "dot":
-                    return L.bs_dot(h, n, a, b, o, stream)
-                return L.bs_cg_update(h, n, 0.37, a, b, c, d, o, stream)
-            reps = max(reps_min, R)
-            for i in range(min(reps, 8)):
-                one(i)
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for i in range(reps):
-                if one(i) != 0:
-                    raise RuntimeError(op)
-            torch.cuda.synchronize()
-            T = (time.perf_counter() - t0) / reps
+            groups = [tuple(s[:arity[op]]) for s in sets]
+            bs.bs_bench_loop(op, n, groups, max(R, 8), out, stream=stream)  # warm-up
+            t_one = bs.bs_bench_loop(op, n, groups, max(R, 8), out, stream=stream) / max(R, 8)
+            reps = max(reps_min, R, int(np.ceil(min_seconds / max(t_one, 1e-7))))
+            T = bs.bs_bench_loop(op, n, groups, reps, out, stream=stream) / reps
             res[op].append((op_bytes(op, n), T))
         del sets
         torch.cuda.empty_cache()
@@ -273,13 +273,29 @@ def sweep(bs, torch, dev, reps_min=50):
     return out
 
 
+def tet_split_tables(bs, cubes, N, seed):
+    """I_l->g of the unstructured tet-split mesh (cubes^3 unit cubes, 24
+    hexahedra each, every element in a random orientation)."""
+    ev, nv, _ = bs_inputs.hex_tet_split(cubes, cubes, cubes)
+    ev, _ = bs_inputs.hex_orient(ev, seed)
+    return bs.bs_mesh_hex_l2g(ev, N, nv)
+
+
 def workloads(bs, torch, dev, gather_lds, steps=30):
-    """The shuffled 40^3 order-5 mesh (scatter, gather) and the 24^3 order-15
-    mesh (all 7 ops, and the CG streaming sequence)."""
+    """The shuffled 40^3 order-5 mesh (scatter, gather), the unstructured
+    tet-split mesh of 11^3 cubes (31944 hexahedra) at order 7 (scatter,
+    gather) and the 24^3 order-15 mesh (all 7 ops, and the CG streaming
+    sequence)."""
     out = {}
     for name, E, N, ops in [("c4_shuffled40_N5", 40, 5, ["scatter", "gather"]),
+                            ("u_tetsplit11_N7", 11, 7, ["scatter", "gather"]),
                             ("c5_box24_N15", 24, 15, OPS)]:
-        m = Mesh(bs, torch, dev, name, E, N, gather_lds)
+        tables = None
+        if name.startswith("u_"):
+            tables = tet_split_tables(bs, E, N, bs_inputs.base_seed(name) + bs_inputs.SEED_ELEM)
+        m = Mesh(bs, torch, dev, name, E, N, gather_lds, tables=tables)
+        if tables is not None:
+            out[name + "_mesh"] = {"elements": 24 * E ** 3, "order": N, "n_local": m.nl, "n_global": m.ng}
         stream = torch.cuda.current_stream().cuda_stream
         R = 3 if name.startswith("c5") else 5
         sets = [m] + [m.clone() for _ in range(R - 1)]

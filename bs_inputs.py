@@ -74,7 +74,8 @@ MESHES = {
     "c5_box24_N15": (24, 15, False),
 }
 CONFIG_INDEX = {"c1_box8_N3": 0, "c2_box32_N7": 1, "c3_sweep": 2,
-                "c4_shuffled40_N5": 3, "c5_box24_N15": 4}
+                "c4_shuffled40_N5": 3, "c5_box24_N15": 4,
+                "u_tetsplit11_N7": 5}  # unstructured: 11^3 cubes cut into 24 hexahedra each
 
 
 def base_seed(name: str) -> int:

@@ -71,6 +71,7 @@ SIGNATURES = {
     "bs_validate_l2g": ([_i64, _i64, _ptr], _int),
     "bs_index_g2l": ([_i64, _i64, _ptr, _ptr, _ptr], _int),
     "bs_gather_plan": ([_i64, _ptr, _int, _ptr, ctypes.POINTER(_i64)], _int),
+    "bs_bench_loop": ([_ptr, _int, _i64, _dbl, _dbl, _int, _ptr, _ptr, _int, _ptr, ctypes.POINTER(_dbl)], _int),
 }
 
 
@@ -418,9 +419,42 @@ def bs_gather_plan(off, nodes_per_block=1024):
     return bs[:nb.value + 1].copy()
 
 
+BS_OP = {"copy": 0, "axpy": 1, "norm": 2, "dot": 3, "cg_update": 4, "scale": 5}
+
+
+def bs_bench_loop(op, n, sets, reps, result=None, alpha=0.37, beta=1.0, *, ctx=None, stream=None):
+    """Host seconds for `reps` back-to-back launches of `op` issued from C++,
+    cycling through `sets` (a list of tuples of float64 device tensors, each
+    of at least n elements, in the order the header lists for the op)."""
+    import torch
+    if op not in BS_OP:
+        raise ValueError(f"unknown op {op!r}")
+    need = {"copy": 2, "axpy": 2, "norm": 1, "dot": 2, "cg_update": 4, "scale": 3}[op]
+    if not sets:
+        raise ValueError("at least one pointer set is needed")
+    ptrs = (ctypes.c_void_p * (4 * len(sets)))()
+    for k, group in enumerate(sets):
+        if len(group) != need:
+            raise ValueError(f"{op} takes {need} tensors per set")
+        for j, t in enumerate(group):
+            ptrs[4 * k + j] = _dev_tensor(t, torch.float64, f"sets[{k}][{j}]")
+            if t.numel() < n:
+                raise ValueError(f"sets[{k}][{j}] holds fewer than n elements")
+    dev = sets[0][0].device
+    if op in ("norm", "dot", "cg_update"):
+        result = _scalar_out(result, sets[0][0])
+    ctx = _ctx_dev(sets[0][0], ctx)
+    sec = _dbl()
+    _check(_lib().bs_bench_loop(ctx.handle, BS_OP[op], int(n), float(alpha), float(beta), len(sets), ptrs,
+                                None if result is None else result.data_ptr(), int(reps), _stream(stream, dev),
+                                ctypes.byref(sec)), "bs_bench_loop")
+    return sec.value
+
+
 __all__ = [
     "BSError", "Context", "context", "LIB_PATH", "SIGNATURES",
     "bs_copy", "bs_axpy", "bs_norm", "bs_dot", "bs_cg_update", "bs_scatter", "bs_gather",
     "bs_gather_dot", "bs_cg_solve", "bs_scale", "bs_gll", "bs_mesh_box_mass",
+    "bs_bench_loop", "BS_OP",
     "bs_mesh_box_count", "bs_mesh_box_l2g", "bs_mesh_hex_l2g", "bs_validate_l2g", "bs_index_g2l", "bs_gather_plan",
 ]

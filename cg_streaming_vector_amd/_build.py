@@ -10,7 +10,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libbs.so")
 
-SOURCES = [os.path.join(CSRC, "bs_kernels.hip"), os.path.join(CSRC, "bs_host.cpp")]
+SOURCES = [os.path.join(CSRC, "bs_kernels.hip"), os.path.join(CSRC, "bs_host.cpp"),
+           os.path.join(CSRC, "bs_bench.cpp")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -578,3 +578,30 @@ def test_unstructured_cg_solve(env):
     assert math.sqrt(h[iters] / h[0]) < 1e-10
     assert np.allclose(host(x), b / m, rtol=1e-9, atol=1e-12)
     assert np.allclose(ox, b / m, rtol=1e-9, atol=1e-12)
+
+
+# -------------------------------------------------------- launch loop -----
+
+def test_bench_loop_runs_the_operations(env):
+    """bs_bench_loop issues the real operations: after a loop over two sets
+    the outputs are those of the last call on each set."""
+    bs, orc, torch, d = env
+    n = 100_003
+    xs = [dev(torch, d, bs_inputs.uniform_pm1(731 + k, n)) for k in range(2)]
+    ys = [dev(torch, d, bs_inputs.uniform_pm1(741 + k, n)) for k in range(2)]
+    out = torch.zeros(1, dtype=torch.float64, device=d)
+    t = bs.bs_bench_loop("norm", n, [(xs[0],), (xs[1],)], 5, out)
+    assert t > 0
+    assert_rel(out.item(), orc.norm(host(xs[0])), "norm via loop")  # call 4 used set 0
+    ycopy = [torch.empty_like(x) for x in xs]
+    bs.bs_bench_loop("copy", n, [(xs[0], ycopy[0]), (xs[1], ycopy[1])], 2)
+    assert_bits(host(ycopy[0]), host(xs[0]), "copy via loop set 0")
+    assert_bits(host(ycopy[1]), host(xs[1]), "copy via loop set 1")
+    y0 = host(ys[0])
+    bs.bs_bench_loop("axpy", n, [(xs[0], ys[0])], 1, alpha=0.37, beta=1.0)
+    assert_bits(host(ys[0]), orc.axpy(0.37, host(xs[0]), 1.0, y0), "axpy via loop")
+    with pytest.raises(bs.BSError):
+        bs._check(bs._lib().bs_bench_loop(bs.context().handle, 9, n, 1.0, 1.0, 1, None, None, 1, None,
+                                           None), "bad op")
+    with pytest.raises(ValueError):
+        bs.bs_bench_loop("dot", n + 1, [(xs[0], ys[0])], 1, out)
