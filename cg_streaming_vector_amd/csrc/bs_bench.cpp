@@ -35,7 +35,7 @@ extern "C" int bs_bench_loop(bs_ctx *ctx, int op, int64_t n, double alpha, doubl
         case BS_OP_SCALE: rc = bs_scale(ctx, n, a, b, c, stream); break;
         }
         if (rc != BS_OK) {
-            hipStreamSynchronize(st);
+            (void)hipStreamSynchronize(st);
             return rc;
         }
     }
