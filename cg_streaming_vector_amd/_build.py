@@ -38,5 +38,20 @@ def build(extra_flags=(), out: str = LIB, verbose: bool = False) -> str:
     return out
 
 
+def resource_report(out: str) -> str:
+    """The compiler's per-kernel register, spill, LDS and occupancy report for
+    the device code, built with the library's own flags, written to `out`."""
+    cmd = [hipcc(), *[f for f in HIPCC_FLAGS if f not in ("-shared", "-fPIC")],
+           "-Rpass-analysis=kernel-resource-usage", "-c", SOURCES[0], "-o", os.devnull]
+    r = subprocess.run(cmd, check=True, capture_output=True, text=True)
+    with open(out, "w") as f:
+        f.write(r.stderr)
+    return out
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import sys
+    if len(sys.argv) == 3 and sys.argv[1] == "--resource-report":
+        print(resource_report(sys.argv[2]))
+    else:
+        print(build(verbose=True))

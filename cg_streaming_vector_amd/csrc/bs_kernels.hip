@@ -16,7 +16,7 @@
 //    order. No atomics anywhere, so results repeat bit for bit;
 //  - scatter: each lane owns pairs of consecutive local entries, loads their
 //    two indices as one 8-byte word and stores the two values as one 16-byte
-//    word, 16 pairs per lane in flight;
+//    word, 32 pairs per lane in flight;
 //  - gather: the balanced blockStarts scheme of the paper, each block staging
 //    at most 1024 CSR entries of v_L in LDS with coalesced index loads, then
 //    one lane per global node summing its entries from LDS in ascending order;

@@ -62,8 +62,64 @@ def load_counter(path, counter):
     return out
 
 
-def summarize(stats_csv, fetch_csv, write_csv, copy_kernel, copy_doubles, source=None, ops=None):
+def load_resources(path):
+    """kernel -> LDS, scratch and launch shape from a *_kernel_trace.csv file
+    (the first dispatch of each kernel; the largest grid seen). Register
+    counts are taken from the compiler's report instead (load_remarks): the
+    trace's VGPR field counts allocation granules of 4 registers, while gfx950
+    allocates in granules of 8."""
+    out = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            k = short_name(row["Kernel_Name"])
+            wg = int(row["Workgroup_Size_X"]) * int(row["Workgroup_Size_Y"]) * int(row["Workgroup_Size_Z"])
+            grid = int(row["Grid_Size_X"]) * int(row["Grid_Size_Y"]) * int(row["Grid_Size_Z"])
+            if k not in out:
+                out[k] = {"lds_bytes": int(row["LDS_Block_Size"]), "scratch_bytes": int(row["Scratch_Size"]),
+                          "workgroup": wg, "max_workgroups": 0}
+            out[k]["max_workgroups"] = max(out[k]["max_workgroups"], grid // max(wg, 1))
+    return out
+
+
+REMARK_KEYS = {"TotalSGPRs": "sgpr", "VGPRs": "vgpr", "AGPRs": "agpr", "ScratchSize [bytes/lane]": "scratch_per_lane",
+               "Occupancy [waves/SIMD]": "occupancy", "SGPRs Spill": "sgpr_spill", "VGPRs Spill": "vgpr_spill",
+               "LDS Size [bytes/block]": "lds_static"}
+
+
+def load_remarks(path, demangle=None):
+    """kernel -> register use, spills and occupancy from the compiler's
+    -Rpass-analysis=kernel-resource-usage remarks (hipcc's stderr)."""
+    import re
+    if demangle is None:
+        demangle = _cxxfilt
+    out, cur = {}, None
+    with open(path) as f:
+        for line in f:
+            m = re.search(r"Function Name: (\S+)", line)
+            if m:
+                cur = short_name(demangle(m.group(1)))
+                out[cur] = {}
+                continue
+            m = re.search(r"remark: \s*([^:]+?): (\S+) \[-Rpass-analysis", line)
+            if cur and m and m.group(1).strip() in REMARK_KEYS:
+                v = m.group(2)
+                out[cur][REMARK_KEYS[m.group(1).strip()]] = int(v) if v.isdigit() else v
+    return out
+
+
+def _cxxfilt(name):
+    import subprocess
+    try:
+        return subprocess.run(["c++filt", name], capture_output=True, text=True, check=True).stdout.strip()
+    except (OSError, subprocess.CalledProcessError):
+        return name
+
+
+def summarize(stats_csv, fetch_csv, write_csv, copy_kernel, copy_doubles, source=None, ops=None, trace_csv=None,
+              remarks=None):
     stats = load_stats(stats_csv) if stats_csv else {}
+    res = load_resources(trace_csv) if trace_csv else {}
+    rem = load_remarks(remarks) if remarks else {}
     fetch = load_counter(fetch_csv, "FETCH_SIZE") if fetch_csv else {}
     write = load_counter(write_csv, "WRITE_SIZE") if write_csv else {}
     known = 8.0 * copy_doubles
@@ -72,7 +128,8 @@ def summarize(stats_csv, fetch_csv, write_csv, copy_kernel, copy_doubles, source
         f_scale = known / (statistics.median(fetch[copy_kernel]) * 1024.0)
         w_scale = known / (statistics.median(write[copy_kernel]) * 1024.0)
     kernels = {}
-    for k in sorted(set(stats) | set(fetch) | set(write)):
+    names = set(stats) | set(fetch) | set(write) | set(res)
+    for k in sorted(names or set(rem)):
         if k.startswith("__amd") or "at::native" in k:
             continue
         d = {}
@@ -82,6 +139,10 @@ def summarize(stats_csv, fetch_csv, write_csv, copy_kernel, copy_doubles, source
             d["fetch_kib_median"] = statistics.median(fetch[k])
         if k in write:
             d["write_kib_median"] = statistics.median(write[k])
+        if k in res:
+            d["resources"] = res[k]
+        if k in rem:
+            d["compiler"] = rem[k]
         if f_scale and k in fetch and k in write:
             d["hbm_bytes_per_launch"] = (d["fetch_kib_median"] * 1024.0 * f_scale
                                          + d["write_kib_median"] * 1024.0 * w_scale)
@@ -115,6 +176,17 @@ def to_markdown(summary, title, commands):
             f"{d['fetch_kib_median']:.0f}" if "fetch_kib_median" in d else "",
             f"{d['write_kib_median']:.0f}" if "write_kib_median" in d else "",
             f"{d['hbm_bytes_per_launch'] / 1e6:.2f}" if "hbm_bytes_per_launch" in d else ""))
+    if any("resources" in d or "compiler" in d for d in summary["kernels"].values()):
+        lines += ["", "| kernel | VGPR | AGPR | SGPR | spills (V/S) | occupancy (waves/SIMD) | LDS B | scratch B "
+                  "| workgroup | max workgroups |", "|---|---|---|---|---|---|---|---|---|---|"]
+        for k, d in summary["kernels"].items():
+            c, r = d.get("compiler", {}), d.get("resources", {})
+            if not c and not r:
+                continue
+            lines.append(f"| `{k}` | {c.get('vgpr', '')} | {c.get('agpr', '')} | {c.get('sgpr', '')} | "
+                         f"{c.get('vgpr_spill', '')}/{c.get('sgpr_spill', '')} | {c.get('occupancy', '')} | "
+                         f"{r.get('lds_bytes', c.get('lds_static', ''))} | {r.get('scratch_bytes', '')} | "
+                         f"{r.get('workgroup', '')} | {r.get('max_workgroups', '')} |")
     if summary.get("ops"):
         lines += ["", "| operation | kernels | avg us (sum) |", "|---|---|---|"]
         for name, d in summary["ops"].items():
@@ -127,6 +199,8 @@ def to_markdown(summary, title, commands):
 def main(argv=None):
     ap = argparse.ArgumentParser(description="Summarize rocprofv3 CSV output of the BS kernels")
     ap.add_argument("--stats")
+    ap.add_argument("--trace", help="*_kernel_trace.csv: LDS, scratch and grid per kernel")
+    ap.add_argument("--remarks", help="hipcc -Rpass-analysis=kernel-resource-usage output: registers, occupancy")
     ap.add_argument("--fetch")
     ap.add_argument("--write")
     ap.add_argument("--copy-kernel", default="k_copy<1>")
@@ -139,7 +213,7 @@ def main(argv=None):
     ap.add_argument("--md")
     a = ap.parse_args(argv)
     ops = {o.split("=", 1)[0]: o.split("=", 1)[1].split("+") for o in a.op}
-    s = summarize(a.stats, a.fetch, a.write, a.copy_kernel, a.copy_doubles, a.source, ops)
+    s = summarize(a.stats, a.fetch, a.write, a.copy_kernel, a.copy_doubles, a.source, ops, a.trace, a.remarks)
     if a.json:
         with open(a.json, "w") as f:
             json.dump(s, f, indent=1)

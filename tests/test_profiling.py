@@ -45,3 +45,39 @@ def test_calibrated_traffic(tmp_path):
     assert k["calls"] == 7 and k["avg_ns"] == 1500.0
     md = profiling.to_markdown(s, "t", ["rocprofv3 ..."])
     assert "k_scatter" in md and "rocprofv3 ..." in md
+
+
+def test_resources_from_trace(tmp_path):
+    hdr = ["Kernel_Name", "VGPR_Count", "Accum_VGPR_Count", "SGPR_Count", "LDS_Block_Size", "Scratch_Size",
+           "Workgroup_Size_X", "Workgroup_Size_Y", "Workgroup_Size_Z", "Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z"]
+    with open(tmp_path / "t.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(hdr)
+        w.writerow(["(anonymous namespace)::k_scatter(y)", 92, 0, 24, 0, 0, 256, 1, 1, 256 * 1024, 1, 1])
+        w.writerow(["(anonymous namespace)::k_scatter(y)", 92, 0, 24, 0, 0, 256, 1, 1, 256 * 4096, 1, 1])
+        w.writerow(["void (anonymous namespace)::k_gather_plan<false>(z)", 8, 0, 30, 12800, 0, 256, 1, 1, 2560, 1,
+                    1])
+    r = profiling.load_resources(tmp_path / "t.csv")
+    assert r["k_scatter"]["max_workgroups"] == 4096 and r["k_scatter"]["workgroup"] == 256
+    assert r["k_gather_plan<false>"]["lds_bytes"] == 12800 and r["k_gather_plan<false>"]["max_workgroups"] == 10
+
+
+def test_compiler_remarks(tmp_path):
+    text = """x.hip:1:1: remark: Function Name: _Z1kv [-Rpass-analysis=kernel-resource-usage]
+x.hip:1:1: remark:     TotalSGPRs: 28 [-Rpass-analysis=kernel-resource-usage]
+x.hip:1:1: remark:     VGPRs: 46 [-Rpass-analysis=kernel-resource-usage]
+x.hip:1:1: remark:     AGPRs: 0 [-Rpass-analysis=kernel-resource-usage]
+x.hip:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]
+x.hip:1:1: remark:     Occupancy [waves/SIMD]: 2 [-Rpass-analysis=kernel-resource-usage]
+x.hip:1:1: remark:     VGPRs Spill: 0 [-Rpass-analysis=kernel-resource-usage]
+x.hip:1:1: remark:     LDS Size [bytes/block]: 32 [-Rpass-analysis=kernel-resource-usage]
+"""
+    (tmp_path / "r.txt").write_text(text)
+    r = profiling.load_remarks(tmp_path / "r.txt", demangle=lambda n: "void (anonymous namespace)::k_dot<4, false>()")
+    k = r["k_dot<4, false>"]
+    assert k["vgpr"] == 46 and k["sgpr"] == 28 and k["occupancy"] == 2 and k["vgpr_spill"] == 0
+    assert k["lds_static"] == 32 and k["scratch_per_lane"] == 0
+    s = profiling.summarize(None, None, None, "k_copy<1>", 1, remarks=None)
+    s["kernels"]["k_dot<4, false>"] = {"compiler": k}
+    md = profiling.to_markdown(s, "t", [])
+    assert "| `k_dot<4, false>` | 46 | 0 | 28 | 0/ | 2 |" in md
