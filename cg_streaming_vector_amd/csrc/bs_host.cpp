@@ -31,6 +31,7 @@
 
 namespace {
 
+// Throws std::bad_alloc; every caller converts that into BS_ENOMEM.
 bool is_permutation(const int32_t *p, int64_t n)
 {
     std::vector<uint8_t> seen((size_t)n, 0);
@@ -118,8 +119,12 @@ int bs_mesh_box_l2g(int ex, int ey, int ez, int order, const int32_t *elem_perm,
     if (int s = bs_mesh_box_count(ex, ey, ez, order, &nl, &ng)) return s;
     if (!l2g) return BS_EINVAL;
     const int64_t K = (int64_t)ex * ey * ez;
-    if (elem_perm && !is_permutation(elem_perm, K)) return BS_EINVAL;
-    if (node_perm && !is_permutation(node_perm, ng)) return BS_EINVAL;
+    try {
+        if (elem_perm && !is_permutation(elem_perm, K)) return BS_EINVAL;
+        if (node_perm && !is_permutation(node_perm, ng)) return BS_EINVAL;
+    } catch (const std::bad_alloc &) {
+        return BS_ENOMEM;
+    }
     const int64_t nq = order + 1, Np = nq * nq * nq;
     const int64_t Gx = (int64_t)ex * order + 1, Gy = (int64_t)ey * order + 1;
     for (int64_t s = 0; s < K; ++s) {
@@ -314,7 +319,14 @@ int bs_mesh_box_mass(int ex, int ey, int ez, int order, double *w_local)
     if (int s = bs_mesh_box_count(ex, ey, ez, order, &nl, &ng)) return s;
     if (!w_local) return BS_EINVAL;
     const int64_t nq = order + 1, Np = nq * nq * nq, K = (int64_t)ex * ey * ez;
-    std::vector<double> r(nq), w(nq), block(Np);
+    std::vector<double> r, w, block;
+    try {
+        r.resize(nq);
+        w.resize(nq);
+        block.resize(Np);
+    } catch (const std::bad_alloc &) {
+        return BS_ENOMEM;
+    }
     bs_gll(order, r.data(), w.data());
     // one element's weights, w_i w_j w_k times the Jacobian 1/8 of the map
     // from [-1,1]^3 onto a unit cube; every element of the box is a unit cube
@@ -347,7 +359,12 @@ int bs_index_g2l(int64_t n_local, int64_t n_global, const int32_t *l2g, int32_t 
         ++off[g + 1];
     }
     for (int64_t g = 0; g < n_global; ++g) off[g + 1] += off[g];
-    std::vector<int32_t> cursor(off, off + n_global);
+    std::vector<int32_t> cursor;
+    try {
+        cursor.assign(off, off + n_global);
+    } catch (const std::bad_alloc &) {
+        return BS_ENOMEM;
+    }
     for (int64_t i = 0; i < n_local; ++i) {
         const int32_t g = l2g[i];
         if (g >= 0) ids[cursor[(size_t)g]++] = (int32_t)i;

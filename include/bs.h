@@ -186,7 +186,8 @@ int bs_mesh_box_count(int ex, int ey, int ez, int order, int64_t *n_local, int64
  * id is gx + Gx*(gy + Gy*gz) with gx = cx*order + i, Gx = ex*order + 1 (same for
  * y, z); node_perm (NULL: identity) renames id g to node_perm[g]. Both
  * permutations must be permutations (checked: BS_EINVAL). l2g receives
- * int32[n_local]. */
+ * int32[n_local]. Sizes as bs_mesh_box_count; BS_ENOMEM if the host memory
+ * for the permutation check is not available. */
 int bs_mesh_box_l2g(int ex, int ey, int ez, int order, const int32_t *elem_perm,
                     const int32_t *node_perm, int32_t *l2g);
 
@@ -227,7 +228,8 @@ int bs_gll(int order, double *nodes, double *weights);
  * from [-1,1]^3 onto the unit cube), in the local layout of bs_mesh_box_l2g.
  * The lumped global mass is their gather, m = Z^T w_L (arXiv 1506.05996,
  * coarse-grid correction: m_N as the global components of the local weights).
- * w_local receives double[n_local]. Errors as bs_mesh_box_count. */
+ * w_local receives double[n_local]. Errors as bs_mesh_box_count, BS_EINVAL
+ * for a NULL output, BS_ENOMEM without host memory for one element's block. */
 int bs_mesh_box_mass(int ex, int ey, int ez, int order, double *w_local);
 
 /* Check that every id is < n_global (negative ids are masks): BS_OK or
@@ -237,7 +239,9 @@ int bs_validate_l2g(int64_t n_local, int64_t n_global, const int32_t *l2g);
 /* CSR form of I_g->l: a stable counting-sort transpose of l2g. off receives
  * int32[n_global+1]; ids receives the off[n_global] local indices (at most
  * n_local; masked entries are left out), ascending within each row. An id
- * >= n_global is BS_EINVAL. */
+ * >= n_global is BS_EINVAL (off and ids may then be partly written);
+ * n_local > INT32_MAX or n_global >= INT32_MAX is BS_ERANGE; BS_ENOMEM
+ * without host memory for the n_global fill cursors. */
 int bs_index_g2l(int64_t n_local, int64_t n_global, const int32_t *l2g, int32_t *off,
                  int32_t *ids);
 
