@@ -161,11 +161,12 @@ class Mesh:
         return op_bytes(op, self.ng, self.nl, self.ng)
 
 
-def time_ops_rotated(torch, sets_launch, ops, reps):
+def time_ops_rotated(torch, sets_launch, ops, reps, trials=1):
     """Average time per launch of each op, launched `reps` times back to back,
     cycling through the arrays of len(sets_launch) distinct sets so that no
     launch finds its operands in cache; HIP events on the launch stream
-    bracket each op's loop."""
+    bracket each op's loop. With trials > 1, returns op -> list of the
+    trials' averages."""
     stream = torch.cuda.current_stream()
     R = len(sets_launch)
     out = {}
@@ -173,14 +174,33 @@ def time_ops_rotated(torch, sets_launch, ops, reps):
         for i in range(R):
             sets_launch[i][op]()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(reps):
-            sets_launch[i % R][op]()
-        e1.record(stream)
-        e1.synchronize()
-        out[op] = e0.elapsed_time(e1) * 1e-3 / reps
+        res = []
+        for _ in range(trials):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(reps):
+                sets_launch[i % R][op]()
+            e1.record(stream)
+            e1.synchronize()
+            res.append(e0.elapsed_time(e1) * 1e-3 / reps)
+        out[op] = res if trials > 1 else res[0]
     return out
+
+
+def copy_ceiling(bs, torch, dev, k=28):
+    """GB/s of the library's own copy at 2^k doubles (two array pairs used in
+    turn, 4.3 GB per pair at k = 28): the best sustained mixed read+write rate
+    this memory system gave any kernel here."""
+    n = 1 << k
+    pairs = [(torch.empty(n, dtype=torch.float64, device=dev), torch.empty(n, dtype=torch.float64, device=dev))
+             for _ in range(2)]
+    for a, _ in pairs:
+        a.uniform_(-1, 1)
+    bs.bs_bench_loop("copy", n, pairs, 4)
+    t = min(bs.bs_bench_loop("copy", n, pairs, 20) / 20 for _ in range(3))
+    del pairs
+    torch.cuda.empty_cache()
+    return 16 * n / t / 1e9
 
 
 def traffic_for(kernels):
@@ -403,6 +423,7 @@ def main():
     ap.add_argument("--layout", choices=["arena", "torch"], default="arena",
                     help="arena: each set's arrays packed in one allocation on 2 MB boundaries")
     ap.add_argument("--per-op-reps", type=int, default=96)
+    ap.add_argument("--trials", type=int, default=5, help="per-op loops repeated; the median is reported")
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--workloads", action="store_true")
     ap.add_argument("--out", default=None)
@@ -430,9 +451,12 @@ def main():
     # (ROT x the smallest operation's bytes > 1 GB, beyond the 256 MB cache)
     sets = [mesh] + [mesh.clone() for _ in range(args.rotate - 1)]
     sets_launch = [m.launchers(bs, stream) for m in sets]
-    per_op = time_ops_rotated(torch, sets_launch, OPS, args.per_op_reps)
+    trials = time_ops_rotated(torch, sets_launch, OPS, args.per_op_reps, trials=args.trials)
+    per_op = {op: float(np.median(t)) for op, t in trials.items()}
     dom = max(OPS, key=lambda op: per_op[op])
     del sets_launch, sets
+    # the same loops on one set: operands that fit stay in the 256 MB cache
+    hot = time_ops_rotated(torch, [launch], OPS, args.per_op_reps)
     torch.cuda.empty_cache()
 
     # timed region: host clock around K steps; HIP events on the launch
@@ -457,12 +481,15 @@ def main():
     ms_step = dt / args.steps * 1e3
     value = step_bytes / (dt / args.steps) / 1e9
 
+    ceiling = copy_ceiling(bs, torch, dev)
     ops_out = {}
     for op in OPS:
         t = per_op[op]
         gbps = mesh.bytes(op) / t / 1e9
-        ops_out[op] = {"bytes": mesh.bytes(op), "us": round(t * 1e6, 2), "GBps": round(gbps, 1),
-                       "pct_peak": round(100 * gbps / PEAK_GBPS, 1)}
+        ops_out[op] = {"bytes": mesh.bytes(op), "us": round(t * 1e6, 2), "us_best": round(min(trials[op]) * 1e6, 2),
+                       "GBps": round(gbps, 1), "pct_peak": round(100 * gbps / PEAK_GBPS, 1),
+                       "pct_copy_ceiling": round(100 * gbps / ceiling, 1),
+                       "hot_us": round(hot[op] * 1e6, 2)}
     achieved = mesh.bytes(dom) / dom_live / 1e9
     traffic = traffic_for(KERNEL_NAME[dom])
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
@@ -498,6 +525,11 @@ def main():
         "pct_peak": round(100 * value / PEAK_GBPS, 1),
         "per_op": ops_out,
         "runtime_copy_GBps": round(rt_copy, 1),
+        "copy_ceiling_GBps": round(ceiling, 1),
+        "per_op_note": f"us: median of {args.trials} trials of {args.per_op_reps} launches over {args.rotate} "
+                       "rotated array sets (cold); us_best: best trial; hot_us: one set, operands "
+                       "cache-resident where they fit; pct_copy_ceiling: against copy_ceiling_GBps, the "
+                       "library's copy of 2^28 doubles",
         "roofline": roofline,
     }
 
@@ -505,12 +537,12 @@ def main():
     if args.sweep:
         extra["sweep"] = sweep(bs, torch, dev)
     if args.workloads:
-        del launch
+        launch = None
         extra["workloads"] = workloads(bs, torch, dev, args.gather == "lds")
 
     if not args.no_cpu_baseline:
         import oracle
-        del launch
+        launch = None
         host = {"ng": mesh.ng, "nl": mesh.nl}
         v = bs_inputs.vectors(name, mesh.ng)
         host.update(v)
