@@ -157,32 +157,37 @@ class Mesh:
             return call
         return {op: mk(fn, args, op) for op, (fn, args) in a.items()}
 
+    def bench_set(self, op):
+        """(n, tensors, n_blocks) of this set for bs_bench_loop."""
+        plan = self.plan if self.gather_lds else None
+        return {
+            "copy": (self.ng, (self.copy_x, self.copy_y), 0),
+            "axpy": (self.ng, (self.axpy_x, self.axpy_y), 0),
+            "norm": (self.ng, (self.norm_x,), 0),
+            "dot": (self.ng, (self.dot_x, self.dot_y), 0),
+            "cg_update": (self.ng, (self.cg_p, self.cg_q, self.cg_x, self.cg_r), 0),
+            "scatter": (self.nl, (self.l2g, self.sc_vg, self.sc_vl), 0),
+            "gather": (self.ng, (self.off, self.ids, self.ga_vl, self.ga_vg, plan),
+                       self.plan.numel() - 1 if self.gather_lds else 0),
+        }[op]
+
     def bytes(self, op):
         return op_bytes(op, self.ng, self.nl, self.ng)
 
 
-def time_ops_rotated(torch, sets_launch, ops, reps, trials=1):
-    """Average time per launch of each op, launched `reps` times back to back,
-    cycling through the arrays of len(sets_launch) distinct sets so that no
-    launch finds its operands in cache; HIP events on the launch stream
-    bracket each op's loop. With trials > 1, returns op -> list of the
-    trials' averages."""
-    stream = torch.cuda.current_stream()
-    R = len(sets_launch)
+def time_ops_native(bs, sets, ops, reps, trials=1):
+    """Average host-timed seconds per launch of each op: `reps` launches
+    issued back to back by the library's C++ loop, cycling through the
+    distinct array sets `sets` (Mesh objects) so that no launch finds its
+    operands in cache. With trials > 1, returns op -> list of the trials'
+    averages."""
     out = {}
     for op in ops:
-        for i in range(R):
-            sets_launch[i][op]()
-        torch.cuda.synchronize()
-        res = []
-        for _ in range(trials):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for i in range(reps):
-                sets_launch[i % R][op]()
-            e1.record(stream)
-            e1.synchronize()
-            res.append(e0.elapsed_time(e1) * 1e-3 / reps)
+        n, _, nb = sets[0].bench_set(op)
+        groups = [m.bench_set(op)[1] for m in sets]
+        res_t = sets[0].out[:1]
+        bs.bs_bench_loop(op, n, groups, len(groups), res_t, n_blocks=nb)  # one pass to warm up
+        res = [bs.bs_bench_loop(op, n, groups, reps, res_t, n_blocks=nb) / reps for _ in range(trials)]
         out[op] = res if trials > 1 else res[0]
     return out
 
@@ -304,22 +309,28 @@ def tet_split_tables(bs, cubes, N, seed):
 def workloads(bs, torch, dev, gather_lds, steps=30):
     """The shuffled 40^3 order-5 mesh (scatter, gather), the unstructured
     tet-split mesh of 11^3 cubes (31944 hexahedra) at order 7 (scatter,
-    gather) and the 24^3 order-15 mesh (all 7 ops, and the CG streaming
-    sequence)."""
+    gather), one GPU's share of the 32^3 order-7 mesh cut into eight z-slabs
+    (32 x 32 x 4 elements, all 7 ops) and the 24^3 order-15 mesh (all 7 ops,
+    and the CG streaming sequence)."""
     out = {}
     for name, E, N, ops in [("c4_shuffled40_N5", 40, 5, ["scatter", "gather"]),
                             ("u_tetsplit11_N7", 11, 7, ["scatter", "gather"]),
+                            ("c2_slab32x32x4_N7", 32, 7, OPS),
                             ("c5_box24_N15", 24, 15, OPS)]:
         tables = None
         if name.startswith("u_"):
             tables = tet_split_tables(bs, E, N, bs_inputs.base_seed(name) + bs_inputs.SEED_ELEM)
+        elif name.startswith("c2_slab"):
+            tables = (bs.bs_mesh_box_l2g(E, E, 4, N), bs.bs_mesh_box_count(E, E, 4, N)[1])
         m = Mesh(bs, torch, dev, name, E, N, gather_lds, tables=tables)
         if tables is not None:
-            out[name + "_mesh"] = {"elements": 24 * E ** 3, "order": N, "n_local": m.nl, "n_global": m.ng}
+            out[name + "_mesh"] = {"elements": 24 * E ** 3 if name.startswith("u_") else E * E * 4, "order": N,
+                                   "n_local": m.nl, "n_global": m.ng}
         stream = torch.cuda.current_stream().cuda_stream
-        R = 3 if name.startswith("c5") else 5
+        # rotated sets: >= 1 GB through the cache between two touches
+        R = 3 if name.startswith("c5") else 48 if name.startswith("c2_slab") else 5
         sets = [m] + [m.clone() for _ in range(R - 1)]
-        per_op = time_ops_rotated(torch, [x.launchers(bs, stream) for x in sets], ops, 3 * R)
+        per_op = time_ops_native(bs, sets, ops, max(3 * R, 96))
         del sets
         res = {op: {"bytes": m.bytes(op), "us": round(per_op[op] * 1e6, 2),
                     "GBps": round(m.bytes(op) / per_op[op] / 1e9, 1),
@@ -450,13 +461,12 @@ def main():
     # per operation: back-to-back launches over ROT sets of distinct arrays
     # (ROT x the smallest operation's bytes > 1 GB, beyond the 256 MB cache)
     sets = [mesh] + [mesh.clone() for _ in range(args.rotate - 1)]
-    sets_launch = [m.launchers(bs, stream) for m in sets]
-    trials = time_ops_rotated(torch, sets_launch, OPS, args.per_op_reps, trials=args.trials)
+    trials = time_ops_native(bs, sets, OPS, args.per_op_reps, trials=args.trials)
     per_op = {op: float(np.median(t)) for op, t in trials.items()}
     dom = max(OPS, key=lambda op: per_op[op])
-    del sets_launch, sets
+    del sets
     # the same loops on one set: operands that fit stay in the 256 MB cache
-    hot = time_ops_rotated(torch, [launch], OPS, args.per_op_reps)
+    hot = time_ops_native(bs, [mesh], OPS, args.per_op_reps)
     torch.cuda.empty_cache()
 
     # timed region: host clock around K steps; HIP events on the launch
@@ -526,8 +536,9 @@ def main():
         "per_op": ops_out,
         "runtime_copy_GBps": round(rt_copy, 1),
         "copy_ceiling_GBps": round(ceiling, 1),
-        "per_op_note": f"us: median of {args.trials} trials of {args.per_op_reps} launches over {args.rotate} "
-                       "rotated array sets (cold); us_best: best trial; hot_us: one set, operands "
+        "per_op_note": f"us: median of {args.trials} trials of {args.per_op_reps} back-to-back launches (issued by "
+                       f"the library's C++ loop, host-timed) over {args.rotate} rotated array sets (cold); us_best: "
+                       "best trial; hot_us: one set, operands "
                        "cache-resident where they fit; pct_copy_ceiling: against copy_ceiling_GBps, the "
                        "library's copy of 2^28 doubles",
         "roofline": roofline,

@@ -75,7 +75,8 @@ MESHES = {
 }
 CONFIG_INDEX = {"c1_box8_N3": 0, "c2_box32_N7": 1, "c3_sweep": 2,
                 "c4_shuffled40_N5": 3, "c5_box24_N15": 4,
-                "u_tetsplit11_N7": 5}  # unstructured: 11^3 cubes cut into 24 hexahedra each
+                "u_tetsplit11_N7": 5,  # unstructured: 11^3 cubes cut into 24 hexahedra each
+                "c2_slab32x32x4_N7": 6}  # one of eight z-slabs of the 32^3 order-7 box
 
 
 def base_seed(name: str) -> int:

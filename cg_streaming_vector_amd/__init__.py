@@ -71,7 +71,8 @@ SIGNATURES = {
     "bs_validate_l2g": ([_i64, _i64, _ptr], _int),
     "bs_index_g2l": ([_i64, _i64, _ptr, _ptr, _ptr], _int),
     "bs_gather_plan": ([_i64, _ptr, _int, _ptr, ctypes.POINTER(_i64)], _int),
-    "bs_bench_loop": ([_ptr, _int, _i64, _dbl, _dbl, _int, _ptr, _ptr, _int, _ptr, ctypes.POINTER(_dbl)], _int),
+    "bs_bench_loop": ([_ptr, _int, _i64, _dbl, _dbl, _i64, _int, _ptr, _ptr, _int, _ptr, ctypes.POINTER(_dbl)],
+                      _int),
 }
 
 
@@ -419,35 +420,57 @@ def bs_gather_plan(off, nodes_per_block=1024):
     return bs[:nb.value + 1].copy()
 
 
-BS_OP = {"copy": 0, "axpy": 1, "norm": 2, "dot": 3, "cg_update": 4, "scale": 5}
+BS_OP = {"copy": 0, "axpy": 1, "norm": 2, "dot": 3, "cg_update": 4, "scale": 5, "scatter": 6, "gather": 7}
+BS_BENCH_SET = 6
+# per op: (dtype letter per pointer slot, length each slot must reach: "n" or an int)
+_BENCH_SLOTS = {"copy": "dd", "axpy": "dd", "norm": "d", "dot": "dd", "cg_update": "dddd", "scale": "ddd",
+                "scatter": "idd", "gather": "iiddi"}
 
 
-def bs_bench_loop(op, n, sets, reps, result=None, alpha=0.37, beta=1.0, *, ctx=None, stream=None):
+def bs_bench_loop(op, n, sets, reps, result=None, alpha=0.37, beta=1.0, *, n_blocks=0, ctx=None, stream=None):
     """Host seconds for `reps` back-to-back launches of `op` issued from C++,
-    cycling through `sets` (a list of tuples of float64 device tensors, each
-    of at least n elements, in the order the header lists for the op)."""
+    cycling through `sets` (a list of tuples of device tensors in the order
+    the header lists for the op). Vector operations take n = their length,
+    scatter n = n_local, gather n = n_global; a gather set's fifth tensor is
+    the blockStarts plan (n_blocks + 1 entries) or None."""
     import torch
     if op not in BS_OP:
         raise ValueError(f"unknown op {op!r}")
-    need = {"copy": 2, "axpy": 2, "norm": 1, "dot": 2, "cg_update": 4, "scale": 3}[op]
+    slots = _BENCH_SLOTS[op]
     if not sets:
         raise ValueError("at least one pointer set is needed")
-    ptrs = (ctypes.c_void_p * (4 * len(sets)))()
+    ptrs = (ctypes.c_void_p * (BS_BENCH_SET * len(sets)))()
     for k, group in enumerate(sets):
-        if len(group) != need:
-            raise ValueError(f"{op} takes {need} tensors per set")
-        for j, t in enumerate(group):
-            ptrs[4 * k + j] = _dev_tensor(t, torch.float64, f"sets[{k}][{j}]")
-            if t.numel() < n:
+        group = tuple(group)
+        if op == "gather" and len(group) == 4:
+            group = group + (None,)
+        if len(group) != len(slots):
+            raise ValueError(f"{op} takes {len(slots)} tensors per set")
+        if op == "scatter":
+            if group[0].numel() < n or group[2].numel() < n:
+                raise ValueError("scatter: l2g and v_local need n_local entries")
+        elif op == "gather":
+            if group[0].numel() < n + 1 or group[3].numel() < n:
+                raise ValueError("gather: off needs n_global + 1 entries and v_global n_global")
+            if group[4] is not None and group[4].numel() < n_blocks + 1:
+                raise ValueError("gather: block_starts needs n_blocks + 1 entries")
+        for j, (t, kind) in enumerate(zip(group, slots)):
+            if t is None:
+                if not (op == "gather" and j == 4):
+                    raise ValueError(f"sets[{k}][{j}] is required")
+                continue
+            ptrs[BS_BENCH_SET * k + j] = _dev_tensor(t, torch.float64 if kind == "d" else torch.int32,
+                                                     f"sets[{k}][{j}]")
+            if op not in ("scatter", "gather") and t.numel() < n:
                 raise ValueError(f"sets[{k}][{j}] holds fewer than n elements")
-    dev = sets[0][0].device
+    first = sets[0][0]
     if op in ("norm", "dot", "cg_update"):
-        result = _scalar_out(result, sets[0][0])
-    ctx = _ctx_dev(sets[0][0], ctx)
+        result = _scalar_out(result, first)
+    ctx = _ctx_dev(first, ctx)
     sec = _dbl()
-    _check(_lib().bs_bench_loop(ctx.handle, BS_OP[op], int(n), float(alpha), float(beta), len(sets), ptrs,
-                                None if result is None else result.data_ptr(), int(reps), _stream(stream, dev),
-                                ctypes.byref(sec)), "bs_bench_loop")
+    _check(_lib().bs_bench_loop(ctx.handle, BS_OP[op], int(n), float(alpha), float(beta), int(n_blocks), len(sets),
+                                ptrs, None if result is None else result.data_ptr(), int(reps),
+                                _stream(stream, first.device), ctypes.byref(sec)), "bs_bench_loop")
     return sec.value
 
 
@@ -455,6 +478,6 @@ __all__ = [
     "BSError", "Context", "context", "LIB_PATH", "SIGNATURES",
     "bs_copy", "bs_axpy", "bs_norm", "bs_dot", "bs_cg_update", "bs_scatter", "bs_gather",
     "bs_gather_dot", "bs_cg_solve", "bs_scale", "bs_gll", "bs_mesh_box_mass",
-    "bs_bench_loop", "BS_OP",
+    "bs_bench_loop", "BS_OP", "BS_BENCH_SET",
     "bs_mesh_box_count", "bs_mesh_box_l2g", "bs_mesh_hex_l2g", "bs_validate_l2g", "bs_index_g2l", "bs_gather_plan",
 ]

@@ -262,26 +262,32 @@ int bs_gather_plan(int64_t n_global, const int32_t *off, int nodes_per_block,
  * performance model: the time of one test is measured on the host around
  * back-to-back launches, and fitted to T(B) = T0 + B / W_max, eq. 8). */
 typedef enum {
-    BS_OP_COPY = 0,      /* sets: x, y          */
-    BS_OP_AXPY = 1,      /* sets: x, y          */
-    BS_OP_NORM = 2,      /* sets: x             */
-    BS_OP_DOT = 3,       /* sets: x, y          */
-    BS_OP_CG_UPDATE = 4, /* sets: p, q, x, r    */
-    BS_OP_SCALE = 5      /* sets: x, d, y       */
+    BS_OP_COPY = 0,      /* n = length; set: x, y                              */
+    BS_OP_AXPY = 1,      /* n = length; set: x, y                              */
+    BS_OP_NORM = 2,      /* n = length; set: x                                 */
+    BS_OP_DOT = 3,       /* n = length; set: x, y                              */
+    BS_OP_CG_UPDATE = 4, /* n = length; set: p, q, x, r                        */
+    BS_OP_SCALE = 5,     /* n = length; set: x, d, y                           */
+    BS_OP_SCATTER = 6,   /* n = n_local; set: l2g, v_global, v_local           */
+    BS_OP_GATHER = 7     /* n = n_global; set: off, ids, v_local, v_global,
+                            block_starts (NULL: no plan; n_blocks its count)   */
 } bs_op;
+
+#define BS_BENCH_SET 6   /* pointers per set in bs_bench_loop */
 
 /* Synchronise `stream`, then issue `reps` calls of operation `op` (a bs_op)
  * back to back on it, call k using pointer set k mod n_sets, synchronise
  * again, and write the host seconds in between to *seconds. sets holds
- * n_sets groups of 4 device pointers (unused slots may be NULL), each group
- * laid out as listed above; alpha and beta are the scalars of AXPY and the
- * fused update; reductions write to the device double `result`. Each call
- * checks its arguments as the operation itself does; the first failing status
- * is returned after the stream is synchronised (*seconds is then not
- * written). BS_EINVAL: ctx, sets or seconds NULL, n < 0, n_sets < 1,
- * reps < 1, or an unknown op. */
-int bs_bench_loop(bs_ctx *ctx, int op, int64_t n, double alpha, double beta, int n_sets,
-                  void *const *sets, double *result, int reps, void *stream, double *seconds);
+ * n_sets groups of BS_BENCH_SET device pointers, each group laid out as
+ * listed above (unused slots NULL); alpha and beta are the scalars of AXPY
+ * and the fused update; reductions write to the device double `result`.
+ * Each call checks its arguments as the operation itself does; the first
+ * failing status is returned after the stream is synchronised (*seconds is
+ * then not written). BS_EINVAL: ctx, sets or seconds NULL, n < 0,
+ * n_sets < 1, reps < 1, or an unknown op. */
+int bs_bench_loop(bs_ctx *ctx, int op, int64_t n, double alpha, double beta, int64_t n_blocks,
+                  int n_sets, void *const *sets, double *result, int reps, void *stream,
+                  double *seconds);
 
 #ifdef __cplusplus
 }

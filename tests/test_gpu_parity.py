@@ -601,7 +601,26 @@ def test_bench_loop_runs_the_operations(env):
     bs.bs_bench_loop("axpy", n, [(xs[0], ys[0])], 1, alpha=0.37, beta=1.0)
     assert_bits(host(ys[0]), orc.axpy(0.37, host(xs[0]), 1.0, y0), "axpy via loop")
     with pytest.raises(bs.BSError):
-        bs._check(bs._lib().bs_bench_loop(bs.context().handle, 9, n, 1.0, 1.0, 1, None, None, 1, None,
+        bs._check(bs._lib().bs_bench_loop(bs.context().handle, 9, n, 1.0, 1.0, 0, 1, None, None, 1, None,
                                            None), "bad op")
     with pytest.raises(ValueError):
         bs.bs_bench_loop("dot", n + 1, [(xs[0], ys[0])], 1, out)
+
+
+def test_bench_loop_scatter_gather(env):
+    """Scatter and gather through bs_bench_loop write what the direct calls
+    write (both gather kernels), on the 8^3 order-3 box."""
+    bs, orc, torch, d = env
+    l2g, off, ids, ol2g, ng = mesh_case(env, "c1_box8_N3")
+    vgv = bs_inputs.uniform_pm1(751, ng)
+    vlv = bs_inputs.uniform_pm1(752, l2g.size)
+    vl = torch.empty(l2g.size, dtype=torch.float64, device=d)
+    bs.bs_bench_loop("scatter", l2g.size, [(dev(torch, d, l2g), dev(torch, d, vgv), vl)], 3)
+    assert_bits(host(vl), orc.scatter(ol2g, vgv), "scatter via loop")
+    plan = bs.bs_gather_plan(off, 1024)
+    want = orc.gather(ol2g, vlv, ng)
+    for p in (None, dev(torch, d, plan)):
+        vg = torch.full((ng,), np.nan, dtype=torch.float64, device=d)
+        bs.bs_bench_loop("gather", ng, [(dev(torch, d, off), dev(torch, d, ids), dev(torch, d, vlv), vg, p)], 2,
+                         n_blocks=0 if p is None else plan.size - 1)
+        assert_bits(host(vg), want, "gather via loop")
