@@ -295,3 +295,60 @@ def test_hex_l2g_errors(bs):
     assert e.value.status == bs.BS_ERANGE
     l2g, ng = bs.bs_mesh_hex_l2g(np.zeros((0, 8), np.int32), 3, 0)
     assert l2g.size == 0 and ng == 0
+
+
+# ------------------------------------------------ property-based tables ----
+
+from hypothesis import given, settings, strategies as st  # noqa: E402
+
+
+@settings(max_examples=60, deadline=None, derandomize=True)
+@given(st.integers(0, 400), st.integers(1, 60), st.integers(0, 2 ** 32 - 1), st.integers(0, 4))
+def test_g2l_property(bs, orc, n_local, n_global, seed, mask_mod):
+    """Any I_l->g (random ids, optional masks): the library's counting-sort
+    CSR equals the oracle's sort-based one."""
+    ids = (bs_inputs.splitmix64(seed, n_local) % np.uint64(n_global)).astype(np.int32)
+    if mask_mod:
+        ids[bs_inputs.splitmix64(seed + 1, n_local) % np.uint64(mask_mod + 1) == 0] = -1
+    off, got = bs.bs_index_g2l(ids, n_global)
+    ooff, oids = orc.g2l(ids, n_global)
+    assert np.array_equal(off, ooff) and np.array_equal(got, oids)
+
+
+@settings(max_examples=60, deadline=None, derandomize=True)
+@given(st.lists(st.integers(0, 40), min_size=0, max_size=300), st.integers(1, 1024))
+def test_gather_plan_property(bs, rows, npb):
+    """blockStarts of any row-length profile: covers every row once, in
+    order, each block within both caps unless it is a single row, and greedy
+    (the next row would have broken a cap)."""
+    off = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+    plan = bs.bs_gather_plan(off, npb)
+    ng = len(rows)
+    assert plan[0] == 0 and plan[-1] == ng
+    if ng == 0:
+        assert list(plan) == [0]
+        return
+    assert np.all(np.diff(plan) >= 1)
+    for a, b in zip(plan[:-1], plan[1:]):
+        ent, nr = off[b] - off[a], b - a
+        assert nr == 1 or (ent <= npb and nr <= npb)
+        if b < ng:
+            assert nr + 1 > npb or off[b + 1] - off[a] > npb
+
+
+@settings(max_examples=25, deadline=None, derandomize=True)
+@given(st.integers(1, 4), st.integers(1, 4), st.integers(1, 3), st.integers(1, 6), st.integers(0, 2 ** 32 - 1),
+       st.booleans())
+def test_hex_l2g_property(bs, orc, nx, ny, nz, N, seed, shuffle):
+    """Random box dimensions and orders, every element in a random cube
+    orientation, vertices renamed, elements optionally shuffled: library
+    table == oracle table, and its node count is the lattice count."""
+    ev, nv = bs_inputs.hex_box(nx, ny, nz)
+    ev, _ = bs_inputs.hex_orient(ev, seed)
+    ev, nv = bs_inputs.hex_relabel(ev, nv, seed + 1, spare=seed % 5)
+    if shuffle:
+        ev = ev[bs_inputs.permutation(seed + 2, len(ev))]
+    l2g, ng = bs.bs_mesh_hex_l2g(ev, N, nv)
+    ol2g, ong = orc.mesh_hex(ev, N, nv)
+    assert ng == ong == (nx * N + 1) * (ny * N + 1) * (nz * N + 1)
+    assert np.array_equal(l2g, ol2g)

@@ -624,3 +624,91 @@ def test_bench_loop_scatter_gather(env):
         bs.bs_bench_loop("gather", ng, [(dev(torch, d, off), dev(torch, d, ids), dev(torch, d, vlv), vg, p)], 2,
                          n_blocks=0 if p is None else plan.size - 1)
         assert_bits(host(vg), want, "gather via loop")
+
+
+# ------------------------------------------------- seeded random cases -----
+
+def _draw(seed, k, lo, hi):
+    """k integers in [lo, hi] from the seeded stream (inputs only)."""
+    return [int(v) for v in (bs_inputs.splitmix64(seed, k) % np.uint64(hi - lo + 1)).astype(np.int64) + lo]
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_vector_ops(env, case):
+    """Lengths log-uniform in [1, 4M] and random 8-byte phases per operand."""
+    w = _draw(900 + case, 6, 0, 2 ** 31)
+    n = max(1, int(2 ** (22 * (w[0] / 2 ** 31))))
+    offset = tuple(v % 2 for v in w[1:5])
+    run_vector_ops(env, n, 1000 + case, offset)
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_random_meshes(env, case):
+    """Random box dimensions and orders, optional element and node
+    permutations, optional Dirichlet masks, random blockStarts capacities:
+    scatter, both gathers and the folded dot against the oracle."""
+    bs, orc, torch, d = env
+    ex, ey, ez, N, shuffle, masked, npb = _draw(950 + case, 7, 1, 1 << 30)
+    ex, ey, ez = 1 + ex % 7, 1 + ey % 6, 1 + ez % 5
+    N = 1 + N % 9
+    G = (ex * N + 1) * (ey * N + 1) * (ez * N + 1)
+    ep = bs_inputs.permutation(960 + case, ex * ey * ez) if shuffle % 2 else None
+    npm = bs_inputs.permutation(970 + case, G) if shuffle % 3 == 0 else None
+    l2g = bs.bs_mesh_box_l2g(ex, ey, ez, N, ep, npm).copy()
+    ol2g, ng = orc.mesh_box(ex, ey, ez, N, ep, npm)
+    assert np.array_equal(l2g, ol2g) and ng == G
+    if masked % 2:
+        m = bs_inputs.splitmix64(980 + case, l2g.size) % np.uint64(7) == 0
+        l2g[m] = -1
+        ol2g = ol2g.copy()
+        ol2g[m] = -1
+    off, ids = bs.bs_index_g2l(l2g, ng)
+    vgv = bs_inputs.uniform_pm1(990 + case, ng)
+    vlv = bs_inputs.uniform_pm1(995 + case, l2g.size)
+    wv = bs_inputs.uniform_pm1(999 + case, ng)
+    vl = torch.full((l2g.size,), np.nan, dtype=torch.float64, device=d)
+    bs.bs_scatter(dev(torch, d, l2g), dev(torch, d, vgv), vl)
+    assert_bits(host(vl), orc.scatter(ol2g, vgv), f"scatter case {case}")
+    want = orc.gather(ol2g, vlv, ng)
+    doff, dids, dvl, dw = dev(torch, d, off), dev(torch, d, ids), dev(torch, d, vlv), dev(torch, d, wv)
+    for cap in (None, 1 + npb % 1024, 1024):
+        plan = None if cap is None else dev(torch, d, bs.bs_gather_plan(off, cap))
+        vg = torch.full((ng,), np.nan, dtype=torch.float64, device=d)
+        bs.bs_gather(doff, dids, dvl, vg, plan)
+        assert_bits(host(vg), want, f"gather case {case} cap {cap}")
+        vg.fill_(np.nan)
+        got = bs.bs_gather_dot(doff, dids, dvl, vg, dw, plan).item()
+        assert_bits(host(vg), want, f"gather_dot values case {case} cap {cap}")
+        assert_rel(got, orc.dot(want, wv), f"gather_dot case {case} cap {cap}")
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_random_unstructured(env, case):
+    """Tet-split and periodic meshes with random orientation, vertex names and
+    element order at random orders: the library's table runs the kernels, the
+    oracle's table the reference, and the two tables must be equal."""
+    bs, orc, torch, d = env
+    a, b, c, N, kind = _draw(1100 + case, 5, 1, 1 << 30)
+    N = 1 + N % 8
+    if kind % 2:
+        ev, nv, _ = bs_inputs.hex_tet_split(1 + a % 3, 1 + b % 3, 1 + c % 2)
+    else:
+        ev, nv = bs_inputs.hex_box(3 + a % 3, 3 + b % 3, 3 + c % 3, periodic=(True, kind % 3 == 0, True))
+    ev, _ = bs_inputs.hex_orient(ev, 1110 + case)
+    ev, nv = bs_inputs.hex_relabel(ev, nv, 1120 + case, spare=case)
+    ev = ev[bs_inputs.permutation(1130 + case, len(ev))]
+    l2g, ng = bs.bs_mesh_hex_l2g(ev, N, nv)
+    ol2g, ong = orc.mesh_hex(ev, N, nv)
+    assert ng == ong and np.array_equal(l2g, ol2g)
+    off, ids = bs.bs_index_g2l(l2g, ng)
+    vgv = bs_inputs.uniform_pm1(1140 + case, ng)
+    vlv = bs_inputs.uniform_pm1(1150 + case, l2g.size)
+    vl = torch.empty(l2g.size, dtype=torch.float64, device=d)
+    bs.bs_scatter(dev(torch, d, l2g), dev(torch, d, vgv), vl)
+    assert_bits(host(vl), orc.scatter(ol2g, vgv), f"scatter unstructured {case}")
+    want = orc.gather(ol2g, vlv, ng)
+    for plan in (None, bs.bs_gather_plan(off, 1024)):
+        vg = torch.full((ng,), np.nan, dtype=torch.float64, device=d)
+        bs.bs_gather(dev(torch, d, off), dev(torch, d, ids), dev(torch, d, vlv), vg,
+                     None if plan is None else dev(torch, d, plan))
+        assert_bits(host(vg), want, f"gather unstructured {case}")
