@@ -19,8 +19,12 @@
 //    word, 32 pairs per lane in flight;
 //  - gather: the balanced blockStarts scheme of the paper, each block staging
 //    at most 1024 CSR entries of v_L in LDS with coalesced index loads, then
-//    one lane per global node summing its entries from LDS in ascending order;
-//    without a plan, one lane per node with all of its loads issued up front.
+//    one lane per global node summing its entries from LDS in ascending order,
+//    plan blocks handed to the XCDs in runs of four; without a plan, one lane
+//    per node with all of its loads issued up front.
+// Built from the same kernels: the pointwise scale y = x / d of the lumped
+// mass, and a device-resident CG iteration on Z^T Z whose scalars (alpha,
+// beta, |r|^2, a done flag) stay in device memory between launches.
 // No MFMA: nothing here is a dense contraction.
 //
 // Bit-exactness: the file is compiled with -ffp-contract=off and the pragma
@@ -115,13 +119,15 @@ __device__ __forceinline__ double block_sum(double v)
 }
 
 // Second stage of every reduction: one block sums the nb per-block partials
-// in a fixed order (each lane a strided run, then the block tree) and writes
-// the result, or its square root. nb == 0 stores +0.0. The kernel boundary
-// between the two stages makes the partials visible across XCDs; a
-// single-kernel "last block" finish would need an agent-scope release per
-// block, which on this multi-XCD part writes back and invalidates L2 for
-// every block and measured several times slower than the second launch.
-// Sum of the partials over one kFinishBlock-thread block, valid in thread 0:
+// in a fixed order and writes the result, or its square root; nb == 0 stores
+// +0.0. The kernel boundary between the two stages makes the partials
+// visible across XCDs. A single-kernel "last block" finish needs either an
+// agent-scope release per block, which on this multi-XCD part writes back
+// that XCD's L2 (about 10 us per call at 256-512 blocks), or scratch in
+// uncached memory with tickets, which was correct but no faster than the
+// second launch at 11M elements.
+//
+// finish_sum: the sum over one kFinishBlock-thread block, valid in thread 0:
 // each lane a strided run in index order, then the wave butterfly, then the
 // 16 wave sums in order.
 __device__ __forceinline__ double finish_sum(const double *__restrict__ partials, int nb)
@@ -152,8 +158,8 @@ __global__ __launch_bounds__(kFinishBlock) void k_finish(const double *__restric
 //  kStart: rr = r.r; history[0] = rr; convergence threshold tol2 * rr; the
 //          history entries after 0 are set to -1 (an iteration that runs
 //          overwrites its entry).
-//  kAlpha: alpha = rr / (p.q).
-//  kBeta:  rr' = r'.r'; beta = rr' / rr; rr = rr'; history[k+1] = rr';
+//  kSetAlpha: alpha = rr / (p.q).
+//  kSetBeta:  rr' = r'.r'; beta = rr' / rr; rr = rr'; history[k+1] = rr';
 //          converged when rr' <= threshold (or rr' == 0).
 enum CgFinish { kStart = 0, kSetAlpha = 1, kSetBeta = 2 };
 

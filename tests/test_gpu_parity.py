@@ -712,3 +712,28 @@ def test_random_unstructured(env, case):
         bs.bs_gather(dev(torch, d, off), dev(torch, d, ids), dev(torch, d, vlv), vg,
                      None if plan is None else dev(torch, d, plan))
         assert_bits(host(vg), want, f"gather unstructured {case}")
+
+
+def test_contexts_on_concurrent_streams(env):
+    """One context per stream: reductions issued alternately on two streams
+    (default priority) with their own contexts keep their own partials, and
+    each result matches the oracle."""
+    bs, orc, torch, d = env
+    n = 3_000_001
+    xs = [bs_inputs.uniform_pm1(761 + k, n) for k in range(2)]
+    X = [dev(torch, d, x) for x in xs]
+    ctxs = [bs.Context(0), bs.Context(0)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.zeros(8, dtype=torch.float64, device=d) for _ in range(2)]
+    torch.cuda.synchronize()
+    for rep in range(8):
+        for k in range(2):
+            bs.bs_norm(X[k], outs[k][rep:rep + 1], ctx=ctxs[k], stream=streams[k])
+    torch.cuda.synchronize()
+    for k in range(2):
+        want = orc.norm(xs[k])
+        got = host(outs[k])
+        assert np.all(got == got[0])
+        assert_rel(got[0], want, f"stream {k}")
+    for c in ctxs:
+        c.close()
