@@ -168,9 +168,30 @@ def hex_orient(ev: np.ndarray, seed: int):
     ev2[e, c] = ev[e, sigma_sym[e][c]]."""
     E = ev.shape[0]
     sym = (splitmix64(seed, E) % np.uint64(48)).astype(np.int64)
+    return reorder_corners(ev, sym).astype(np.int32), sym
+
+
+def reorder_corners(a: np.ndarray, sym: np.ndarray) -> np.ndarray:
+    """a[e, c, ...] -> a[e, sigma_sym[e][c], ...] (corner data of elements, such
+    as vertex ids or corner coordinates, in the orientation hex_orient chose)."""
     table = np.array([cube_symmetry(s)[2] for s in range(48)], dtype=np.int64)
-    ev2 = np.take_along_axis(ev, table[sym], axis=1).astype(np.int32)
-    return ev2, sym
+    idx = table[np.asarray(sym)]
+    return a[np.arange(a.shape[0])[:, None], idx]
+
+
+def hex_box_coords(nx: int, ny: int, nz: int) -> np.ndarray:
+    """Corner coordinates float64[E, 8, 3] of the unit cubes of hex_box (the
+    lattice point of each corner, not wrapped, so periodic boxes get their
+    true element shapes)."""
+    xe = np.empty((nx * ny * nz, 8, 3))
+    e = 0
+    for cz in range(nz):
+        for cy in range(ny):
+            for cx in range(nx):
+                for c in range(8):
+                    xe[e, c] = (cx + (c & 1), cy + ((c >> 1) & 1), cz + ((c >> 2) & 1))
+                e += 1
+    return xe
 
 
 def hex_relabel(ev: np.ndarray, n_vert: int, seed: int, spare: int = 0):

@@ -81,6 +81,8 @@ def lib():
         L.or_scale.argtypes = [_c_int64, _ptr, _ptr, _ptr]
         L.or_mesh_hex.argtypes = [_c_int64, ctypes.c_int, _c_int64, _ptr, _ptr]
         L.or_mesh_hex.restype = _c_int64
+        L.or_mesh_hex_mass.argtypes = [_c_int64, ctypes.c_int, _ptr, _ptr]
+        L.or_mesh_hex_mass.restype = ctypes.c_int
         L.or_scale.restype = None
         _lib = L
     return _lib
@@ -272,3 +274,14 @@ def mesh_hex(ev, p, n_vert=None):
     if ng < 0:
         raise ValueError("bad hex mesh")
     return l2g, int(ng)
+
+
+def mesh_hex_mass(xe, p):
+    """Local lumped-mass weights w_i w_j w_k |det J| of hexahedra given by
+    their corner coordinates xe (float64[E, 8, 3], corner c = a + 2b + 4d)."""
+    xe = np.ascontiguousarray(xe, dtype=np.float64).reshape(-1, 8, 3)
+    E = xe.shape[0]
+    w = np.empty(E * (p + 1) ** 3, dtype=np.float64)
+    if lib().or_mesh_hex_mass(E, p, xe.ctypes.data, w.ctypes.data) != 0:
+        raise ValueError("bad arguments")
+    return w

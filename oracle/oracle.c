@@ -25,6 +25,7 @@
  *   or_gll_weights, or_mesh_box_mass, or_scale   lumped mass and the 1/m scaling
  *                 (arXiv 1506.05996, coarse-grid correction)
  *   or_mesh_hex   I_l->g of an unstructured hex mesh given by corner vertices
+ *   or_mesh_hex_mass   lumped-mass weights of an unstructured hex mesh (arXiv 1506.05996)
  *                 (unstructured mesh of the CEED formulation section; arXiv 1506.05996, local-to-global table)
  *
  * The reductions (dot, norm, the residual norm of the fused update) are
@@ -518,4 +519,49 @@ int64_t or_mesh_hex(int64_t n_elem, int p, int64_t n_vert, const int32_t *ev, in
 fail:
     free(cls); free(order); free(sig);
     return -1;
+}
+
+/* Local lumped-mass weights of an unstructured hex mesh: node (i,j,k) of
+ * element e carries w_i w_j w_k |det J(r_i, r_j, r_k)|, J the Jacobian of the
+ * element's trilinear map x(xi) = sum_c phi_c(xi) X_c ("GPU accelerated
+ * spectral finite elements on all-hex meshes": the geometry of each element
+ * is its own map, and the lumped mass takes the quadrature weights times the
+ * Jacobian at the nodes). xe[24 e + 3 c + a] is coordinate a of corner
+ * c = a + 2b + 4d of element e (the corner order of or_mesh_hex).
+ * phi_c is the product over the axes of (1 - t)/2 (bit 0) or (1 + t)/2
+ * (bit 1), so dphi_c/dxi_a is that product with axis a's factor replaced by
+ * -1/2 or +1/2. Returns 0, or -1 if p < 1, n_elem < 0 or no memory. */
+int or_mesh_hex_mass(int64_t n_elem, int p, const double *xe, double *w_local)
+{
+    if (n_elem < 0 || p < 1) return -1;
+    const int64_t nq = p + 1, Np = nq * nq * nq;
+    double *r = (double *)malloc((size_t)nq * sizeof(double));
+    double *w = (double *)malloc((size_t)nq * sizeof(double));
+    if (!r || !w) { free(r); free(w); return -1; }
+    or_gll_nodes(p, r);
+    or_gll_weights(p, w);
+    for (int64_t e = 0; e < n_elem; ++e)
+        for (int64_t k = 0; k < nq; ++k)
+            for (int64_t j = 0; j < nq; ++j)
+                for (int64_t i = 0; i < nq; ++i) {
+                    const double t[3] = {r[i], r[j], r[k]};
+                    double J[3][3] = {{0}};   /* J[row = x,y,z][col = d/dxi_a] */
+                    for (int c = 0; c < 8; ++c)
+                        for (int a = 0; a < 3; ++a) {
+                            double d = 1.0;
+                            for (int b = 0; b < 3; ++b) {
+                                const int bit = (c >> b) & 1;
+                                if (b == a) d *= bit ? 0.5 : -0.5;
+                                else d *= bit ? (1.0 + t[b]) / 2.0 : (1.0 - t[b]) / 2.0;
+                            }
+                            for (int x = 0; x < 3; ++x) J[x][a] += d * xe[24 * e + 3 * c + x];
+                        }
+                    const double det = J[0][0] * (J[1][1] * J[2][2] - J[1][2] * J[2][1])
+                                     - J[0][1] * (J[1][0] * J[2][2] - J[1][2] * J[2][0])
+                                     + J[0][2] * (J[1][0] * J[2][1] - J[1][1] * J[2][0]);
+                    w_local[e * Np + i + nq * (j + nq * k)] = w[i] * w[j] * w[k] * fabs(det);
+                }
+    free(r);
+    free(w);
+    return 0;
 }

@@ -53,6 +53,13 @@ MUTANTS = [
     ("hex_vertices_in_corner_order", "y > 0 && s[2 * y] < s[2 * (y - 1)]", "y > 0 && 0", "hex"),
     ("hex_numbered_by_signature", "if (first[cls[L]] < 0) first[cls[L]] = NG++;",
      "if (first[cls[L]] < 0) first[cls[L]] = NG++;\n        first[cls[L]] = cls[L];", "hex"),
+    ("hexmass_factors_mirrored", "else d *= bit ? (1.0 + t[b]) / 2.0 : (1.0 - t[b]) / 2.0;",
+     "else d *= bit ? (1.0 - t[b]) / 2.0 : (1.0 + t[b]) / 2.0;", "hexmass"),
+    ("hexmass_signed_det", "w[i] * w[j] * w[k] * fabs(det);", "w[i] * w[j] * w[k] * det;", "hexmass"),
+    ("hexmass_derivative_scale", "if (b == a) d *= bit ? 0.5 : -0.5;", "if (b == a) d *= bit ? 1.0 : -1.0;",
+     "hexmass"),
+    ("hexmass_cofactor_sign", "- J[0][1] * (J[1][0] * J[2][2] - J[1][2] * J[2][0])",
+     "+ J[0][1] * (J[1][0] * J[2][2] - J[1][2] * J[2][0])", "hexmass"),
 ]
 
 

@@ -640,3 +640,75 @@ def test_hex_rejects_bad_elements(orc):
         orc.mesh_hex(ev, 2, int(ev.max()))
     l2g, ng = orc.mesh_hex(np.zeros((0, 8), np.int32), 3, 0)
     assert l2g.size == 0 and ng == 0
+
+
+# ------------------------------------------- unstructured lumped mass ------
+
+def gll_rule(N):
+    """GLL points and weights from numpy's Legendre class (independent of the
+    oracle): -1, the roots of P_N', +1; w = 2 / (N (N+1) P_N(r)^2)."""
+    r = gll_points(N)
+    P = np.polynomial.legendre.Legendre.basis(N)(r)
+    return r, 2.0 / (N * (N + 1) * P * P)
+
+
+@pytest.mark.parametrize("N", [1, 3, 7])
+def test_hexmass_unit_box(orc, N):
+    xe = bs_inputs.hex_box_coords(3, 2, 2)
+    w = orc.mesh_hex_mass(xe, N)
+    assert np.allclose(w, orc.mesh_box_mass(3, 2, 2, N), rtol=1e-14, atol=0)
+
+
+@pytest.mark.parametrize("N", [1, 2, 5])
+def test_hexmass_affine_elements(orc, N):
+    """An affine image A x + b of the unit cubes has the constant Jacobian
+    det A / 8 on the reference cube: every weight is w_i w_j w_k |det A| / 8
+    and every element holds |det A|."""
+    A = np.array([[1.3, 0.2, -0.1], [0.05, 0.9, 0.3], [-0.2, 0.1, 1.1]])
+    xe = bs_inputs.hex_box_coords(2, 2, 1) @ A.T + np.array([0.5, -1.0, 2.0])
+    w = orc.mesh_hex_mass(xe, N).reshape(4, -1)
+    r, g = gll_rule(N)
+    want = (g[None, None, :] * g[None, :, None] * g[:, None, None]).ravel() * abs(np.linalg.det(A)) / 8
+    for e in range(4):
+        assert np.allclose(w[e], want, rtol=1e-13, atol=0)
+        assert w[e].sum() == pytest.approx(abs(np.linalg.det(A)), rel=1e-13)
+
+
+@pytest.mark.parametrize("N", [2, 4, 6])
+def test_hexmass_trilinear_frustum(orc, N):
+    """Bottom face the unit square, top face [0, s]^2 at height 1: with
+    u, v, w = (1 + xi)/2 ... the map is x = u h, y = v h, z = w, h = 1 + (s-1) w,
+    so det J = h^2 / 8 pointwise and the volume (1 + s + s^2) / 3, which GLL
+    integrates exactly from N = 2 (degree 2 in w)."""
+    s = 1.7
+    xe = np.array([[[0, 0, 0], [1, 0, 0], [0, 1, 0], [1, 1, 0],
+                    [0, 0, 1], [s, 0, 1], [0, s, 1], [s, s, 1]]], dtype=np.float64)
+    w = orc.mesh_hex_mass(xe, N)
+    r, g = gll_rule(N)
+    h = 1 + (s - 1) * (1 + r) / 2
+    want = (g[:, None, None] * h[:, None, None] ** 2 * g[None, :, None] * g[None, None, :]).ravel() / 8
+    assert np.allclose(w, want, rtol=1e-13, atol=0)
+    assert w.sum() == pytest.approx((1 + s + s * s) / 3, rel=1e-13)
+
+
+@pytest.mark.parametrize("N", [2, 5])
+def test_hexmass_tet_split_volumes(orc, N):
+    """Each of the four hexahedra of a tetrahedron is its barycentric quarter:
+    in a unit cube's Kuhn split every hexahedron has volume 1/24, and their
+    Jacobians are of degree 2 per variable, so GLL from N = 2 is exact."""
+    ev, nv, X = bs_inputs.hex_tet_split(2, 1, 2)
+    w = orc.mesh_hex_mass(X[ev], N).reshape(len(ev), -1)
+    assert np.allclose(w.sum(axis=1), 1.0 / 24, rtol=1e-13, atol=0)
+    assert np.all(w > 0)
+
+
+def test_hexmass_orientation(orc):
+    """Any of the 48 corner orders (reflections give det J < 0) renames the
+    element's nodes and leaves the weight of each physical node alone."""
+    N = 4
+    ev, nv, X = bs_inputs.hex_tet_split(1, 1, 1)
+    xe = X[ev]
+    sym = (bs_inputs.splitmix64(601, len(ev)) % np.uint64(48)).astype(np.int64)
+    w0 = orc.mesh_hex_mass(xe, N)
+    w1 = orc.mesh_hex_mass(bs_inputs.reorder_corners(xe, sym), N)
+    assert np.allclose(unrotate(w1, sym, N), w0, rtol=1e-14, atol=0)
