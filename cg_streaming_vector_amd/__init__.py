@@ -68,6 +68,7 @@ SIGNATURES = {
     "bs_mesh_box_count": ([_int, _int, _int, _int, ctypes.POINTER(_i64), ctypes.POINTER(_i64)], _int),
     "bs_mesh_box_l2g": ([_int, _int, _int, _int, _ptr, _ptr, _ptr], _int),
     "bs_mesh_hex_l2g": ([_i64, _int, _i64, _ptr, _ptr, ctypes.POINTER(_i64)], _int),
+    "bs_mesh_hex_mass": ([_i64, _int, _ptr, _ptr], _int),
     "bs_validate_l2g": ([_i64, _i64, _ptr], _int),
     "bs_index_g2l": ([_i64, _i64, _ptr, _ptr, _ptr], _int),
     "bs_gather_plan": ([_i64, _ptr, _int, _ptr, ctypes.POINTER(_i64)], _int),
@@ -394,6 +395,19 @@ def bs_mesh_hex_l2g(ev, order, n_vertices=None):
     return l2g, ng.value
 
 
+def bs_mesh_hex_mass(xe, order):
+    """Local lumped-mass weights (float64[n_elements (order+1)^3]) of hexahedra
+    given by their corner coordinates xe (float64[n_elements, 8, 3])."""
+    xe = np.ascontiguousarray(xe)
+    if xe.dtype != np.float64 or xe.size % 24:
+        raise TypeError("xe must be float64 with 8 x 3 coordinates per element")
+    E = xe.size // 24
+    nl = E * (int(order) + 1) ** 3
+    w = np.empty(nl if 0 <= nl <= 2 ** 31 - 1 else 1, dtype=np.float64)
+    _check(_lib().bs_mesh_hex_mass(E, int(order), xe.ctypes.data, w.ctypes.data), "bs_mesh_hex_mass")
+    return w
+
+
 def bs_validate_l2g(l2g, n_global):
     l2g = _host_i32(l2g, "l2g")
     _check(_lib().bs_validate_l2g(l2g.size, int(n_global), l2g.ctypes.data), "bs_validate_l2g")
@@ -479,5 +493,5 @@ __all__ = [
     "bs_copy", "bs_axpy", "bs_norm", "bs_dot", "bs_cg_update", "bs_scatter", "bs_gather",
     "bs_gather_dot", "bs_cg_solve", "bs_scale", "bs_gll", "bs_mesh_box_mass",
     "bs_bench_loop", "BS_OP", "BS_BENCH_SET",
-    "bs_mesh_box_count", "bs_mesh_box_l2g", "bs_mesh_hex_l2g", "bs_validate_l2g", "bs_index_g2l", "bs_gather_plan",
+    "bs_mesh_box_count", "bs_mesh_box_l2g", "bs_mesh_hex_l2g", "bs_mesh_hex_mass", "bs_validate_l2g", "bs_index_g2l", "bs_gather_plan",
 ]

@@ -337,6 +337,72 @@ int bs_mesh_box_mass(int ex, int ey, int ez, int order, double *w_local)
     return BS_OK;
 }
 
+int bs_mesh_hex_mass(int64_t n_elements, int order, const double *xe, double *w_local)
+{
+    if (n_elements < 0 || order < 1 || (n_elements > 0 && (!xe || !w_local))) return BS_EINVAL;
+    const int64_t nq = order + 1;
+    if (nq > 2048) return BS_ERANGE;
+    const int64_t Np = nq * nq * nq;
+    if (n_elements > INT32_MAX / Np) return BS_ERANGE;
+    std::vector<double> r, w, h0, h1;
+    try {
+        r.resize(nq);
+        w.resize(nq);
+        h0.resize(nq);
+        h1.resize(nq);
+    } catch (const std::bad_alloc &) {
+        return BS_ENOMEM;
+    }
+    bs_gll(order, r.data(), w.data());
+    // the two linear blending functions of one axis at the GLL points
+    for (int64_t t = 0; t < nq; ++t) {
+        h0[t] = (1.0 - r[t]) / 2.0;
+        h1[t] = (1.0 + r[t]) / 2.0;
+    }
+    for (int64_t e = 0; e < n_elements; ++e) {
+        const double *X = xe + 24 * e;  // X[3 c + a], corner c = a + 2b + 4d
+        // edge vectors along each reference axis: for axis a, the four edges
+        // from corner c (bit a clear) to c + 2^a, halved (d/dxi of a linear
+        // blend over [-1, 1])
+        double edge[3][4][3];
+        for (int a = 0; a < 3; ++a) {
+            int m = 0;
+            for (int c = 0; c < 8; ++c) {
+                if ((c >> a) & 1) continue;
+                for (int x = 0; x < 3; ++x) edge[a][m][x] = (X[3 * (c | 1 << a) + x] - X[3 * c + x]) / 2.0;
+                ++m;
+            }
+        }
+        int sign = 0;
+        for (int64_t k = 0; k < nq; ++k)
+            for (int64_t j = 0; j < nq; ++j)
+                for (int64_t i = 0; i < nq; ++i) {
+                    const int64_t idx[3] = {i, j, k};
+                    double col[3][3];
+                    for (int a = 0; a < 3; ++a) {
+                        // bilinear blend of axis a's four edges over the other
+                        // two axes (edges listed with the lower axis fastest)
+                        const int b0 = a == 0 ? 1 : 0, b1 = a == 2 ? 1 : 2;
+                        const double u0 = h0[idx[b0]], u1 = h1[idx[b0]];
+                        const double v0 = h0[idx[b1]], v1 = h1[idx[b1]];
+                        for (int x = 0; x < 3; ++x)
+                            col[a][x] = (u0 * v0) * edge[a][0][x] + (u1 * v0) * edge[a][1][x] +
+                                        (u0 * v1) * edge[a][2][x] + (u1 * v1) * edge[a][3][x];
+                    }
+                    // det J = col0 . (col1 x col2)
+                    const double cx = col[1][1] * col[2][2] - col[1][2] * col[2][1];
+                    const double cy = col[1][2] * col[2][0] - col[1][0] * col[2][2];
+                    const double cz = col[1][0] * col[2][1] - col[1][1] * col[2][0];
+                    const double det = col[0][0] * cx + col[0][1] * cy + col[0][2] * cz;
+                    const int sg = det > 0.0 ? 1 : det < 0.0 ? -1 : 0;
+                    if (sg == 0 || (sign != 0 && sg != sign)) return BS_EINVAL;
+                    sign = sg;
+                    w_local[e * Np + i + nq * (j + nq * k)] = w[i] * w[j] * w[k] * std::fabs(det);
+                }
+    }
+    return BS_OK;
+}
+
 int bs_validate_l2g(int64_t n_local, int64_t n_global, const int32_t *l2g)
 {
     if (n_local < 0 || n_global < 0 || (n_local > 0 && !l2g)) return BS_EINVAL;

@@ -232,6 +232,22 @@ int bs_gll(int order, double *nodes, double *weights);
  * for a NULL output, BS_ENOMEM without host memory for one element's block. */
 int bs_mesh_box_mass(int ex, int ey, int ez, int order, double *w_local);
 
+/* Local lumped-mass weights of an unstructured hex mesh (arXiv 1506.05996,
+ * the element geometry as a map from the reference cube and the lumped mass
+ * as quadrature weights times the Jacobian at the nodes): node (i,j,k) of
+ * element e gets w_i w_j w_k |det J(r_i, r_j, r_k)| with J the Jacobian of
+ * the element's trilinear map. The lumped global mass is their gather.
+ *   xe        double[n_elements * 24], host: xe[24e + 3c + a] is coordinate a
+ *             of corner c = a + 2b + 4d of element e (the corner order of
+ *             bs_mesh_hex_l2g).
+ *   w_local   double[n_elements * (order+1)^3], host, written in the local
+ *             layout of bs_mesh_hex_l2g.
+ * BS_EINVAL: bad sizes or NULL, or an element whose Jacobian vanishes or
+ * changes sign at one of its nodes (a degenerate or tangled element; w_local
+ * may then be partly written). BS_ERANGE as bs_mesh_hex_l2g. BS_ENOMEM: no
+ * host memory. */
+int bs_mesh_hex_mass(int64_t n_elements, int order, const double *xe, double *w_local);
+
 /* Check that every id is < n_global (negative ids are masks): BS_OK or
  * BS_EINVAL. */
 int bs_validate_l2g(int64_t n_local, int64_t n_global, const int32_t *l2g);

@@ -352,3 +352,39 @@ def test_hex_l2g_property(bs, orc, nx, ny, nz, N, seed, shuffle):
     ol2g, ong = orc.mesh_hex(ev, N, nv)
     assert ng == ong == (nx * N + 1) * (ny * N + 1) * (nz * N + 1)
     assert np.array_equal(l2g, ol2g)
+
+
+@pytest.mark.parametrize("N", [1, 2, 4, 7])
+def test_hex_mass_matches_oracle(bs, orc, N):
+    """The library's weights (edge-vector Jacobian, scalar triple product) and
+    the oracle's (shape-function derivatives, cofactor determinant) agree to
+    rounding on oriented tet-split elements, affine boxes and a frustum."""
+    ev, nv, X = bs_inputs.hex_tet_split(2, 1, 1)
+    xe = bs_inputs.reorder_corners(X[ev], (bs_inputs.splitmix64(611, len(ev)) % np.uint64(48)).astype(np.int64))
+    A = np.array([[1.1, 0.3, 0.0], [-0.2, 0.8, 0.1], [0.0, 0.4, 1.2]])
+    boxes = bs_inputs.hex_box_coords(2, 2, 2) @ A.T
+    s = 0.6
+    frustum = np.array([[[0, 0, 0], [1, 0, 0], [0, 1, 0], [1, 1, 0],
+                         [0, 0, 1], [s, 0, 1], [0, s, 1], [s, s, 1]]], dtype=np.float64)
+    for geom in (xe, boxes, frustum):
+        got = bs.bs_mesh_hex_mass(geom, N)
+        want = orc.mesh_hex_mass(geom, N)
+        assert np.allclose(got, want, rtol=1e-13, atol=0)
+
+
+def test_hex_mass_errors(bs):
+    xe = bs_inputs.hex_box_coords(1, 1, 1)
+    with pytest.raises(bs.BSError):
+        bs.bs_mesh_hex_mass(xe, 0)
+    flat = xe.copy()
+    flat[0, 4:, 2] = 0.0  # top face on the bottom face: det J = 0
+    with pytest.raises(bs.BSError) as e:
+        bs.bs_mesh_hex_mass(flat, 3)
+    assert e.value.status == bs.BS_EINVAL
+    tangled = xe.copy()
+    tangled[0, 7] = (-1.0, -1.0, -1.0)  # far corner pulled through the element
+    with pytest.raises(bs.BSError):
+        bs.bs_mesh_hex_mass(tangled, 3)
+    L = bs._lib()
+    assert L.bs_mesh_hex_mass(1, 3, None, None) == bs.BS_EINVAL
+    assert bs.bs_mesh_hex_mass(np.zeros((0, 8, 3)), 3).size == 0

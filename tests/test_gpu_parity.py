@@ -737,3 +737,32 @@ def test_contexts_on_concurrent_streams(env):
         assert_rel(got[0], want, f"stream {k}")
     for c in ctxs:
         c.close()
+
+
+def test_unstructured_lumped_mass(env):
+    """Lumped mass of the tet-split mesh (randomly oriented): m = Z^T w_L
+    through both gathers bit for bit against the oracle on the oracle's
+    weights; sum(m) = the volume of the box; r / m bit for bit; and the
+    library's weights agree with the oracle's to rounding."""
+    bs, orc, torch, d = env
+    ev, nv, X = bs_inputs.hex_tet_split(5, 4, 3)
+    ev, sym = bs_inputs.hex_orient(ev, 771)
+    xe = bs_inputs.reorder_corners(X[bs_inputs.hex_tet_split(5, 4, 3)[0]], sym)
+    assert np.array_equal(xe, X[ev])
+    N = 5
+    l2g, ng = bs.bs_mesh_hex_l2g(ev, N, nv)
+    ol2g, _ = orc.mesh_hex(ev, N, nv)
+    off, ids = bs.bs_index_g2l(l2g, ng)
+    ow = orc.mesh_hex_mass(xe, N)
+    assert np.allclose(bs.bs_mesh_hex_mass(xe, N), ow, rtol=1e-13, atol=0)
+    want = orc.gather(ol2g, ow, ng)
+    for plan in (None, bs.bs_gather_plan(off, 1024)):
+        m = torch.empty(ng, dtype=torch.float64, device=d)
+        bs.bs_gather(dev(torch, d, off), dev(torch, d, ids), dev(torch, d, ow), m,
+                     None if plan is None else dev(torch, d, plan))
+        assert_bits(host(m), want, "unstructured lumped mass")
+    assert abs(host(m).sum() - 5 * 4 * 3) <= 1e-11 * 60
+    r = bs_inputs.uniform_pm1(772, ng)
+    y = torch.empty(ng, dtype=torch.float64, device=d)
+    bs.bs_scale(dev(torch, d, r), m, y)
+    assert_bits(host(y), orc.scale(r, want), "r / m unstructured")
