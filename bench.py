@@ -306,7 +306,10 @@ def tet_split_tables(bs, cubes, N, seed):
     return bs.bs_mesh_hex_l2g(ev, N, nv)
 
 
-def workloads(bs, torch, dev, gather_lds, steps=30):
+WORKLOADS = ["c4_shuffled40_N5", "u_tetsplit11_N7", "c2_slab32x32x4_N7", "c5_box24_N15"]
+
+
+def workloads(bs, torch, dev, gather_lds, steps=30, only=None):
     """The shuffled 40^3 order-5 mesh (scatter, gather), the unstructured
     tet-split mesh of 11^3 cubes (31944 hexahedra) at order 7 (scatter,
     gather), one GPU's share of the 32^3 order-7 mesh cut into eight z-slabs
@@ -317,6 +320,8 @@ def workloads(bs, torch, dev, gather_lds, steps=30):
                             ("u_tetsplit11_N7", 11, 7, ["scatter", "gather"]),
                             ("c2_slab32x32x4_N7", 32, 7, OPS),
                             ("c5_box24_N15", 24, 15, OPS)]:
+        if only and name not in only:
+            continue
         tables = None
         if name.startswith("u_"):
             tables = tet_split_tables(bs, E, N, bs_inputs.base_seed(name) + bs_inputs.SEED_ELEM)
@@ -439,6 +444,8 @@ def main():
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--workloads", action="store_true")
     ap.add_argument("--out", default=None)
+    ap.add_argument("--workload", action="append", choices=WORKLOADS, default=[],
+                    help="time only this workload (repeatable; skips the step; for profiling one mesh at a time)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the BS operations here run on a single MI355X; "
@@ -452,6 +459,13 @@ def main():
     dev = torch.device("cuda:0")
     bs._lib()
     ctx = bs.context(0)
+    if args.workload:
+        res = workloads(bs, torch, dev, args.gather == "lds", only=args.workload)
+        if args.out:
+            with open(args.out, "w") as f:
+                json.dump({"workloads": res}, f, indent=1)
+        print(json.dumps({"workloads": res}), flush=True)
+        return
 
     name, E, N = "c2_box32_N7", 32, 7
     mesh = Mesh(bs, torch, dev, name, E, N, gather_lds=(args.gather == "lds"), layout=args.layout)

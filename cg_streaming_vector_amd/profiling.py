@@ -116,7 +116,9 @@ def _cxxfilt(name):
 
 
 def summarize(stats_csv, fetch_csv, write_csv, copy_kernel, copy_doubles, source=None, ops=None, trace_csv=None,
-              remarks=None):
+              remarks=None, calibration=None):
+    """calibration: (fetch_scale, write_scale) to use when the run has no copy
+    kernel of its own (taken from an earlier summary's calibration block)."""
     stats = load_stats(stats_csv) if stats_csv else {}
     res = load_resources(trace_csv) if trace_csv else {}
     rem = load_remarks(remarks) if remarks else {}
@@ -127,6 +129,10 @@ def summarize(stats_csv, fetch_csv, write_csv, copy_kernel, copy_doubles, source
     if copy_kernel in fetch and copy_kernel in write:
         f_scale = known / (statistics.median(fetch[copy_kernel]) * 1024.0)
         w_scale = known / (statistics.median(write[copy_kernel]) * 1024.0)
+    reused = False
+    if f_scale is None and calibration:
+        f_scale, w_scale = calibration
+        reused = True
     kernels = {}
     names = set(stats) | set(fetch) | set(write) | set(res)
     for k in sorted(names or set(rem)):
@@ -148,7 +154,7 @@ def summarize(stats_csv, fetch_csv, write_csv, copy_kernel, copy_doubles, source
                                          + d["write_kib_median"] * 1024.0 * w_scale)
         kernels[k] = d
     out = {"calibration": {"copy_kernel": copy_kernel, "copy_doubles": copy_doubles,
-                           "fetch_scale": f_scale, "write_scale": w_scale},
+                           "fetch_scale": f_scale, "write_scale": w_scale, "reused": reused},
            "kernels": kernels}
     if ops:
         # an operation may be several kernels launched back to back (a
@@ -166,8 +172,15 @@ def to_markdown(summary, title, commands):
     lines = [f"# {title}", "", "Commands:", ""]
     lines += [f"    {c}" for c in commands]
     cal = summary["calibration"]
-    lines += ["", f"Counter calibration on `{cal['copy_kernel']}` ({cal['copy_doubles']} doubles copied): "
-              f"fetch x{cal['fetch_scale']}, write x{cal['write_scale']}" if cal["fetch_scale"] else "", ""]
+    if cal["fetch_scale"] and cal.get("reused"):
+        note = (f"Counter calibration reused from the step profile's `{cal['copy_kernel']}` run: "
+                f"fetch x{cal['fetch_scale']}, write x{cal['write_scale']}")
+    elif cal["fetch_scale"]:
+        note = (f"Counter calibration on `{cal['copy_kernel']}` ({cal['copy_doubles']} doubles copied): "
+                f"fetch x{cal['fetch_scale']}, write x{cal['write_scale']}")
+    else:
+        note = ""
+    lines += ["", note, ""]
     lines += ["| kernel | calls | avg us | FETCH KiB | WRITE KiB | HBM MB/launch |",
               "|---|---|---|---|---|---|"]
     for k, d in summary["kernels"].items():
@@ -209,11 +222,17 @@ def main(argv=None):
     ap.add_argument("--title", default="BS kernels")
     ap.add_argument("--command", action="append", default=[])
     ap.add_argument("--op", action="append", default=[], help="NAME=kernel1+kernel2 (summed averages)")
+    ap.add_argument("--calibration", help="summary JSON whose counter calibration to reuse")
     ap.add_argument("--json")
     ap.add_argument("--md")
     a = ap.parse_args(argv)
     ops = {o.split("=", 1)[0]: o.split("=", 1)[1].split("+") for o in a.op}
-    s = summarize(a.stats, a.fetch, a.write, a.copy_kernel, a.copy_doubles, a.source, ops, a.trace, a.remarks)
+    cal = None
+    if a.calibration:
+        c = json.load(open(a.calibration))["calibration"]
+        cal = (c["fetch_scale"], c["write_scale"])
+    s = summarize(a.stats, a.fetch, a.write, a.copy_kernel, a.copy_doubles, a.source, ops, a.trace, a.remarks,
+                  cal)
     if a.json:
         with open(a.json, "w") as f:
             json.dump(s, f, indent=1)

@@ -81,3 +81,14 @@ x.hip:1:1: remark:     LDS Size [bytes/block]: 32 [-Rpass-analysis=kernel-resour
     s["kernels"]["k_dot<4, false>"] = {"compiler": k}
     md = profiling.to_markdown(s, "t", [])
     assert "| `k_dot<4, false>` | 46 | 0 | 28 | 0/ | 2 |" in md
+
+
+def test_reused_calibration(tmp_path):
+    fetch = [("(anonymous namespace)::k_scatter(y)", "FETCH_SIZE", 30.0)]
+    write = [("(anonymous namespace)::k_scatter(y)", "WRITE_SIZE", 20.0)]
+    write_counters(tmp_path / "f.csv", fetch)
+    write_counters(tmp_path / "w.csv", write)
+    s = profiling.summarize(None, tmp_path / "f.csv", tmp_path / "w.csv", "k_copy<1>", 1000, calibration=(2.0, 1.0))
+    assert s["calibration"]["reused"]
+    assert s["kernels"]["k_scatter"]["hbm_bytes_per_launch"] == pytest.approx(30 * 1024 * 2 + 20 * 1024)
+    assert "reused" in profiling.to_markdown(s, "t", [])
