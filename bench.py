@@ -212,7 +212,7 @@ def traffic_for(kernels):
     """HBM bytes per launch of an operation (the sum over its kernels) from the
     committed rocprofv3 --pmc summary, if the kernel source has not changed
     since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "pmc_traffic_c2.json")
+    path = os.path.join(ROOT, "profiles", "pmc_traffic_box32_N7.json")
     if not os.path.exists(path):
         return None
     try:
@@ -264,7 +264,7 @@ def cpu_baseline(mesh_host, budget_s=12.0):
 
 
 def sweep(bs, torch, dev, reps_min=100, min_seconds=0.05):
-    """c3: each vector op over n = 2^10 .. 2^28, fitted to T(B) = T0 + B/W_max.
+    """The size sweep: each vector op over n = 2^10 .. 2^28, fitted to T(B) = T0 + B/W_max.
     The launches of each point are issued by the library's C++ loop
     (bs_bench_loop), timed on the host around the whole run as the pages
     time it; at least reps_min launches and min_seconds per point."""
@@ -306,7 +306,7 @@ def tet_split_tables(bs, cubes, N, seed):
     return bs.bs_mesh_hex_l2g(ev, N, nv)
 
 
-WORKLOADS = ["c4_shuffled40_N5", "u_tetsplit11_N7", "c2_slab32x32x4_N7", "c5_box24_N15"]
+WORKLOADS = ["shuffled40_N5", "tetsplit11_N7", "slab32x32x4_N7", "box24_N15"]
 
 
 def workloads(bs, torch, dev, gather_lds, steps=30, only=None):
@@ -316,24 +316,24 @@ def workloads(bs, torch, dev, gather_lds, steps=30, only=None):
     (32 x 32 x 4 elements, all 7 ops) and the 24^3 order-15 mesh (all 7 ops,
     and the CG streaming sequence)."""
     out = {}
-    for name, E, N, ops in [("c4_shuffled40_N5", 40, 5, ["scatter", "gather"]),
-                            ("u_tetsplit11_N7", 11, 7, ["scatter", "gather"]),
-                            ("c2_slab32x32x4_N7", 32, 7, OPS),
-                            ("c5_box24_N15", 24, 15, OPS)]:
+    for name, E, N, ops in [("shuffled40_N5", 40, 5, ["scatter", "gather"]),
+                            ("tetsplit11_N7", 11, 7, ["scatter", "gather"]),
+                            ("slab32x32x4_N7", 32, 7, OPS),
+                            ("box24_N15", 24, 15, OPS)]:
         if only and name not in only:
             continue
         tables = None
-        if name.startswith("u_"):
+        if name.startswith("tetsplit"):
             tables = tet_split_tables(bs, E, N, bs_inputs.base_seed(name) + bs_inputs.SEED_ELEM)
-        elif name.startswith("c2_slab"):
+        elif name.startswith("slab"):
             tables = (bs.bs_mesh_box_l2g(E, E, 4, N), bs.bs_mesh_box_count(E, E, 4, N)[1])
         m = Mesh(bs, torch, dev, name, E, N, gather_lds, tables=tables)
         if tables is not None:
-            out[name + "_mesh"] = {"elements": 24 * E ** 3 if name.startswith("u_") else E * E * 4, "order": N,
+            out[name + "_mesh"] = {"elements": 24 * E ** 3 if name.startswith("tetsplit") else E * E * 4, "order": N,
                                    "n_local": m.nl, "n_global": m.ng}
         stream = torch.cuda.current_stream().cuda_stream
         # rotated sets: >= 1 GB through the cache between two touches
-        R = 3 if name.startswith("c5") else 48 if name.startswith("c2_slab") else 5
+        R = 3 if name.startswith("box24") else 48 if name.startswith("slab") else 5
         sets = [m] + [m.clone() for _ in range(R - 1)]
         per_op = time_ops_native(bs, sets, ops, max(3 * R, 96))
         del sets
@@ -341,8 +341,8 @@ def workloads(bs, torch, dev, gather_lds, steps=30, only=None):
                     "GBps": round(m.bytes(op) / per_op[op] / 1e9, 1),
                     "pct_peak": round(100 * m.bytes(op) / per_op[op] / 1e9 / PEAK_GBPS, 1)} for op in ops}
         out[name] = res
-        if name == "c5_box24_N15":
-            out["cg_sequence_c5"] = cg_sequence(bs, torch, dev, m)
+        if name == "box24_N15":
+            out["cg_sequence_box24_N15"] = cg_sequence(bs, torch, dev, m)
         del m
         torch.cuda.empty_cache()
     return out
@@ -467,7 +467,7 @@ def main():
         print(json.dumps({"workloads": res}), flush=True)
         return
 
-    name, E, N = "c2_box32_N7", 32, 7
+    name, E, N = "box32_N7", 32, 7
     mesh = Mesh(bs, torch, dev, name, E, N, gather_lds=(args.gather == "lds"), layout=args.layout)
     stream = torch.cuda.current_stream().cuda_stream
     launch = mesh.launchers(bs, stream)

@@ -28,7 +28,7 @@ _GAMMA = np.uint64(0x9E3779B97F4A7C15)
 _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
 
-# Per-array seed offsets; the base seed of a workload is 1000 + its index.
+# Per-array seed offsets from the base seed of a workload.
 SEED_X, SEED_P, SEED_R, SEED_Q, SEED_Y, SEED_ELEM, SEED_NODE = 1, 2, 3, 4, 5, 6, 7
 
 
@@ -66,21 +66,21 @@ def permutation(seed: int, n: int) -> np.ndarray:
     return np.argsort(w, kind="stable").astype(np.int32)
 
 
-# The five workloads: (name, elements per side, order, shuffled).
+# The box meshes: (name, elements per side, order, shuffled).
 MESHES = {
-    "c1_box8_N3": (8, 3, False),
-    "c2_box32_N7": (32, 7, False),
-    "c4_shuffled40_N5": (40, 5, True),
-    "c5_box24_N15": (24, 15, False),
+    "box8_N3": (8, 3, False),
+    "box32_N7": (32, 7, False),
+    "shuffled40_N5": (40, 5, True),
+    "box24_N15": (24, 15, False),
 }
-CONFIG_INDEX = {"c1_box8_N3": 0, "c2_box32_N7": 1, "c3_sweep": 2,
-                "c4_shuffled40_N5": 3, "c5_box24_N15": 4,
-                "u_tetsplit11_N7": 5,  # unstructured: 11^3 cubes cut into 24 hexahedra each
-                "c2_slab32x32x4_N7": 6}  # one of eight z-slabs of the 32^3 order-7 box
+BASE_SEED = {"box8_N3": 1000, "box32_N7": 1001, "sweep": 1002,
+             "shuffled40_N5": 1003, "box24_N15": 1004,
+             "tetsplit11_N7": 1005,  # unstructured: 11^3 cubes cut into 24 hexahedra each
+             "slab32x32x4_N7": 1006}  # one of eight z-slabs of the 32^3 order-7 box
 
 
 def base_seed(name: str) -> int:
-    return 1000 + CONFIG_INDEX[name]
+    return BASE_SEED[name]
 
 
 def mesh_perms(name: str, E: int, N: int):

@@ -130,7 +130,7 @@ def test_full_size_tables_match_oracle(bs, orc):
     off, ids = bs.bs_index_g2l(l2g, ng)
     ooff, oids = orc.g2l(ol2g, ng)
     assert np.array_equal(off, ooff) and np.array_equal(ids, oids)
-    ep, npm = bs_inputs.mesh_perms("c4_shuffled40_N5", 40, 5)
+    ep, npm = bs_inputs.mesh_perms("shuffled40_N5", 40, 5)
     l2g = bs.bs_mesh_box_l2g(40, 40, 40, 5, ep, npm)
     ol2g, ng = orc.mesh_box(40, 40, 40, 5, ep, npm)
     assert np.array_equal(l2g, ol2g)

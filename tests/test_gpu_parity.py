@@ -175,7 +175,7 @@ def test_sweep_sizes(env, k):
     """The 2^10 .. 2^28 sweep: every op, whole vectors against the oracle."""
     bs, orc, torch, d = env
     n = 1 << k
-    name = "c3_sweep"
+    name = "sweep"
     v = bs_inputs.vectors(name, n, "xpqr")
     x, p, q, r = (dev(torch, d, v[c]) for c in "xpqr")
     y = torch.empty_like(x)
@@ -196,10 +196,10 @@ def test_sweep_sizes(env, k):
 # ----------------------------------------------------- scatter / gather ----
 
 MESHES = {
-    "c1_box8_N3": (8, 3),
-    "c2_box32_N7": (32, 7),
-    "c4_shuffled40_N5": (40, 5),
-    "c5_box24_N15": (24, 15),
+    "box8_N3": (8, 3),
+    "box32_N7": (32, 7),
+    "shuffled40_N5": (40, 5),
+    "box24_N15": (24, 15),
 }
 
 
@@ -243,7 +243,7 @@ def test_scatter_gather_mesh(env, name):
 def test_gather_multiplicity_and_identity(env):
     """gather(1_L) is the node multiplicity; scatter(g) returns l2g."""
     bs, orc, torch, d = env
-    l2g, off, ids, ol2g, ng = mesh_case(env, "c2_box32_N7")
+    l2g, off, ids, ol2g, ng = mesh_case(env, "box32_N7")
     m = np.diff(off).astype(np.float64)
     vg = torch.empty(ng, dtype=torch.float64, device=d)
     bs.bs_gather(dev(torch, d, off), dev(torch, d, ids), torch.ones(l2g.size, dtype=torch.float64, device=d), vg)
@@ -401,7 +401,7 @@ def test_cg_sequence_matches_oracle(env):
 
 # ----------------------------------------- gather + dot, device-resident CG ----
 
-@pytest.mark.parametrize("name", ["c1_box8_N3", "c2_box32_N7"])
+@pytest.mark.parametrize("name", ["box8_N3", "box32_N7"])
 def test_gather_dot(env, name):
     """bs_gather_dot: the gather's bits unchanged, w . v_G to 1e-12."""
     bs, orc, torch, d = env
@@ -432,7 +432,7 @@ def test_scale_bit_exact(env, n):
     assert_bits(host(xt), orc.scale(x, dv), f"scale in place n={n}")
 
 
-@pytest.mark.parametrize("name", ["c1_box8_N3", "c2_box32_N7"])
+@pytest.mark.parametrize("name", ["box8_N3", "box32_N7"])
 def test_lumped_mass_and_inverse_scale(env, name):
     """m = Z^T w_L through bs_gather, then y = r / m through bs_scale, bit for
     bit against the oracle on the same weights; the library's own weights
@@ -467,7 +467,7 @@ def cg_setup(env, name):
     return t, ol2g, ng, b
 
 
-@pytest.mark.parametrize("name", ["c1_box8_N3", "c2_box32_N7"])
+@pytest.mark.parametrize("name", ["box8_N3", "box32_N7"])
 def test_cg_solve_matches_oracle(env, name):
     """Four device-resident CG iterations on Z^T Z against the oracle's CG:
     same residual history to 1e-12 while it is significant, same x, and
@@ -491,7 +491,7 @@ def test_cg_solve_early_exit_and_zero_iterations(env):
     """A tolerance stops the iteration on the device: later history entries
     stay -1 and x no longer changes; iters = 0 only measures rr0."""
     bs, orc, torch, d = env
-    t, ol2g, ng, b = cg_setup(env, "c1_box8_N3")
+    t, ol2g, ng, b = cg_setup(env, "box8_N3")
     x, r, p = t["x"].clone(), t["r"].clone(), t["p"].clone()
     hist = host(bs.bs_cg_solve(t["l2g"], t["off"], t["ids"], x, r, p, t["q"], t["pl"], 12, 1e-10, t["plan"]))
     done = [i for i in range(1, 13) if hist[i] >= 0]
@@ -611,7 +611,7 @@ def test_bench_loop_scatter_gather(env):
     """Scatter and gather through bs_bench_loop write what the direct calls
     write (both gather kernels), on the 8^3 order-3 box."""
     bs, orc, torch, d = env
-    l2g, off, ids, ol2g, ng = mesh_case(env, "c1_box8_N3")
+    l2g, off, ids, ol2g, ng = mesh_case(env, "box8_N3")
     vgv = bs_inputs.uniform_pm1(751, ng)
     vlv = bs_inputs.uniform_pm1(752, l2g.size)
     vl = torch.empty(l2g.size, dtype=torch.float64, device=d)
