@@ -47,8 +47,8 @@ PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 METRIC = "effective GB/s and % of HBM peak per BS op (fp64, N=7 hex mesh, 1 GPU)"
 OPS = ["copy", "axpy", "norm", "dot", "cg_update", "scatter", "gather"]
 KERNEL_NAME = {  # op -> its kernels as rocprofv3 names them (namespace and arguments stripped)
-    "copy": ["k_copy<1>"], "axpy": ["k_axpy<1>"], "norm": ["k_dot<4, true>", "k_finish"],
-    "dot": ["k_dot<4, false>", "k_finish"], "cg_update": ["k_cg_update<4>", "k_finish"],
+    "copy": ["k_copy<1>"], "axpy": ["k_axpy<1>"], "norm": ["k_dot<4, true>"],
+    "dot": ["k_dot<4, false>"], "cg_update": ["k_cg_update<4>"],
     "scatter": ["k_scatter"], "gather": ["k_gather_plan<false>"],
 }
 GATHER_NPB = 1024
@@ -484,22 +484,24 @@ def main():
     hot = time_ops_native(bs, [mesh], OPS, args.per_op_reps)
     torch.cuda.empty_cache()
 
-    # timed region: host clock around K steps; HIP events on the launch
-    # stream around the dominant kernel in every step
+    # timed region: host clock around K steps; in every step the dominant
+    # kernel records a pair of HIP events at its own start and end (the
+    # library launches it with them, as armed by time_next), on its stream
     for _ in range(args.warmup):
         for op in OPS:
             launch[op]()
-    torch.cuda.synchronize()
     cur = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in ev:  # create them
+        a.record(cur)
+        b.record(cur)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
         for op in OPS:
             if op == dom:
-                ev[k][0].record(cur)
+                ctx.time_next(*ev[k])
             launch[op]()
-            if op == dom:
-                ev[k][1].record(cur)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     dom_live = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3

@@ -52,6 +52,7 @@ SIGNATURES = {
     "bs_ctx_create": ([_int, ctypes.POINTER(_ptr)], _int),
     "bs_ctx_destroy": ([_ptr], None),
     "bs_ctx_info": ([_ptr, ctypes.POINTER(_int), ctypes.POINTER(_int), ctypes.POINTER(_int)], _int),
+    "bs_ctx_time_next": ([_ptr, _ptr, _ptr], _int),
     "bs_copy": ([_ptr, _i64, _ptr, _ptr, _ptr], _int),
     "bs_axpy": ([_ptr, _i64, _dbl, _ptr, _dbl, _ptr, _ptr], _int),
     "bs_norm": ([_ptr, _i64, _ptr, _ptr, _ptr], _int),
@@ -117,6 +118,20 @@ class Context:
         d, c, m = _int(), _int(), _int()
         _check(_lib().bs_ctx_info(self._h, ctypes.byref(d), ctypes.byref(c), ctypes.byref(m)), "bs_ctx_info")
         return {"device": d.value, "cu_count": c.value, "max_partials": m.value}
+
+    def time_next(self, start=None, stop=None):
+        """Arm kernel timing: the next kernel launched with this context
+        records the torch.cuda.Events `start` and `stop` (timing enabled, each
+        recorded once beforehand so that it exists) at its own start and end.
+        No arguments disarm."""
+        def handle(e):
+            if e is None:
+                return None
+            h = e.cuda_event
+            if not h:
+                raise ValueError("record the event once before arming, so that it exists")
+            return h
+        _check(_lib().bs_ctx_time_next(self._h, handle(start), handle(stop)), "bs_ctx_time_next")
 
     def close(self):
         if getattr(self, "_h", None) is not None and self._h.value:

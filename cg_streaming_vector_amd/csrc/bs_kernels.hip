@@ -12,8 +12,9 @@
 //    the unroll depth and blocks per CU chosen per operation by measurement;
 //  - reductions: per-lane accumulation, a wavefront butterfly through
 //    cross-lane shuffles, the block's wavefronts through LDS, one partial per
-//    block, then a one-block second kernel that sums the partials in a fixed
-//    order. No atomics anywhere, so results repeat bit for bit;
+//    block; the last block to arrive (an atomic ticket) sums the partials in
+//    a fixed order in the same kernel. No atomics touch the values, so
+//    results repeat bit for bit;
 //  - scatter: each lane owns pairs of consecutive local entries, loads their
 //    two indices as one 8-byte word and stores the two values as one 16-byte
 //    word, 32 pairs per lane in flight;
@@ -32,6 +33,7 @@
 // IEEE definition. Reductions use explicit fma for the per-lane sums (they
 // are checked against a relative tolerance, not bits).
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -118,23 +120,163 @@ __device__ __forceinline__ double block_sum(double v)
     return s;
 }
 
-// Second stage of every reduction: one block sums the nb per-block partials
-// in a fixed order and writes the result, or its square root; nb == 0 stores
-// +0.0. The kernel boundary between the two stages makes the partials
-// visible across XCDs. A single-kernel "last block" finish needs either an
-// agent-scope release per block, which on this multi-XCD part writes back
-// that XCD's L2 (about 10 us per call at 256-512 blocks), or scratch in
-// uncached memory with tickets, which was correct but no faster than the
-// second launch at 11M elements.
+// Finishes of the device-resident CG iteration (unpreconditioned CG, the
+// vector operations of the BS paper's CG list):
+//  kStart: rr = r.r; history[0] = rr; convergence threshold tol2 * rr; the
+//          history entries after 0 are set to -1 (an iteration that runs
+//          overwrites its entry).
+//  kSetAlpha: alpha = rr / (p.q).
+//  kSetBeta:  rr' = r'.r'; beta = rr' / rr; rr = rr'; history[k+1] = rr';
+//          converged when rr' <= threshold (or rr' == 0).
+// cg_apply stores the scalars from the reduced sum s (one thread);
+// cg_hist_init clears the history (any threads of one block).
+enum CgFinish { kStart = 0, kSetAlpha = 1, kSetBeta = 2 };
+
+__device__ __forceinline__ void cg_hist_init(double *hist, int iters, int nthreads)
+{
+    for (int i = 1 + (int)threadIdx.x; i <= iters; i += nthreads) hist[i] = -1.0;
+}
+
+__device__ __forceinline__ void cg_apply(int mode, double s, double *cgs, double *hist, int k, double tol2)
+{
+    if (mode == kStart) {
+        cgs[kRR] = s;
+        cgs[kThreshold] = tol2 * s;
+        cgs[kDone] = (s == 0.0) ? 1.0 : 0.0;
+        hist[0] = s;
+    } else if (mode == kSetAlpha) {
+        cgs[kAlpha] = cgs[kRR] / s;
+    } else {
+        cgs[kBeta] = s / cgs[kRR];
+        cgs[kRR] = s;
+        hist[k + 1] = s;
+        if (s == 0.0 || s <= cgs[kThreshold]) cgs[kDone] = 1.0;
+    }
+}
+
+// One-kernel finish of the vector reductions (norm, dot, fused update), with
+// no second launch. Each block publishes its partial with an agent-scope
+// atomic store, which on this multi-XCD part writes through to the memory
+// side instead of staying in the block's XCD-local L2; waits until that store
+// has completed (s_waitcnt vmcnt(0)); then takes a ticket with an agent-scope
+// atomic add. The block that draws the last ticket reads every partial back
+// with agent-scope atomic loads, which fetch from the memory side and so
+// never see a line left in its own L2 by an earlier call, and sums them in
+// index order. Partials and tickets are touched only by agent-scope atomics,
+// so every value crosses the XCDs coherently; the wait alone orders the
+// partial before the ticket, as the memory model's own release sequence does
+// for an earlier atomic store. (A release RMW would add an L2 write-back of
+// all ordinary stores of the XCD, about 10 us per call at 256-512 blocks.)
+// Grids of up to kOneTicket blocks draw from one counter; larger ones count
+// first per group of blocks with the same blockIdx mod 8 (the block's XCD),
+// each group's counter on its own 256-byte line, so that arrivals do not
+// queue on one address (at 512 blocks one counter costs 3 us, grouping 0).
+// The last arrival at each counter resets it to zero for the next call. The
+// tickets only choose which block finishes: the sum is in a fixed order, so
+// results repeat bit for bit.
+constexpr unsigned kOneTicket = 256;
+constexpr int kTicketStride = 64;                // unsigned ints: 256 bytes
+constexpr int kTickets = 9 * kTicketStride;      // [0] the grid, [(1 + g) * stride] group g
+
+enum FinMode { kFinOut = 0, kFinSqrt = 1, kFinCg = 2 };
+struct Fin {
+    int mode;           // kFinOut: *out = s; kFinSqrt: *out = sqrt(s); kFinCg: cg_apply(cg, s)
+    int cg;             // CgFinish
+    double *partials;   // one slot per block
+    unsigned *tickets;  // kTickets counters, zero between calls
+    double *out;
+    double *cgs;
+    double *hist;
+    int k, iters;
+    double tol2;
+};
+
+// Called by every thread of every block with the block's partial (valid in
+// thread 0); true in the block that is to finish.
+__device__ __forceinline__ bool last_arrival(double part, const Fin &f)
+{
+    __shared__ bool last;
+    if (threadIdx.x == 0) {
+        __hip_atomic_store(&f.partials[blockIdx.x], part, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);
+        bool l;
+        if (gridDim.x <= kOneTicket) {
+            l = __hip_atomic_fetch_add(&f.tickets[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                gridDim.x - 1;
+        } else {
+            const unsigned g = blockIdx.x & 7u;
+            const unsigned members = gridDim.x / 8u + (g < (gridDim.x & 7u) ? 1u : 0u);
+            unsigned *gc = &f.tickets[(1 + g) * kTicketStride];
+            l = false;
+            if (__hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == members - 1) {
+                __hip_atomic_store(gc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                l = __hip_atomic_fetch_add(&f.tickets[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 7u;
+            }
+        }
+        if (l) __hip_atomic_store(&f.tickets[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = l;
+    }
+    __syncthreads();
+    return last;
+}
+
+// In the finishing block (all kBlock threads): the partials summed in a fixed
+// order (each lane a strided run, the wave butterfly, the waves in order),
+// then stored as the mode says.
+__device__ __forceinline__ void finish_last(const Fin &f)
+{
+    __shared__ double wsum[kBlock / kWave];
+    const unsigned nb = gridDim.x;
+    double s = 0.0;
+    for (unsigned i = threadIdx.x; i < nb; i += kBlock)
+        s += __hip_atomic_load(&f.partials[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s = wave_sum(s);
+    if ((threadIdx.x & (kWave - 1)) == 0) wsum[threadIdx.x / kWave] = s;
+    if (f.mode == kFinCg && f.cg == kStart) cg_hist_init(f.hist, f.iters, kBlock);
+    __syncthreads();
+    if (threadIdx.x != 0) return;
+    double t = 0.0;
+#pragma unroll
+    for (int i = 0; i < kBlock / kWave; ++i) t += wsum[i];
+    if (f.mode == kFinOut)
+        *f.out = t;
+    else if (f.mode == kFinSqrt)
+        *f.out = std::sqrt(t);
+    else
+        cg_apply(f.cg, t, f.cgs, f.hist, f.k, f.tol2);
+}
+
+__device__ __forceinline__ void finish_block(double part, const Fin &f)
+{
+    if (last_arrival(part, f)) finish_last(f);
+}
+
+// Two-kernel reductions (the gather's folded dot, whose grid has one block
+// per plan block, and the 8-byte fallbacks): one block sums the nb per-block
+// partials in a fixed order and writes the result; nb == 0 stores +0.0. The
+// kernel boundary makes the partials visible across XCDs.
 //
 // finish_sum: the sum over one kFinishBlock-thread block, valid in thread 0:
 // each lane a strided run in index order, then the wave butterfly, then the
-// 16 wave sums in order.
+// 16 wave sums in order. A lane issues its loads kFinishBatch at a time, all
+// before the adds: the gather's folded dot leaves one partial per plan block
+// (55297 at 24^3 order 15), and one load in flight per lane made this sum
+// latency-bound (23 us).
+constexpr int kFinishBatch = 32;
 __device__ __forceinline__ double finish_sum(const double *__restrict__ partials, int nb)
 {
     __shared__ double wsum[kFinishBlock / kWave];
     double s = 0.0;
-    for (int i = threadIdx.x; i < nb; i += kFinishBlock) s += partials[i];
+    for (int i0 = threadIdx.x; i0 < nb; i0 += kFinishBatch * kFinishBlock) {
+        double v[kFinishBatch];
+#pragma unroll
+        for (int k = 0; k < kFinishBatch; ++k) {
+            const int i = i0 + k * kFinishBlock;
+            v[k] = i < nb ? partials[i] : 0.0;
+        }
+#pragma unroll
+        for (int k = 0; k < kFinishBatch; ++k) s += v[k];
+    }
     s = wave_sum(s);
     if ((threadIdx.x & (kWave - 1)) == 0) wsum[threadIdx.x / kWave] = s;
     __syncthreads();
@@ -153,40 +295,17 @@ __global__ __launch_bounds__(kFinishBlock) void k_finish(const double *__restric
     if (threadIdx.x == 0) *out = take_sqrt ? std::sqrt(s) : s;
 }
 
-// Finishes of the device-resident CG iteration (unpreconditioned CG, the
-// vector operations of the BS paper's CG list):
-//  kStart: rr = r.r; history[0] = rr; convergence threshold tol2 * rr; the
-//          history entries after 0 are set to -1 (an iteration that runs
-//          overwrites its entry).
-//  kSetAlpha: alpha = rr / (p.q).
-//  kSetBeta:  rr' = r'.r'; beta = rr' / rr; rr = rr'; history[k+1] = rr';
-//          converged when rr' <= threshold (or rr' == 0).
-enum CgFinish { kStart = 0, kSetAlpha = 1, kSetBeta = 2 };
-
+// Second stage of the CG iteration's alpha (after the gather's folded p.q).
 __global__ __launch_bounds__(kFinishBlock) void k_cg_finish(const double *__restrict__ partials, int nb,
                                                             double *__restrict__ cgs, double *__restrict__ hist,
                                                             int k, int iters, double tol2, int mode)
 {
-    if (mode == kStart) {
-        for (int i = 1 + threadIdx.x; i <= iters; i += kFinishBlock) hist[i] = -1.0;
-    } else if (cgs[kDone] != 0.0) {
+    if (mode == kStart)
+        cg_hist_init(hist, iters, kFinishBlock);
+    else if (cgs[kDone] != 0.0)
         return;
-    }
     const double s = finish_sum(partials, nb);
-    if (threadIdx.x != 0) return;
-    if (mode == kStart) {
-        cgs[kRR] = s;
-        cgs[kThreshold] = tol2 * s;
-        cgs[kDone] = (s == 0.0) ? 1.0 : 0.0;
-        hist[0] = s;
-    } else if (mode == kSetAlpha) {
-        cgs[kAlpha] = cgs[kRR] / s;
-    } else {
-        cgs[kBeta] = s / cgs[kRR];
-        cgs[kRR] = s;
-        hist[k + 1] = s;
-        if (s == 0.0 || s <= cgs[kThreshold]) cgs[kDone] = 1.0;
-    }
+    if (threadIdx.x == 0) cg_apply(mode, s, cgs, hist, k, tol2);
 }
 
 // ------------------------------------------------------- vector layout ----
@@ -322,7 +441,7 @@ __global__ __launch_bounds__(kBlock) void k_scale_scalar(int64_t n, const double
 // lane in flight instead of trading registers for waves it will not get.
 template <int U, bool kSquare>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_dot(
-    Split sp, const double *__restrict__ x, const double *__restrict__ y, double *__restrict__ partials)
+    Split sp, const double *__restrict__ x, const double *__restrict__ y, Fin f)
 {
     const d2 *xv = reinterpret_cast<const d2 *>(x + sp.head);
     const d2 *yv = reinterpret_cast<const d2 *>((kSquare ? x : y) + sp.head);
@@ -357,8 +476,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 2))) 
         if (sp.head) acc0 = __builtin_fma(x[0], yy[0], acc0);
         if (sp.tail >= 0) acc1 = __builtin_fma(x[sp.tail], yy[sp.tail], acc1);
     }
-    const double part = block_sum(acc0 + acc1);
-    if (threadIdx.x == 0) partials[blockIdx.x] = part;
+    finish_block(block_sum(acc0 + acc1), f);
 }
 
 // -------------------------------------------------- BS5 fused CG update ----
@@ -377,8 +495,7 @@ __device__ __forceinline__ void cg2(double a, d2 p, d2 q, d2 &x, d2 &r)
 template <int U>
 __global__ __launch_bounds__(kBlock) void k_cg_update(Split sp, Coef ca, const double *__restrict__ p,
                                                       const double *__restrict__ q, double *__restrict__ x,
-                                                      double *__restrict__ r, double *__restrict__ partials,
-                                                      const double *cgs)
+                                                      double *__restrict__ r, Fin f, const double *cgs)
 {
     if (skipped(cgs)) return;
     const double a = ca.get();
@@ -434,8 +551,7 @@ __global__ __launch_bounds__(kBlock) void k_cg_update(Split sp, Coef ca, const d
             acc1 = __builtin_fma(nr, nr, acc1);
         }
     }
-    const double part = block_sum(acc0 + acc1);
-    if (threadIdx.x == 0) partials[blockIdx.x] = part;
+    finish_block(block_sum(acc0 + acc1), f);
 }
 
 // --------------------------------------------------------- BS7 scatter ----
@@ -693,8 +809,10 @@ struct bs_ctx {
     int device;
     int cus;
     int max_partials;
-    double *partials;  // first-stage reduction results, one per block
-    double *cgs;       // device-resident CG scalars (CgSlot)
+    double *partials;   // first-stage reduction results, one per block
+    unsigned *tickets;  // arrival counters of the one-kernel reductions (kTickets, zero between calls)
+    double *cgs;        // device-resident CG scalars (CgSlot)
+    hipEvent_t time_start, time_stop;  // armed by bs_ctx_time_next for the next kernel, else null
 };
 
 namespace {
@@ -702,6 +820,20 @@ namespace {
 inline bool misaligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
 inline int launch_status() { return hipGetLastError() == hipSuccess ? BS_OK : BS_EHIP; }
+
+// Every kernel of the operations goes through here. If bs_ctx_time_next has
+// armed the context, this launch carries the two events, which the runtime
+// sets to the kernel's own start and end, and the context disarms.
+template <typename K, typename... Args>
+void launch(bs_ctx *c, K kernel, dim3 grid, dim3 block, unsigned shmem, hipStream_t st, Args... args)
+{
+    if (c->time_start || c->time_stop) {
+        hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, c->time_start, c->time_stop, 0, args...);
+        c->time_start = c->time_stop = nullptr;
+    } else {
+        hipLaunchKernelGGL(kernel, grid, block, shmem, st, args...);
+    }
+}
 
 // Grid of a vector kernel with shape s over n2 pairs: the tiles needed, at
 // most CUs * blocks_per_cu (when that is set). A reduction's grid is also
@@ -749,42 +881,73 @@ inline int check_ctx(const bs_ctx *c)
 
 int finish_launch(bs_ctx *c, unsigned nb, double *out, bool take_sqrt, hipStream_t st)
 {
-    hipLaunchKernelGGL(k_finish, dim3(1), dim3(kFinishBlock), 0, st, c->partials, (int)nb, out, take_sqrt);
+    launch(c, k_finish, dim3(1), dim3(kFinishBlock), 0, st, c->partials, (int)nb, out, take_sqrt);
     return launch_status();
 }
 
-// First stage of norm / dot into the context's partials; returns the block
-// count through *nb.
-int dot_stage(bs_ctx *c, int64_t n, const double *x, const double *y, bool square, hipStream_t st,
-              unsigned *nb)
+// How a one-kernel reduction of this context stores its result.
+Fin fin_out(const bs_ctx *c, double *out, bool take_sqrt)
+{
+    Fin f{};
+    f.mode = take_sqrt ? kFinSqrt : kFinOut;
+    f.partials = c->partials;
+    f.tickets = c->tickets;
+    f.out = out;
+    return f;
+}
+
+Fin fin_cg(const bs_ctx *c, int mode, double *hist, int k, int iters, double tol2)
+{
+    Fin f{};
+    f.mode = kFinCg;
+    f.cg = mode;
+    f.partials = c->partials;
+    f.tickets = c->tickets;
+    f.cgs = c->cgs;
+    f.hist = hist;
+    f.k = k;
+    f.iters = iters;
+    f.tol2 = tol2;
+    return f;
+}
+
+// Second launch for the two-kernel paths (8-byte fallbacks).
+int finish_two_stage(bs_ctx *c, unsigned nb, const Fin &f, hipStream_t st)
+{
+    if (f.mode == kFinCg) {
+        launch(c, k_cg_finish, dim3(1), dim3(kFinishBlock), 0, st, c->partials, (int)nb, c->cgs, f.hist,
+                           f.k, f.iters, f.tol2, f.cg);
+        return launch_status();
+    }
+    return finish_launch(c, nb, f.out, f.mode == kFinSqrt, st);
+}
+
+// norm / dot of n > 0 elements, finished as f says.
+int dot_launch(bs_ctx *c, int64_t n, const double *x, const double *y, bool square, const Fin &f, hipStream_t st)
 {
     const void *ptrs[2] = {x, square ? x : y};
     int64_t head;
     if (common_head(ptrs, 2, &head)) {
         const Split sp = split_of(n, head);
-        if (square) {
-            *nb = vector_grid(c, sp.n2, kNormShape, true);
-            hipLaunchKernelGGL((k_dot<kNormShape.unroll, true>), dim3(*nb), dim3(kBlock), 0, st, sp, x, x,
-                               c->partials);
-        } else {
-            *nb = vector_grid(c, sp.n2, kDotShape, true);
-            hipLaunchKernelGGL((k_dot<kDotShape.unroll, false>), dim3(*nb), dim3(kBlock), 0, st, sp, x, y,
-                               c->partials);
-        }
-    } else {
-        *nb = scalar_grid(c, n);
-        hipLaunchKernelGGL(k_dot_scalar, dim3(*nb), dim3(kBlock), 0, st, n, x, y, c->partials);
+        if (square)
+            launch(c, (k_dot<kNormShape.unroll, true>), dim3(vector_grid(c, sp.n2, kNormShape, true)),
+                               dim3(kBlock), 0, st, sp, x, x, f);
+        else
+            launch(c, (k_dot<kDotShape.unroll, false>), dim3(vector_grid(c, sp.n2, kDotShape, true)),
+                               dim3(kBlock), 0, st, sp, x, y, f);
+        return launch_status();
     }
-    return launch_status();
+    const unsigned nb = scalar_grid(c, n);
+    launch(c, k_dot_scalar, dim3(nb), dim3(kBlock), 0, st, n, x, y, c->partials);
+    if (hipGetLastError() != hipSuccess) return BS_EHIP;
+    return finish_two_stage(c, nb, f, st);
 }
 
 int reduce_launch(bs_ctx *c, int64_t n, const double *x, const double *y, double *out, bool square,
                   hipStream_t st)
 {
     if (n == 0) return finish_launch(c, 0, out, false, st);
-    unsigned nb;
-    if (int s = dot_stage(c, n, x, y, square, st, &nb)) return s;
-    return finish_launch(c, nb, out, square, st);
+    return dot_launch(c, n, x, y, square, fin_out(c, out, square), st);
 }
 
 // Gather launch shared by bs_gather, bs_gather_dot and the CG iteration.
@@ -795,19 +958,19 @@ int gather_launch(bs_ctx *c, int64_t ng, const int32_t *off, const int32_t *ids,
     if (bstart) {
         *nb = (unsigned)nblocks;
         if (w)
-            hipLaunchKernelGGL(k_gather_plan<true>, dim3(*nb), dim3(kBlock), 0, st, bstart, off, ids, vl, vg, w,
+            launch(c, k_gather_plan<true>, dim3(*nb), dim3(kBlock), 0, st, bstart, off, ids, vl, vg, w,
                                c->partials, cgs);
         else
-            hipLaunchKernelGGL(k_gather_plan<false>, dim3(*nb), dim3(kBlock), 0, st, bstart, off, ids, vl, vg,
+            launch(c, k_gather_plan<false>, dim3(*nb), dim3(kBlock), 0, st, bstart, off, ids, vl, vg,
                                nullptr, nullptr, cgs);
     } else {
         const int64_t per = (int64_t)kBlock * kGatherRowR;
         *nb = (unsigned)((ng + per - 1) / per);
         if (w)
-            hipLaunchKernelGGL(k_gather_rows<true>, dim3(*nb), dim3(kBlock), 0, st, ng, off, ids, vl, vg, w,
+            launch(c, k_gather_rows<true>, dim3(*nb), dim3(kBlock), 0, st, ng, off, ids, vl, vg, w,
                                c->partials, cgs);
         else
-            hipLaunchKernelGGL(k_gather_rows<false>, dim3(*nb), dim3(kBlock), 0, st, ng, off, ids, vl, vg,
+            launch(c, k_gather_rows<false>, dim3(*nb), dim3(kBlock), 0, st, ng, off, ids, vl, vg,
                                nullptr, nullptr, cgs);
     }
     return launch_status();
@@ -865,12 +1028,24 @@ int bs_ctx_create(int device, bs_ctx **out)
     c->cus = cus;
     c->max_partials = kMaxPartials;
     c->partials = nullptr;
+    c->tickets = nullptr;
     c->cgs = nullptr;
+    c->time_start = c->time_stop = nullptr;
     if (hipMalloc(&c->partials, sizeof(double) * kMaxPartials) != hipSuccess ||
+        hipMalloc(&c->tickets, sizeof(unsigned) * kTickets) != hipSuccess ||
         hipMalloc(&c->cgs, sizeof(double) * kCgSlots) != hipSuccess) {
         if (c->partials) (void)hipFree(c->partials);
+        if (c->tickets) (void)hipFree(c->tickets);
         delete c;
         return BS_ENOMEM;
+    }
+    // the tickets start at zero; every reduction leaves them at zero
+    if (hipMemset(c->tickets, 0, sizeof(unsigned) * kTickets) != hipSuccess) {
+        (void)hipFree(c->partials);
+        (void)hipFree(c->tickets);
+        (void)hipFree(c->cgs);
+        delete c;
+        return BS_EHIP;
     }
     *out = c;
     return BS_OK;
@@ -882,9 +1057,18 @@ void bs_ctx_destroy(bs_ctx *c)
     if (hipSetDevice(c->device) == hipSuccess) {
         (void)hipDeviceSynchronize();
         (void)hipFree(c->partials);
+        (void)hipFree(c->tickets);
         (void)hipFree(c->cgs);
     }
     delete c;
+}
+
+int bs_ctx_time_next(bs_ctx *c, void *start_event, void *stop_event)
+{
+    if (!c) return BS_EINVAL;
+    c->time_start = static_cast<hipEvent_t>(start_event);
+    c->time_stop = static_cast<hipEvent_t>(stop_event);
+    return BS_OK;
 }
 
 int bs_ctx_info(const bs_ctx *c, int *device, int *cu_count, int *max_partials)
@@ -909,10 +1093,10 @@ int bs_copy(bs_ctx *c, int64_t n, const double *x, double *y, void *stream)
     int64_t head;
     if (common_head(ptrs, 2, &head)) {
         const Split sp = split_of(n, head);
-        hipLaunchKernelGGL(k_copy<kCopyShape.unroll>, dim3(vector_grid(c, sp.n2, kCopyShape, false)), dim3(kBlock),
+        launch(c, k_copy<kCopyShape.unroll>, dim3(vector_grid(c, sp.n2, kCopyShape, false)), dim3(kBlock),
                            0, st, sp, x, y);
     } else {
-        hipLaunchKernelGGL(k_copy_scalar, dim3(scalar_grid(c, n)), dim3(kBlock), 0, st, n, x, y);
+        launch(c, k_copy_scalar, dim3(scalar_grid(c, n)), dim3(kBlock), 0, st, n, x, y);
     }
     return launch_status();
 }
@@ -928,10 +1112,10 @@ int bs_axpy(bs_ctx *c, int64_t n, double alpha, const double *x, double beta, do
     int64_t head;
     if (common_head(ptrs, 2, &head)) {
         const Split sp = split_of(n, head);
-        hipLaunchKernelGGL(k_axpy<kAxpyShape.unroll>, dim3(vector_grid(c, sp.n2, kAxpyShape, false)), dim3(kBlock),
+        launch(c, k_axpy<kAxpyShape.unroll>, dim3(vector_grid(c, sp.n2, kAxpyShape, false)), dim3(kBlock),
                            0, st, sp, Coef{alpha, nullptr}, x, Coef{beta, nullptr}, y, nullptr);
     } else {
-        hipLaunchKernelGGL(k_axpy_scalar, dim3(scalar_grid(c, n)), dim3(kBlock), 0, st, n, alpha, x, beta, y);
+        launch(c, k_axpy_scalar, dim3(scalar_grid(c, n)), dim3(kBlock), 0, st, n, alpha, x, beta, y);
     }
     return launch_status();
 }
@@ -947,10 +1131,10 @@ int bs_scale(bs_ctx *c, int64_t n, const double *x, const double *d, double *y, 
     int64_t head;
     if (common_head(ptrs, 3, &head)) {
         const Split sp = split_of(n, head);
-        hipLaunchKernelGGL(k_scale<kAxpyShape.unroll>, dim3(vector_grid(c, sp.n2, kAxpyShape, false)), dim3(kBlock),
+        launch(c, k_scale<kAxpyShape.unroll>, dim3(vector_grid(c, sp.n2, kAxpyShape, false)), dim3(kBlock),
                            0, st, sp, x, d, y);
     } else {
-        hipLaunchKernelGGL(k_scale_scalar, dim3(scalar_grid(c, n)), dim3(kBlock), 0, st, n, x, d, y);
+        launch(c, k_scale_scalar, dim3(scalar_grid(c, n)), dim3(kBlock), 0, st, n, x, d, y);
     }
     return launch_status();
 }
@@ -983,17 +1167,14 @@ int bs_cg_update(bs_ctx *c, int64_t n, double alpha, const double *p, const doub
     if (n == 0) return finish_launch(c, 0, rr, false, st);
     const void *ptrs[4] = {p, q, x, r};
     int64_t head;
-    unsigned nb;
     if (common_head(ptrs, 4, &head)) {
         const Split sp = split_of(n, head);
-        nb = vector_grid(c, sp.n2, kCgShape, true);
-        hipLaunchKernelGGL(k_cg_update<kCgShape.unroll>, dim3(nb), dim3(kBlock), 0, st, sp, Coef{alpha, nullptr}, p,
-                           q, x, r, c->partials, nullptr);
-    } else {
-        nb = scalar_grid(c, n);
-        hipLaunchKernelGGL(k_cg_update_scalar, dim3(nb), dim3(kBlock), 0, st, n, alpha, p, q, x, r,
-                           c->partials);
+        launch(c, k_cg_update<kCgShape.unroll>, dim3(vector_grid(c, sp.n2, kCgShape, true)), dim3(kBlock),
+                           0, st, sp, Coef{alpha, nullptr}, p, q, x, r, fin_out(c, rr, false), nullptr);
+        return launch_status();
     }
+    const unsigned nb = scalar_grid(c, n);
+    launch(c, k_cg_update_scalar, dim3(nb), dim3(kBlock), 0, st, n, alpha, p, q, x, r, c->partials);
     if (hipGetLastError() != hipSuccess) return BS_EHIP;
     return finish_launch(c, nb, rr, false, st);
 }
@@ -1010,11 +1191,11 @@ int bs_scatter(bs_ctx *c, int64_t n_local, const int32_t *l2g, const double *v_g
     if (!misaligned(l2g, 8) && !misaligned(v_local, 16)) {
         const int64_t per = 2LL * kBlock * kScatterPairs;
         const int64_t nb = (n_local + per - 1) / per;
-        hipLaunchKernelGGL(k_scatter, dim3((unsigned)nb), dim3(kBlock), 0, st, n_local, l2g, v_global, v_local,
+        launch(c, k_scatter, dim3((unsigned)nb), dim3(kBlock), 0, st, n_local, l2g, v_global, v_local,
                            nullptr);
     } else {
         const int64_t nb = (n_local + kBlock - 1) / kBlock;
-        hipLaunchKernelGGL(k_scatter_scalar, dim3((unsigned)nb), dim3(kBlock), 0, st, n_local, l2g, v_global,
+        launch(c, k_scatter_scalar, dim3((unsigned)nb), dim3(kBlock), 0, st, n_local, l2g, v_global,
                            v_local);
     }
     return launch_status();
@@ -1066,28 +1247,24 @@ int bs_cg_solve(bs_ctx *c, int64_t n_global, int64_t n_local, const int32_t *l2g
     const Split sp = split_of(n_global, 0);
     const double *cgs = c->cgs;
     // rr0 = r.r, history, threshold
+    if (int s = dot_launch(c, n_global, r, r, true, fin_cg(c, kStart, rr_hist, 0, iters, tol * tol), st)) return s;
     unsigned nb;
-    if (int s = dot_stage(c, n_global, r, r, true, st, &nb)) return s;
-    hipLaunchKernelGGL(k_cg_finish, dim3(1), dim3(kFinishBlock), 0, st, c->partials, (int)nb, c->cgs, rr_hist, 0,
-                       iters, tol * tol, (int)kStart);
     const int64_t sc_per = 2LL * kBlock * kScatterPairs;
     const unsigned sc_nb = (unsigned)((n_local + sc_per - 1) / sc_per);
     const unsigned cg_nb = vector_grid(c, sp.n2, kCgShape, true);
     const unsigned ax_nb = vector_grid(c, sp.n2, kAxpyShape, false);
     for (int k = 0; k < iters; ++k) {
         // q = Z^T Z p and p.q in the gather's pass; alpha = rr / p.q
-        hipLaunchKernelGGL(k_scatter, dim3(sc_nb), dim3(kBlock), 0, st, n_local, l2g, p, p_local, cgs);
+        launch(c, k_scatter, dim3(sc_nb), dim3(kBlock), 0, st, n_local, l2g, p, p_local, cgs);
         if (int s = gather_launch(c, n_global, off, ids, p_local, q, block_starts, n_blocks, p, cgs, st, &nb))
             return s;
-        hipLaunchKernelGGL(k_cg_finish, dim3(1), dim3(kFinishBlock), 0, st, c->partials, (int)nb, c->cgs,
+        launch(c, k_cg_finish, dim3(1), dim3(kFinishBlock), 0, st, c->partials, (int)nb, c->cgs,
                            rr_hist, k, iters, 0.0, (int)kSetAlpha);
-        // x += alpha p, r -= alpha q, r.r; beta = rr' / rr
-        hipLaunchKernelGGL(k_cg_update<kCgShape.unroll>, dim3(cg_nb), dim3(kBlock), 0, st, sp,
-                           Coef{0.0, cgs + kAlpha}, p, q, x, r, c->partials, cgs);
-        hipLaunchKernelGGL(k_cg_finish, dim3(1), dim3(kFinishBlock), 0, st, c->partials, (int)cg_nb, c->cgs,
-                           rr_hist, k, iters, 0.0, (int)kSetBeta);
+        // x += alpha p, r -= alpha q, r.r; beta = rr' / rr (the update's last block)
+        launch(c, k_cg_update<kCgShape.unroll>, dim3(cg_nb), dim3(kBlock), 0, st, sp,
+                           Coef{0.0, cgs + kAlpha}, p, q, x, r, fin_cg(c, kSetBeta, rr_hist, k, iters, 0.0), cgs);
         // p = (1 r) + (beta p)
-        hipLaunchKernelGGL(k_axpy<kAxpyShape.unroll>, dim3(ax_nb), dim3(kBlock), 0, st, sp, Coef{1.0, nullptr}, r,
+        launch(c, k_axpy<kAxpyShape.unroll>, dim3(ax_nb), dim3(kBlock), 0, st, sp, Coef{1.0, nullptr}, r,
                            Coef{0.0, cgs + kBeta}, p, cgs);
         if (hipGetLastError() != hipSuccess) return BS_EHIP;
     }

@@ -68,6 +68,21 @@ void bs_ctx_destroy(bs_ctx *ctx);
 /* Device and compute-unit count of a context; NULL outputs are skipped. */
 int bs_ctx_info(const bs_ctx *ctx, int *device, int *cu_count, int *max_partials);
 
+/* Kernel timing, for measuring each operation against the pages' bandwidth
+ * model (arXiv 2009.10917, performance model: time per operation and the
+ * bytes it streams). Arms the context so that the next kernel it launches
+ * (the first, streaming kernel of the next device operation called with it)
+ * records the HIP events `start_event` and `stop_event` (hipEvent_t passed as
+ * void*, created by the caller with timing enabled; either may be NULL) at
+ * that kernel's own start and end, as hipExtLaunchKernel does, so that
+ * hipEventElapsedTime gives the kernel's duration without the queue gaps that
+ * events recorded on the stream around the call include. One-shot: the
+ * launch disarms the context. An operation that enqueues nothing (an error, a
+ * zero-length copy) leaves it armed; NULL, NULL disarms. The caller owns the
+ * events and keeps them alive until they have completed. Errors: BS_EINVAL
+ * (ctx NULL). */
+int bs_ctx_time_next(bs_ctx *ctx, void *start_event, void *stop_event);
+
 /* ------------------------------------------------------------------------
  * BS1 copy (arXiv 2009.10917, BS test list): y[i] = x[i] for 0 <= i < n, a
  * bit copy (NaN payloads and signed zeros kept). x and y are contiguous

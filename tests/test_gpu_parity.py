@@ -170,6 +170,62 @@ def test_reductions_deterministic(env):
     assert len(set(a)) == 1 and len(set(b)) == 1
 
 
+def test_one_kernel_reductions_back_to_back(env):
+    """The reductions finish in the last block to arrive (an atomic ticket,
+    partials through coherent agent-scope accesses). Queue many calls back to
+    back with no synchronisation between them: six input sets of different
+    values, grids of 1 to 512 blocks (one counter, and counters per group of
+    blocks) interleaved so that every call follows one of another size and
+    other values, each result in its own slot. Every result must match the
+    oracle to 1e-12 and repeat bit for bit per input, which fails if a finish
+    read a stale partial (of an earlier call, or from its own XCD's cache) or
+    if a ticket counter was left nonzero."""
+    bs, orc, torch, d = env
+    sizes = [11_390_625, 3_000_001, 700_001, 9_000, 513, 3]
+    vals = [{k: bs_inputs.uniform_pm1(4000 + 8 * i + j, n) for j, k in enumerate("xy")}
+            for i, n in enumerate(sizes)]
+    ref = [{"dot": orc.dot(v["x"], v["y"]), "norm": orc.norm(v["x"])} for v in vals]
+    t = [{k: dev(torch, d, a) for k, a in v.items()} for v in vals]
+    order = [(5 * i + i // 4) % len(sizes) for i in range(240)]
+    out = torch.full((2 * len(order),), float("nan"), dtype=torch.float64, device=d)
+    for i, s in enumerate(order):
+        bs.bs_dot(t[s]["x"], t[s]["y"], out[2 * i:2 * i + 1])
+        bs.bs_norm(t[s]["x"], out[2 * i + 1:2 * i + 2])
+    torch.cuda.synchronize()
+    got = host(out)
+    first = {}
+    for i, s in enumerate(order):
+        for j, k in enumerate(("dot", "norm")):
+            g = got[2 * i + j]
+            assert_rel(g, ref[s][k], f"{k} call {i} size {sizes[s]}")
+            assert first.setdefault((s, k), g) == g, f"{k} call {i} size {sizes[s]} not repeatable"
+
+
+def test_one_kernel_cg_update_back_to_back(env):
+    """As above for the fused update: alpha = 0 keeps x and r, so each call on
+    a set returns that set's r.r; p and q are distinct arrays per set."""
+    bs, orc, torch, d = env
+    sizes = [11_390_625, 2_000_003, 9_000, 3]
+    sets = []
+    for i, n in enumerate(sizes):
+        v = [bs_inputs.uniform_pm1(5000 + 8 * i + j, n) for j in range(4)]
+        sets.append(([dev(torch, d, a) for a in v], orc.dot(v[3], v[3]), v))
+    order = [(3 * i + i // 5) % len(sizes) for i in range(160)]
+    out = torch.full((len(order),), float("nan"), dtype=torch.float64, device=d)
+    for i, s in enumerate(order):
+        p, q, x, r = sets[s][0]
+        bs.bs_cg_update(0.0, p, q, x, r, out[i:i + 1])
+    torch.cuda.synchronize()
+    got = host(out)
+    first = {}
+    for i, s in enumerate(order):
+        assert_rel(got[i], sets[s][1], f"rr call {i} size {sizes[s]}")
+        assert first.setdefault(s, got[i]) == got[i], f"rr call {i} size {sizes[s]} not repeatable"
+    for (tv, _, v) in sets:
+        assert_bits(host(tv[2]), v[2], "x unchanged at alpha 0")
+        assert_bits(host(tv[3]), v[3], "r unchanged at alpha 0")
+
+
 @pytest.mark.parametrize("k", list(range(10, 29)))
 def test_sweep_sizes(env, k):
     """The 2^10 .. 2^28 sweep: every op, whole vectors against the oracle."""
@@ -581,6 +637,45 @@ def test_unstructured_cg_solve(env):
 
 
 # -------------------------------------------------------- launch loop -----
+
+def test_kernel_timing_events(env):
+    """bs_ctx_time_next: the next kernel records the two events at its own
+    start and end. Its duration lies inside what events recorded on the stream
+    around the call measure; an operation that enqueues nothing leaves the
+    context armed; the launch after the timed one does not touch the events;
+    the timed launch computes the same result."""
+    bs, orc, torch, d = env
+    n = 11_390_625
+    v = [bs_inputs.uniform_pm1(6100 + k, n) for k in range(4)]
+    p, q, x, r = (dev(torch, d, a) for a in v)
+    ctx = bs.context()
+    st = torch.cuda.current_stream()
+    k0, k1, s0, s1 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+    for e in (k0, k1):
+        e.record(st)
+    torch.cuda.synchronize()
+    ctx.time_next(k0, k1)
+    empty = torch.empty(0, dtype=torch.float64, device=d)
+    bs.bs_copy(empty, empty)  # enqueues nothing: still armed
+    s0.record(st)
+    rr = bs.bs_cg_update(0.37, p, q, x, r)
+    s1.record(st)
+    torch.cuda.synchronize()
+    kernel_ms, call_ms = k0.elapsed_time(k1), s0.elapsed_time(s1)
+    assert 0.0 < kernel_ms <= call_ms * 1.02 + 1e-3, (kernel_ms, call_ms)
+    ox, orr_, orr = orc.cg_update(0.37, v[0], v[1], v[2], v[3])
+    assert_bits(host(x), ox, "timed cg x")
+    assert_rel(rr.item(), orr, "timed cg rr")
+    # disarmed: a later launch leaves the events as they were
+    bs.bs_dot(p, q)
+    torch.cuda.synchronize()
+    assert k0.elapsed_time(k1) == kernel_ms
+    ctx.time_next(k0, k1)
+    ctx.time_next()  # disarm
+    bs.bs_dot(p, q)
+    torch.cuda.synchronize()
+    assert k0.elapsed_time(k1) == kernel_ms
+
 
 def test_bench_loop_runs_the_operations(env):
     """bs_bench_loop issues the real operations: after a loop over two sets
