@@ -870,13 +870,44 @@ inline bool common_head(const void *const *ptrs, int k, int64_t *head)
     return true;
 }
 
-inline int check_ctx(const bs_ctx *c)
+// Makes a device current for the length of one ABI call and gives the
+// calling thread its previous device back when the call returns.
+class DeviceScope {
+public:
+    DeviceScope() = default;
+    DeviceScope(const DeviceScope &) = delete;
+    DeviceScope &operator=(const DeviceScope &) = delete;
+    ~DeviceScope()
+    {
+        if (switched_) (void)hipSetDevice(prev_);
+    }
+    int enter(int device)
+    {
+        if (hipGetDevice(&prev_) != hipSuccess) return BS_EHIP;
+        if (prev_ != device) {
+            if (hipSetDevice(device) != hipSuccess) return BS_EHIP;
+            switched_ = true;
+        }
+        return BS_OK;
+    }
+    int enter(const bs_ctx *c) { return c ? enter(c->device) : BS_EINVAL; }
+
+private:
+    int prev_ = -1;
+    bool switched_ = false;
+};
+
+// Do the byte ranges [a, a + na) and [b, b + nb) share memory?
+inline bool overlap(const void *a, int64_t na, const void *b, int64_t nb)
 {
-    if (!c) return BS_EINVAL;
-    int cur = -1;
-    if (hipGetDevice(&cur) != hipSuccess) return BS_EHIP;
-    if (cur != c->device && hipSetDevice(c->device) != hipSuccess) return BS_EHIP;
-    return BS_OK;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return na > 0 && nb > 0 && x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
+
+// Two double[n] operands that are the same array or do not meet at all.
+inline bool same_or_apart(const double *a, const double *b, int64_t n)
+{
+    return a == b || !overlap(a, 8 * n, b, 8 * n);
 }
 
 int finish_launch(bs_ctx *c, unsigned nb, double *out, bool take_sqrt, hipStream_t st)
@@ -1018,7 +1049,8 @@ int bs_ctx_create(int device, bs_ctx **out)
     *out = nullptr;
     int ndev = 0;
     if (hipGetDeviceCount(&ndev) != hipSuccess || device < 0 || device >= ndev) return BS_EHIP;
-    if (hipSetDevice(device) != hipSuccess) return BS_EHIP;
+    DeviceScope scope;
+    if (scope.enter(device) != BS_OK) return BS_EHIP;
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus < 1)
         return BS_EHIP;
@@ -1054,7 +1086,8 @@ int bs_ctx_create(int device, bs_ctx **out)
 void bs_ctx_destroy(bs_ctx *c)
 {
     if (!c) return;
-    if (hipSetDevice(c->device) == hipSuccess) {
+    DeviceScope scope;
+    if (scope.enter(c->device) == BS_OK) {
         (void)hipDeviceSynchronize();
         (void)hipFree(c->partials);
         (void)hipFree(c->tickets);
@@ -1082,9 +1115,11 @@ int bs_ctx_info(const bs_ctx *c, int *device, int *cu_count, int *max_partials)
 
 int bs_copy(bs_ctx *c, int64_t n, const double *x, double *y, void *stream)
 {
-    if (int s = check_ctx(c)) return s;
+    DeviceScope scope;
+    if (int s = scope.enter(c)) return s;
     if (n < 0 || (n > 0 && (!x || !y))) return BS_EINVAL;
     if (misaligned(x, 8) || misaligned(y, 8)) return BS_EALIGN;
+    if (!same_or_apart(x, y, n)) return BS_EINVAL;
     // a copy onto itself changes nothing (and keeps the kernel's restrict
     // qualifiers honest)
     if (n == 0 || x == y) return BS_OK;
@@ -1103,10 +1138,12 @@ int bs_copy(bs_ctx *c, int64_t n, const double *x, double *y, void *stream)
 
 int bs_axpy(bs_ctx *c, int64_t n, double alpha, const double *x, double beta, double *y, void *stream)
 {
-    if (int s = check_ctx(c)) return s;
+    DeviceScope scope;
+    if (int s = scope.enter(c)) return s;
     if (n < 0 || (n > 0 && (!x || !y))) return BS_EINVAL;
     if (n == 0) return BS_OK;
     if (misaligned(x, 8) || misaligned(y, 8)) return BS_EALIGN;
+    if (!same_or_apart(x, y, n)) return BS_EINVAL;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const void *ptrs[2] = {x, y};
     int64_t head;
@@ -1122,10 +1159,12 @@ int bs_axpy(bs_ctx *c, int64_t n, double alpha, const double *x, double beta, do
 
 int bs_scale(bs_ctx *c, int64_t n, const double *x, const double *d, double *y, void *stream)
 {
-    if (int s = check_ctx(c)) return s;
+    DeviceScope scope;
+    if (int s = scope.enter(c)) return s;
     if (n < 0 || (n > 0 && (!x || !d || !y))) return BS_EINVAL;
     if (n == 0) return BS_OK;
     if (misaligned(x, 8) || misaligned(d, 8) || misaligned(y, 8)) return BS_EALIGN;
+    if (!same_or_apart(x, y, n) || !same_or_apart(d, y, n)) return BS_EINVAL;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const void *ptrs[3] = {x, d, y};
     int64_t head;
@@ -1141,7 +1180,8 @@ int bs_scale(bs_ctx *c, int64_t n, const double *x, const double *d, double *y, 
 
 int bs_norm(bs_ctx *c, int64_t n, const double *x, double *result, void *stream)
 {
-    if (int s = check_ctx(c)) return s;
+    DeviceScope scope;
+    if (int s = scope.enter(c)) return s;
     if (n < 0 || !result || (n > 0 && !x)) return BS_EINVAL;
     if ((n > 0 && misaligned(x, 8)) || misaligned(result, 8)) return BS_EALIGN;
     return reduce_launch(c, n, x, x, result, true, static_cast<hipStream_t>(stream));
@@ -1149,7 +1189,8 @@ int bs_norm(bs_ctx *c, int64_t n, const double *x, double *result, void *stream)
 
 int bs_dot(bs_ctx *c, int64_t n, const double *x, const double *y, double *result, void *stream)
 {
-    if (int s = check_ctx(c)) return s;
+    DeviceScope scope;
+    if (int s = scope.enter(c)) return s;
     if (n < 0 || !result || (n > 0 && (!x || !y))) return BS_EINVAL;
     if ((n > 0 && (misaligned(x, 8) || misaligned(y, 8))) || misaligned(result, 8)) return BS_EALIGN;
     return reduce_launch(c, n, x, y, result, false, static_cast<hipStream_t>(stream));
@@ -1158,11 +1199,18 @@ int bs_dot(bs_ctx *c, int64_t n, const double *x, const double *y, double *resul
 int bs_cg_update(bs_ctx *c, int64_t n, double alpha, const double *p, const double *q, double *x,
                  double *r, double *rr, void *stream)
 {
-    if (int s = check_ctx(c)) return s;
+    DeviceScope scope;
+    if (int s = scope.enter(c)) return s;
     if (n < 0 || !rr || (n > 0 && (!p || !q || !x || !r))) return BS_EINVAL;
     if ((n > 0 && (misaligned(p, 8) || misaligned(q, 8) || misaligned(x, 8) || misaligned(r, 8))) ||
         misaligned(rr, 8))
         return BS_EALIGN;
+    // x and r are written through restrict pointers: neither may meet the
+    // other or p, q (p and q are only read and may be the same array)
+    const int64_t nbytes = 8 * n;
+    if (overlap(x, nbytes, r, nbytes) || overlap(x, nbytes, p, nbytes) || overlap(x, nbytes, q, nbytes) ||
+        overlap(r, nbytes, p, nbytes) || overlap(r, nbytes, q, nbytes))
+        return BS_EINVAL;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (n == 0) return finish_launch(c, 0, rr, false, st);
     const void *ptrs[4] = {p, q, x, r};
@@ -1182,7 +1230,8 @@ int bs_cg_update(bs_ctx *c, int64_t n, double alpha, const double *p, const doub
 int bs_scatter(bs_ctx *c, int64_t n_local, const int32_t *l2g, const double *v_global, double *v_local,
                void *stream)
 {
-    if (int s = check_ctx(c)) return s;
+    DeviceScope scope;
+    if (int s = scope.enter(c)) return s;
     if (n_local < 0 || (n_local > 0 && (!l2g || !v_global || !v_local))) return BS_EINVAL;
     if (n_local > INT32_MAX) return BS_ERANGE;
     if (n_local == 0) return BS_OK;
@@ -1204,7 +1253,8 @@ int bs_scatter(bs_ctx *c, int64_t n_local, const int32_t *l2g, const double *v_g
 int bs_gather(bs_ctx *c, int64_t n_global, const int32_t *off, const int32_t *ids, const double *v_local,
               double *v_global, const int32_t *block_starts, int64_t n_blocks, void *stream)
 {
-    if (int s = check_ctx(c)) return s;
+    DeviceScope scope;
+    if (int s = scope.enter(c)) return s;
     if (int s = gather_args(c, n_global, off, ids, v_local, v_global, block_starts, n_blocks, false)) return s;
     if (n_global == 0) return BS_OK;
     unsigned nb;
@@ -1216,7 +1266,8 @@ int bs_gather_dot(bs_ctx *c, int64_t n_global, const int32_t *off, const int32_t
                   double *v_global, const int32_t *block_starts, int64_t n_blocks, const double *w,
                   double *result, void *stream)
 {
-    if (int s = check_ctx(c)) return s;
+    DeviceScope scope;
+    if (int s = scope.enter(c)) return s;
     if (!result || (n_global > 0 && !w)) return BS_EINVAL;
     if (int s = gather_args(c, n_global, off, ids, v_local, v_global, block_starts, n_blocks, true)) return s;
     if (misaligned(result, 8) || (n_global > 0 && misaligned(w, 8))) return BS_EALIGN;
@@ -1233,7 +1284,8 @@ int bs_cg_solve(bs_ctx *c, int64_t n_global, int64_t n_local, const int32_t *l2g
                 const int32_t *ids, const int32_t *block_starts, int64_t n_blocks, double *x, double *r,
                 double *p, double *q, double *p_local, int iters, double tol, double *rr_hist, void *stream)
 {
-    if (int s = check_ctx(c)) return s;
+    DeviceScope scope;
+    if (int s = scope.enter(c)) return s;
     if (n_global < 1 || n_local < 1 || iters < 0 || !(tol >= 0.0) || !l2g || !x || !r || !p || !q || !p_local ||
         !rr_hist)
         return BS_EINVAL;
@@ -1243,6 +1295,14 @@ int bs_cg_solve(bs_ctx *c, int64_t n_global, int64_t n_local, const int32_t *l2g
     for (const void *v : vec)
         if (misaligned(v, 16) && v != rr_hist) return BS_EALIGN;
     if (misaligned(rr_hist, 8) || misaligned(l2g, 8)) return BS_EALIGN;
+    {
+        // every vector of the iteration is written at some step: no two may meet
+        const void *arr[5] = {x, r, p, q, p_local};
+        const int64_t len[5] = {8 * n_global, 8 * n_global, 8 * n_global, 8 * n_global, 8 * n_local};
+        for (int i = 0; i < 5; ++i)
+            for (int j = i + 1; j < 5; ++j)
+                if (overlap(arr[i], len[i], arr[j], len[j])) return BS_EINVAL;
+    }
     hipStream_t st = static_cast<hipStream_t>(stream);
     const Split sp = split_of(n_global, 0);
     const double *cgs = c->cgs;

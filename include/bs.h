@@ -27,6 +27,11 @@
  *  - A context owns the reduction scratch of one device. Calls that use the
  *    same context must be ordered (one stream, or explicit dependencies);
  *    concurrent reductions on one context race.
+ *  - A call makes its context's device current while it runs and gives the
+ *    calling thread its previous current device back before it returns.
+ *  - Overlapping operands are checked where the sizes say how far each one
+ *    reaches (the vector operations and the CG iteration): an overlap the
+ *    call does not allow is BS_EINVAL.
  */
 #ifndef BS_H
 #define BS_H
@@ -86,13 +91,15 @@ int bs_ctx_time_next(bs_ctx *ctx, void *start_event, void *stop_event);
 /* ------------------------------------------------------------------------
  * BS1 copy (arXiv 2009.10917, BS test list): y[i] = x[i] for 0 <= i < n, a
  * bit copy (NaN payloads and signed zeros kept). x and y are contiguous
- * double[n]; x == y is allowed, any other overlap is undefined. */
+ * double[n]; x == y is allowed (nothing to do), any other overlap is
+ * BS_EINVAL. */
 int bs_copy(bs_ctx *ctx, int64_t n, const double *x, double *y, void *stream);
 
 /* BS2 AXPY, the CG "vector addition" y = alpha x + beta y (arXiv
  * 2009.10917, CG vector-operation list): y[i] = (alpha*x[i]) + (beta*y[i]),
  * each product rounded, then the sum; bit-exact. y is read also when
- * beta == 0. x, y contiguous double[n]; x == y allowed. */
+ * beta == 0. x, y contiguous double[n]; x == y allowed, any other overlap is
+ * BS_EINVAL. */
 int bs_axpy(bs_ctx *ctx, int64_t n, double alpha, const double *x, double beta,
             double *y, void *stream);
 
@@ -100,7 +107,8 @@ int bs_axpy(bs_ctx *ctx, int64_t n, double alpha, const double *x, double beta,
  * the scaling of a global vector by the inverted (lumped, diagonal) mass
  * matrix (arXiv 1506.05996, coarse-grid correction: y = r / m), the one
  * streaming operation that a lumped-mass / Jacobi step adds to the BS set.
- * x, d, y contiguous double[n]; y == x allowed. Bit-exact. */
+ * x, d, y contiguous double[n]; y may be x or d, any other overlap of y
+ * with them is BS_EINVAL. Bit-exact. */
 int bs_scale(bs_ctx *ctx, int64_t n, const double *x, const double *d, double *y, void *stream);
 
 /* BS3 norm (arXiv 2009.10917, CG vector-operation list and the two-kernel
@@ -121,7 +129,8 @@ int bs_dot(bs_ctx *ctx, int64_t n, const double *x, const double *y, double *res
  * pass, saving a read and a write of r): x[i] = x[i] + (alpha*p[i]);
  * r[i] = r[i] - (alpha*q[i]) (bit-exact), and *rr = sum of the updated r[i]^2
  * into the device double `rr` (reduction guarantees as bs_norm). p, q, x, r
- * contiguous double[n] and pairwise distinct. */
+ * contiguous double[n]. x and r are written: neither may overlap the other,
+ * p or q (BS_EINVAL); p and q are only read and may be the same array. */
 int bs_cg_update(bs_ctx *ctx, int64_t n, double alpha, const double *p, const double *q,
                  double *x, double *r, double *rr, void *stream);
 
@@ -175,8 +184,9 @@ int bs_gather_dot(bs_ctx *ctx, int64_t n_global, const int32_t *off, const int32
  * p0 = r0 (for x0 = 0: r = p = b). rr_hist (device double[iters+1]) receives
  * r.r before the first iteration and after each; once rr <= tol^2 * rr0 (or
  * rr == 0) the remaining iterations do nothing and their entries stay -1.
- * x, r, p, q: distinct device double[n_global]; p_local: device
- * double[n_local]; all 16-byte aligned (BS_EALIGN), l2g 8-byte aligned.
+ * x, r, p, q: device double[n_global]; p_local: device double[n_local];
+ * no two of these five may overlap (BS_EINVAL); all 16-byte aligned
+ * (BS_EALIGN), l2g 8-byte aligned.
  * l2g, off, ids, block_starts as bs_scatter / bs_gather. Uses the context's
  * scratch: one solve at a time per context. */
 int bs_cg_solve(bs_ctx *ctx, int64_t n_global, int64_t n_local, const int32_t *l2g,

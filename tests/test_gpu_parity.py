@@ -417,8 +417,51 @@ def test_errors_enqueue_nothing(env):
     assert L.bs_gather(h, 4, raw, raw, raw, raw, raw, 0, None) == bs.BS_EINVAL
     with pytest.raises(TypeError):
         bs.bs_copy(x.float(), x.float())
+    # operands that overlap where the call does not allow it (8 bytes a double)
+    assert L.bs_copy(h, 4, raw, raw + 8, None) == bs.BS_EINVAL
+    assert L.bs_axpy(h, 4, 1.0, raw + 16, 1.0, raw, None) == bs.BS_EINVAL
+    assert L.bs_scale(h, 4, raw, raw + 40, raw + 32, None) == bs.BS_EINVAL
+    o = raw + 72  # a device double for the residual, apart from the vectors
+    assert L.bs_cg_update(h, 2, 1.0, raw, raw + 16, raw + 32, raw + 32, o, None) == bs.BS_EINVAL  # x == r
+    assert L.bs_cg_update(h, 2, 1.0, raw, raw + 16, raw + 8, raw + 32, o, None) == bs.BS_EINVAL   # x meets p
+    assert L.bs_cg_update(h, 2, 1.0, raw, raw + 16, raw + 32, raw + 24, o, None) == bs.BS_EINVAL  # r meets q
     torch.cuda.synchronize()
     assert torch.count_nonzero(x).item() == 0
+
+
+def test_overlap_rules_of_the_iteration(env):
+    """The CG iteration rejects overlapping vectors before it enqueues
+    anything; the fused update takes p and q as one array."""
+    bs, orc, torch, d = env
+    L, h = bs._lib(), bs.context().handle
+    E, N = 2, 2
+    l2g = bs.bs_mesh_box_l2g(E, E, E, N)
+    ng = bs.bs_mesh_box_count(E, E, E, N)[1]
+    nl = l2g.size
+    off, ids = bs.bs_index_g2l(l2g, ng)
+    dl2g, doff, dids = dev(torch, d, l2g), dev(torch, d, off), dev(torch, d, ids)
+    s = ng + (ng & 1)  # doubles per vector slot, keeping every slot 16-byte aligned
+    buf = torch.zeros(4 * s + nl, dtype=torch.float64, device=d)  # x, r, p, q, p_local back to back
+    base, hist = buf.data_ptr(), torch.zeros(4, dtype=torch.float64, device=d)
+    x, r, p, q, pl = (base + 8 * s * k for k in range(5))
+
+    def solve(*vecs):
+        return L.bs_cg_solve(h, ng, nl, dl2g.data_ptr(), doff.data_ptr(), dids.data_ptr(), None, 0, *vecs, 3,
+                             0.0, hist.data_ptr(), None)
+
+    assert solve(x, r, p, q, q) == bs.BS_EINVAL       # p_local on q
+    assert solve(x, x, p, q, pl) == bs.BS_EINVAL      # x == r
+    assert solve(x, r, p, p + 16, pl) == bs.BS_EINVAL  # q shifted into p
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(buf).item() == 0 and torch.count_nonzero(hist).item() == 0
+    # p == q is allowed: both are only read
+    v = bs_inputs.vectors("box8_N3", 4099)
+    pp, xx, rr_ = dev(torch, d, v["p"]), dev(torch, d, v["x"]), dev(torch, d, v["r"])
+    got = bs.bs_cg_update(0.37, pp, pp, xx, rr_).item()
+    wx, wr, wrr = orc.cg_update(0.37, v["p"], v["p"], v["x"], v["r"])
+    assert_bits(host(xx), wx, "x with p == q")
+    assert_bits(host(rr_), wr, "r with p == q")
+    assert_rel(got, wrr, "rr with p == q")
 
 
 # ------------------------------------------------- CG streaming sequence ----
