@@ -230,13 +230,11 @@ def traffic_for(kernels):
     return total
 
 
-def cpu_baseline(mesh_host, budget_s=12.0):
-    """The oracle, as it stands, on the same step (host arrays), repeated
-    until about budget_s seconds; returns GB/s over the algorithmic bytes."""
+def _oracle_steps(h, budget_s):
+    """Full oracle steps on the host arrays until about budget_s seconds;
+    returns (steps, seconds)."""
     import oracle
-    h = mesh_host
     n = h["ng"]
-    nb = sum(op_bytes(op, n, h["nl"], n) for op in OPS)
     reps, t = 0, 0.0
     while t < budget_s and reps < 1000:
         t0 = time.perf_counter()
@@ -249,6 +247,24 @@ def cpu_baseline(mesh_host, budget_s=12.0):
         oracle.gather(h["l2g"], h["vl"], n)
         t += time.perf_counter() - t0
         reps += 1
+    return reps, t
+
+
+def cpu_baseline(mesh_host, budget_s=12.0, budget_1_thread_s=4.0):
+    """The oracle, as it stands, on the same step (host arrays), repeated
+    until about budget_s seconds on all of the host's OpenMP threads, then
+    for about budget_1_thread_s on one; GB/s over the algorithmic bytes."""
+    import oracle
+    h = mesh_host
+    n = h["ng"]
+    nb = sum(op_bytes(op, n, h["nl"], n) for op in OPS)
+    threads = oracle.threads()
+    reps, t = _oracle_steps(h, budget_s)
+    oracle.set_threads(1)
+    try:
+        reps1, t1 = _oracle_steps(h, budget_1_thread_s)
+    finally:
+        oracle.set_threads(threads)
     model = "unknown CPU"
     try:
         for line in open("/proc/cpuinfo"):
@@ -257,10 +273,12 @@ def cpu_baseline(mesh_host, budget_s=12.0):
                 break
     except OSError:
         pass
-    return {"value": round(nb * reps / t / 1e9, 3), "unit": "GB/s", "cores": oracle.threads(),
+    return {"value": round(nb * reps / t / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{reps} full step(s) of the 32^3 order-7 mesh (all 7 ops, oracle tables), "
-                      f"{t:.1f} s of wall time on {oracle.threads()} OpenMP threads of {model}"}
+                      f"{t:.1f} s of wall time on {threads} OpenMP threads of {model}",
+            "value_1_thread": round(nb * reps1 / t1 / 1e9, 3),
+            "sample_1_thread": f"{reps1} full step(s), {t1:.1f} s of wall time on 1 thread"}
 
 
 def sweep(bs, torch, dev, reps_min=100, min_seconds=0.05):

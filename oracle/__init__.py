@@ -54,6 +54,8 @@ def lib():
         L = ctypes.CDLL(_LIB)
         L.or_threads.argtypes = []
         L.or_threads.restype = ctypes.c_int
+        L.or_set_threads.argtypes = [ctypes.c_int]
+        L.or_set_threads.restype = None
         L.or_copy.argtypes = [_c_int64, _ptr, _ptr]
         L.or_copy.restype = None
         L.or_axpy.argtypes = [_c_int64, _c_double, _ptr, _c_double, _ptr]
@@ -105,6 +107,11 @@ def _nptr(a):
 def threads():
     """OpenMP threads the oracle's parallel loops use."""
     return lib().or_threads()
+
+
+def set_threads(n):
+    """Use n OpenMP threads from now on (results do not depend on it)."""
+    lib().or_set_threads(int(n))
 
 
 # --------------------------------------------------------------- BS1..BS7 --

@@ -50,6 +50,15 @@ int or_threads(void)
     return omp_get_max_threads();
 }
 
+/* Sets how many threads the parallel loops below use from now on (n > 0;
+   other values change nothing): the baseline is timed on all cores and on
+   one. No result depends on it: the reductions combine fixed chunks in a
+   fixed order. */
+void or_set_threads(int n)
+{
+    if (n > 0) omp_set_num_threads(n);
+}
+
 /* ---------------------------------------------------------------- BS1 --- */
 /* y = x as a bit copy: NaN payloads and signed zeros are preserved. */
 void or_copy(int64_t n, const double *x, double *y)
