@@ -81,6 +81,26 @@ def load_resources(path):
     return out
 
 
+def load_in_step(path, before, kernel, after):
+    """Durations (ns) of the launches of `kernel` that a trace shows between a
+    launch of `before` and one of `after` on the same queue, in start order:
+    the launches inside the timed steps of a benchmark whose step runs the
+    kernels in a fixed sequence, without the per-operation loops around them."""
+    rows = []
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            rows.append((row.get("Queue_Id", ""), int(row["Start_Timestamp"]), int(row["End_Timestamp"]),
+                         short_name(row["Kernel_Name"])))
+    rows.sort()
+    out = []
+    for i in range(1, len(rows) - 1):
+        q, t0, t1, k = rows[i]
+        if k == kernel and rows[i - 1][0] == q == rows[i + 1][0] and rows[i - 1][3] == before \
+                and rows[i + 1][3] == after:
+            out.append(t1 - t0)
+    return out
+
+
 REMARK_KEYS = {"TotalSGPRs": "sgpr", "VGPRs": "vgpr", "AGPRs": "agpr", "ScratchSize [bytes/lane]": "scratch_per_lane",
                "Occupancy [waves/SIMD]": "occupancy", "SGPRs Spill": "sgpr_spill", "VGPRs Spill": "vgpr_spill",
                "LDS Size [bytes/block]": "lds_static"}
@@ -116,9 +136,11 @@ def _cxxfilt(name):
 
 
 def summarize(stats_csv, fetch_csv, write_csv, copy_kernel, copy_doubles, source=None, ops=None, trace_csv=None,
-              remarks=None, calibration=None):
+              remarks=None, calibration=None, in_step=None):
     """calibration: (fetch_scale, write_scale) to use when the run has no copy
-    kernel of its own (taken from an earlier summary's calibration block)."""
+    kernel of its own (taken from an earlier summary's calibration block).
+    in_step: {name: (before, kernel, after)}, averaged over the trace's
+    launches of kernel between those two neighbours (needs trace_csv)."""
     stats = load_stats(stats_csv) if stats_csv else {}
     res = load_resources(trace_csv) if trace_csv else {}
     rem = load_remarks(remarks) if remarks else {}
@@ -163,6 +185,12 @@ def summarize(stats_csv, fetch_csv, write_csv, copy_kernel, copy_doubles, source
         for name, ks in ops.items():
             if all(k in kernels and "avg_ns" in kernels[k] for k in ks):
                 out["ops"][name] = {"kernels": ks, "avg_ns": sum(kernels[k]["avg_ns"] for k in ks)}
+    if in_step and trace_csv:
+        out["in_step"] = {}
+        for name, (before, kernel, after) in in_step.items():
+            d = load_in_step(trace_csv, before, kernel, after)
+            out["in_step"][name] = {"before": before, "kernel": kernel, "after": after, "launches": len(d),
+                                    "avg_ns": statistics.mean(d) if d else None}
     if source:
         out["kernel_source_sha256"] = hashlib.sha256(open(source, "rb").read()).hexdigest()
     return out
@@ -204,6 +232,13 @@ def to_markdown(summary, title, commands):
         lines += ["", "| operation | kernels | avg us (sum) |", "|---|---|---|"]
         for name, d in summary["ops"].items():
             lines.append(f"| {name} | {' + '.join('`%s`' % k for k in d['kernels'])} | {d['avg_ns'] / 1e3:.2f} |")
+    if summary.get("in_step"):
+        lines += ["", "Launches inside the timed steps (the trace's launches of the kernel between the two "
+                  "neighbours the step runs it between):", "",
+                  "| operation | kernel | between | launches | avg us |", "|---|---|---|---|---|"]
+        for name, d in summary["in_step"].items():
+            avg = f"{d['avg_ns'] / 1e3:.2f}" if d["avg_ns"] is not None else ""
+            lines.append(f"| {name} | `{d['kernel']}` | `{d['before']}` and `{d['after']}` | {d['launches']} | {avg} |")
     if "kernel_source_sha256" in summary:
         lines += ["", f"Kernel source sha256: `{summary['kernel_source_sha256']}`"]
     return "\n".join(lines) + "\n"
@@ -223,6 +258,8 @@ def main(argv=None):
     ap.add_argument("--command", action="append", default=[])
     ap.add_argument("--op", action="append", default=[], help="NAME=kernel1+kernel2 (summed averages)")
     ap.add_argument("--calibration", help="summary JSON whose counter calibration to reuse")
+    ap.add_argument("--in-step", action="append", default=[],
+                    help="NAME=before|kernel|after: average of kernel's launches between those neighbours")
     ap.add_argument("--json")
     ap.add_argument("--md")
     a = ap.parse_args(argv)
@@ -231,8 +268,15 @@ def main(argv=None):
     if a.calibration:
         c = json.load(open(a.calibration))["calibration"]
         cal = (c["fetch_scale"], c["write_scale"])
+    in_step = {}
+    for o in a.in_step:
+        name, spec = o.split("=", 1)
+        parts = spec.split("|")
+        if len(parts) != 3:
+            ap.error(f"--in-step {o!r}: expected NAME=before|kernel|after")
+        in_step[name] = tuple(p.strip() for p in parts)
     s = summarize(a.stats, a.fetch, a.write, a.copy_kernel, a.copy_doubles, a.source, ops, a.trace, a.remarks,
-                  cal)
+                  cal, in_step)
     if a.json:
         with open(a.json, "w") as f:
             json.dump(s, f, indent=1)

@@ -92,3 +92,31 @@ def test_reused_calibration(tmp_path):
     assert s["calibration"]["reused"]
     assert s["kernels"]["k_scatter"]["hbm_bytes_per_launch"] == pytest.approx(30 * 1024 * 2 + 20 * 1024)
     assert "reused" in profiling.to_markdown(s, "t", [])
+
+
+def test_in_step_launches(tmp_path):
+    """Only the launches between the step's neighbours are averaged; the
+    per-operation loop's back-to-back launches of the same kernel are not."""
+    rows = []
+    t = 0
+
+    def launch(name, dur, queue=1):
+        nonlocal t
+        rows.append([queue, t, t + dur, f"void (anonymous namespace)::{name}(x)"])
+        t += dur + 10
+
+    for _ in range(3):          # the per-operation loop: the kernel back to back
+        launch("k_cg_update<4>", 1000)
+    for d in (1200, 1400):      # two steps: dot, update, scatter
+        launch("k_dot<4, false>", 500)
+        launch("k_cg_update<4>", d)
+        launch("k_scatter", 700)
+    launch("k_dot<4, false>", 500, queue=2)  # a neighbour on another queue does not count
+    launch("k_cg_update<4>", 9999)
+    launch("k_scatter", 700)
+    with open(tmp_path / "trace.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Queue_Id", "Start_Timestamp", "End_Timestamp", "Kernel_Name"])
+        w.writerows(rows)
+    d = profiling.load_in_step(tmp_path / "trace.csv", "k_dot<4, false>", "k_cg_update<4>", "k_scatter")
+    assert d == [1200, 1400]
