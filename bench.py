@@ -5,8 +5,12 @@ mesh (N_G = 11,390,625 global nodes, N_L = 16,777,216 local entries), fp64:
 BS1 copy, BS2 AXPY (alpha 0.37, beta 1), BS3 norm, BS4 dot and BS5 fused CG
 update on global-length vectors, BS7 scatter through I_l->g and BS6 gather
 through the CSR form of I_g->l. Each operation works on arrays of its own,
-so between two touches of the same array the step streams ~1.6 GB through
-the 256 MB last-level cache: every operation reads cold data from HBM.
+and consecutive steps run on 12 different sets of all these arrays, so
+between two touches of the same array about 21 GB stream through the 256 MB
+last-level cache: every operation reads cold data from HBM. (With a single
+set, arrays read with the ordinary cache policy, such as the gather's v_L,
+were found to survive in that cache from one step to the next, past the
+non-temporal traffic of the other operations.)
 
 The figure of merit is effective bandwidth, algorithmic bytes over time
 ("Portable high-order finite element kernels I", arXiv 2009.10917, where
@@ -488,7 +492,6 @@ def main():
     name, E, N = "box32_N7", 32, 7
     mesh = Mesh(bs, torch, dev, name, E, N, gather_lds=(args.gather == "lds"), layout=args.layout)
     stream = torch.cuda.current_stream().cuda_stream
-    launch = mesh.launchers(bs, stream)
     step_bytes = sum(mesh.bytes(op) for op in OPS)
 
     # per operation: back-to-back launches over ROT sets of distinct arrays
@@ -497,17 +500,19 @@ def main():
     trials = time_ops_native(bs, sets, OPS, args.per_op_reps, trials=args.trials)
     per_op = {op: float(np.median(t)) for op, t in trials.items()}
     dom = max(OPS, key=lambda op: per_op[op])
-    del sets
     # the same loops on one set: operands that fit stay in the 256 MB cache
     hot = time_ops_native(bs, [mesh], OPS, args.per_op_reps)
-    torch.cuda.empty_cache()
 
-    # timed region: host clock around K steps; in every step the dominant
-    # kernel records a pair of HIP events at its own start and end (the
-    # library launches it with them, as armed by time_next), on its stream
-    for _ in range(args.warmup):
+    # timed region: host clock around K steps; step k runs on array set
+    # k mod ROT, so that every operation of a step reads data no step has
+    # touched for ROT - 1 steps (about 21 GB of traffic): cold in the cache,
+    # as in the per-operation loops. In every step the dominant kernel
+    # records a pair of HIP events at its own start and end (the library
+    # launches it with them, as armed by time_next), on its stream.
+    step_launch = [m.launchers(bs, stream) for m in sets]
+    for w in range(args.warmup):
         for op in OPS:
-            launch[op]()
+            step_launch[w % len(sets)][op]()
     cur = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for a, b in ev:  # create them
@@ -516,12 +521,15 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
+        run = step_launch[k % len(sets)]
         for op in OPS:
             if op == dom:
                 ctx.time_next(*ev[k])
-            launch[op]()
+            run[op]()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    del step_launch, sets
+    torch.cuda.empty_cache()
     dom_live = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
     ms_step = dt / args.steps * 1e3
     value = step_bytes / (dt / args.steps) / 1e9
@@ -567,7 +575,8 @@ def main():
         "config": {"workload": "box mesh 32^3 elements, order N=7, lexicographic numbering; "
                                "all 7 BS ops per step", "elements": E ** 3, "order": N,
                    "n_global": mesh.ng, "n_local": mesh.nl, "step_bytes": step_bytes,
-                   "gather_kernel": args.gather, "layout": args.layout, "cu_count": ctx.info()["cu_count"]},
+                   "gather_kernel": args.gather, "layout": args.layout, "step_sets": args.rotate,
+                   "cu_count": ctx.info()["cu_count"]},
         "pct_peak": round(100 * value / PEAK_GBPS, 1),
         "per_op": ops_out,
         "runtime_copy_GBps": round(rt_copy, 1),
@@ -584,12 +593,10 @@ def main():
     if args.sweep:
         extra["sweep"] = sweep(bs, torch, dev)
     if args.workloads:
-        launch = None
         extra["workloads"] = workloads(bs, torch, dev, args.gather == "lds")
 
     if not args.no_cpu_baseline:
         import oracle
-        launch = None
         host = {"ng": mesh.ng, "nl": mesh.nl}
         v = bs_inputs.vectors(name, mesh.ng)
         host.update(v)
