@@ -188,7 +188,12 @@ int bs_gather_dot(bs_ctx *ctx, int64_t n_global, const int32_t *off, const int32
  * no two of these five may overlap (BS_EINVAL); all 16-byte aligned
  * (BS_EALIGN), l2g 8-byte aligned.
  * l2g, off, ids, block_starts as bs_scatter / bs_gather. Uses the context's
- * scratch: one solve at a time per context. */
+ * scratch: one solve at a time per context. When the iteration's vectors and
+ * tables together fit in the device's 256 MB last-level cache, its kernels
+ * read and write them with the ordinary cache policy so that each kernel
+ * finds what the previous one left there; larger working sets stream
+ * non-temporally, like the standalone operations. The results are the same
+ * bits either way. */
 int bs_cg_solve(bs_ctx *ctx, int64_t n_global, int64_t n_local, const int32_t *l2g,
                 const int32_t *off, const int32_t *ids, const int32_t *block_starts,
                 int64_t n_blocks, double *x, double *r, double *p, double *q, double *p_local,
