@@ -501,7 +501,7 @@ def main():
     trials = time_ops_native(bs, sets, OPS, args.per_op_reps, trials=args.trials)
     per_op = {op: float(np.median(t)) for op, t in trials.items()}
     dom = max(OPS, key=lambda op: per_op[op])
-    # the same loops on one set: operands that fit stay in the 256 MB cache
+    # the same loops on one set (only ordinary-policy reads can hit the 256 MB cache)
     hot = time_ops_native(bs, [mesh], OPS, args.per_op_reps)
 
     # timed region: host clock around K steps; step k runs on array set
@@ -584,9 +584,10 @@ def main():
         "copy_ceiling_GBps": round(ceiling, 1) if ceiling else None,
         "per_op_note": f"us: median of {args.trials} trials of {args.per_op_reps} back-to-back launches (issued by "
                        f"the library's C++ loop, host-timed) over {args.rotate} rotated array sets (cold); us_best: "
-                       "best trial; hot_us: one set, operands "
-                       "cache-resident where they fit; pct_copy_ceiling: against copy_ceiling_GBps, the "
-                       "library's copy of 2^28 doubles",
+                       "best trial; hot_us: the same loop on one set (the vector kernels' non-temporal "
+                       "accesses do not allocate in the last-level cache, so only the scatter's and gather's "
+                       "ordinary-policy reads can find cached data); pct_copy_ceiling: against "
+                       "copy_ceiling_GBps, the library's copy of 2^28 doubles",
         "roofline": roofline,
     }
 
