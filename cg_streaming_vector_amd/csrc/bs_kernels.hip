@@ -25,7 +25,10 @@
 //    per node with all of its loads issued up front.
 // Built from the same kernels: the pointwise scale y = x / d of the lumped
 // mass, and a device-resident CG iteration on Z^T Z whose scalars (alpha,
-// beta, |r|^2, a done flag) stay in device memory between launches.
+// beta, |r|^2, a done flag) stay in device memory between launches. When the
+// iteration's vectors and tables fit in the 256 MB last-level cache, it runs
+// twins of its kernels that use the ordinary cache policy instead of
+// non-temporal accesses, so each kernel finds the previous one's data there.
 // No MFMA: nothing here is a dense contraction.
 //
 // Bit-exactness: the file is compiled with -ffp-contract=off and the pragma
