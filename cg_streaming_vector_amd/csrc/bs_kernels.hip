@@ -256,14 +256,27 @@ __device__ __forceinline__ bool last_arrival(double part, const Fin &f)
 
 // In the finishing block (all kBlock threads): the partials summed in a fixed
 // order (each lane a strided run, the wave butterfly, the waves in order),
-// then stored as the mode says.
+// then stored as the mode says. A lane issues its loads kFinishLoads at a
+// time before adding them, so a grid of up to kFinishLoads * kBlock blocks
+// costs one round trip to memory, not one per kBlock partials; the lane adds
+// its partials in the same order either way (a +0.0 past the end changes no
+// bits: the running sum starts at +0.0 and never becomes -0.0).
+constexpr int kFinishLoads = 4;
 __device__ __forceinline__ void finish_last(const Fin &f)
 {
     __shared__ double wsum[kBlock / kWave];
     const unsigned nb = gridDim.x;
     double s = 0.0;
-    for (unsigned i = threadIdx.x; i < nb; i += kBlock)
-        s += __hip_atomic_load(&f.partials[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (unsigned i0 = threadIdx.x; i0 < nb; i0 += kFinishLoads * kBlock) {
+        double v[kFinishLoads];
+#pragma unroll
+        for (int k = 0; k < kFinishLoads; ++k) {
+            const unsigned i = i0 + k * kBlock;
+            v[k] = i < nb ? __hip_atomic_load(&f.partials[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.0;
+        }
+#pragma unroll
+        for (int k = 0; k < kFinishLoads; ++k) s += v[k];
+    }
     s = wave_sum(s);
     if ((threadIdx.x & (kWave - 1)) == 0) wsum[threadIdx.x / kWave] = s;
     if (f.mode == kFinCg && f.cg == kStart) cg_hist_init(f.hist, f.iters, kBlock);
