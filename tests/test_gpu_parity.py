@@ -586,6 +586,38 @@ def test_cg_solve_matches_oracle(env, name):
         assert np.allclose(host(x), b / m, rtol=1e-12, atol=1e-14)
 
 
+def test_cg_solve_cache_resident_slab(env):
+    """The CG iteration on one GPU's share of the 32^3 order-7 box (a
+    32 x 32 x 4-element slab, 1.47M nodes): its vectors and tables, about
+    87 MB, fit in the last-level cache, so the iteration runs the
+    cache-keeping kernels, at full tiles and some two thousand gather blocks.
+    Residual history and x against the oracle's CG, as for the boxes."""
+    bs, orc, torch, d = env
+    E, N = 32, 7
+    l2g = bs.bs_mesh_box_l2g(E, E, 4, N)
+    ng = bs.bs_mesh_box_count(E, E, 4, N)[1]
+    off, ids = bs.bs_index_g2l(l2g, ng)
+    ol2g, ong = orc.mesh_box(E, E, 4, N)
+    assert ong == ng and np.array_equal(l2g, ol2g)
+    working_set = 8 * (4 * ng + l2g.size) + 4 * (2 * l2g.size + ng + 1)
+    assert working_set < 256 << 20
+    b = bs_inputs.uniform_pm1(bs_inputs.base_seed("slab32x32x4_N7") + 3, ng)
+    ox, _, ohist = orc.cg_sequence(ol2g, ng, b, 4)
+    plan = dev(torch, d, bs.bs_gather_plan(off, 1024))
+    dl2g, doff, dids = dev(torch, d, l2g), dev(torch, d, off), dev(torch, d, ids)
+    x = torch.zeros(ng, dtype=torch.float64, device=d)
+    r, p = dev(torch, d, b), dev(torch, d, b)
+    q = torch.empty(ng, dtype=torch.float64, device=d)
+    pl = torch.empty(l2g.size, dtype=torch.float64, device=d)
+    h = host(bs.bs_cg_solve(dl2g, doff, dids, x, r, p, q, pl, 4, 0.0, plan))
+    assert_rel(h[0], ohist[0], "rr0")
+    assert_rel(h[1], ohist[1], "rr1")
+    assert math.sqrt(h[4] / h[0]) < 1e-13
+    m = np.diff(off)
+    assert np.allclose(host(x), ox, rtol=1e-12, atol=1e-14)
+    assert np.allclose(host(x), b / m, rtol=1e-12, atol=1e-14)
+
+
 def test_cg_solve_early_exit_and_zero_iterations(env):
     """A tolerance stops the iteration on the device: later history entries
     stay -1 and x no longer changes; iters = 0 only measures rr0."""
