@@ -10,8 +10,8 @@
 //    across the 64-lane wavefront;
 //  - grid-stride loops over a grid sized from the compute-unit count, with
 //    the unroll depth and blocks per CU chosen per operation by measurement;
-//  - reductions: per-lane accumulation, a wavefront butterfly through
-//    cross-lane shuffles, the block's wavefronts through LDS, one partial per
+//  - reductions: per-lane accumulation, a wavefront sum by DPP lane moves,
+//    the block's wavefronts through LDS, one partial per
 //    block; the last block to arrive (an atomic ticket) sums the partials in
 //    a fixed order in the same kernel. No atomics touch the values, so
 //    results repeat bit for bit;
@@ -130,12 +130,31 @@ __device__ __forceinline__ void st2(d2 *p, d2 v) { stp<kStream>(p, v); }
 
 // ------------------------------------------------------------ reductions --
 
-// Butterfly over the 64 lanes of a wavefront; every lane ends with the sum.
+// A double moved across lanes by one DPP control (0 where the control
+// leaves a lane without a source or the row mask leaves it unwritten).
+template <int kCtrl, int kRowMask = 0xf>
+__device__ __forceinline__ double dpp_move(double v)
+{
+    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), kCtrl, kRowMask, 0xf, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), kCtrl, kRowMask, 0xf, false);
+    return __hiloint2double(hi, lo);
+}
+
+// Sum over the 64 lanes of a wavefront by DPP (no LDS): pairs, quads, 8 and
+// 16 lanes within each row of 16, then the rows by broadcasts of lanes 15 and
+// 31; lane 63 ends with the total, which every lane then reads. The order of
+// the additions is fixed, so the bits repeat.
 __device__ __forceinline__ double wave_sum(double v)
 {
-#pragma unroll
-    for (int m = kWave / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-    return v;
+    v += dpp_move<0xb1>(v);        // quad_perm [1,0,3,2]
+    v += dpp_move<0x4e>(v);        // quad_perm [2,3,0,1]
+    v += dpp_move<0x124>(v);       // row_ror:4
+    v += dpp_move<0x128>(v);       // row_ror:8
+    v += dpp_move<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+    v += dpp_move<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+    const int lo = __builtin_amdgcn_readlane(__double2loint(v), 63);
+    const int hi = __builtin_amdgcn_readlane(__double2hiint(v), 63);
+    return __hiloint2double(hi, lo);
 }
 
 // Sum over the block; the result is valid in thread 0.
@@ -255,7 +274,7 @@ __device__ __forceinline__ bool last_arrival(double part, const Fin &f)
 }
 
 // In the finishing block (all kBlock threads): the partials summed in a fixed
-// order (each lane a strided run, the wave butterfly, the waves in order),
+// order (each lane a strided run, the wave's DPP sum, the waves in order),
 // then stored as the mode says. A lane issues its loads kFinishLoads at a
 // time before adding them, so a grid of up to kFinishLoads * kBlock blocks
 // costs one round trip to memory, not one per kBlock partials; the lane adds
@@ -304,7 +323,7 @@ __device__ __forceinline__ void finish_block(double part, const Fin &f)
 // kernel boundary makes the partials visible across XCDs.
 //
 // finish_sum: the sum over one kFinishBlock-thread block, valid in thread 0:
-// each lane a strided run in index order, then the wave butterfly, then the
+// each lane a strided run in index order, then the wave's DPP sum, then the
 // 16 wave sums in order. A lane issues its loads kFinishBatch at a time, all
 // before the adds: the gather's folded dot leaves one partial per plan block
 // (55297 at 24^3 order 15), and one load in flight per lane made this sum
