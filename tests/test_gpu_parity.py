@@ -618,6 +618,36 @@ def test_cg_solve_cache_resident_slab(env):
     assert np.allclose(host(x), b / m, rtol=1e-12, atol=1e-14)
 
 
+@pytest.mark.parametrize("ex,ey,ez,N", [(1, 1, 1, 1), (3, 2, 5, 2), (7, 4, 3, 5), (10, 11, 9, 4), (13, 9, 12, 6),
+                                         (24, 24, 24, 7)])
+def test_cg_solve_boxes(env, ex, ey, ez, N):
+    """The device CG on boxes of several shapes and orders, on both sides of
+    the cache-resident switch (the last box's vectors and tables exceed the
+    256 MB last-level cache, the others fit): residual history and x against
+    the oracle's CG, with and without a gather plan."""
+    bs, orc, torch, d = env
+    l2g = bs.bs_mesh_box_l2g(ex, ey, ez, N)
+    ng = bs.bs_mesh_box_count(ex, ey, ez, N)[1]
+    off, ids = bs.bs_index_g2l(l2g, ng)
+    ol2g, _ = orc.mesh_box(ex, ey, ez, N)
+    b = bs_inputs.uniform_pm1(9000 + ex * 1000 + ey * 100 + ez * 10 + N, ng)
+    m = np.diff(off)
+    iters = len(np.unique(m))
+    ox, _, ohist = orc.cg_sequence(ol2g, ng, b, iters)
+    dl2g, doff, dids = dev(torch, d, l2g), dev(torch, d, off), dev(torch, d, ids)
+    q = torch.empty(ng, dtype=torch.float64, device=d)
+    pl = torch.empty(l2g.size, dtype=torch.float64, device=d)
+    for plan in (None, dev(torch, d, bs.bs_gather_plan(off, 1024))):
+        x = torch.zeros(ng, dtype=torch.float64, device=d)
+        r, p = dev(torch, d, b), dev(torch, d, b)
+        h = host(bs.bs_cg_solve(dl2g, doff, dids, x, r, p, q, pl, iters, 0.0, plan))
+        assert_rel(h[0], ohist[0], "rr0")
+        assert abs(h[1] - ohist[1]) <= 1e-12 * ohist[0]
+        assert math.sqrt(h[iters] / h[0]) < 1e-12
+        assert np.allclose(host(x), ox, rtol=1e-11, atol=1e-13)
+        assert np.allclose(host(x), b / m, rtol=1e-11, atol=1e-13)
+
+
 def test_cg_solve_early_exit_and_zero_iterations(env):
     """A tolerance stops the iteration on the device: later history entries
     stay -1 and x no longer changes; iters = 0 only measures rr0."""
