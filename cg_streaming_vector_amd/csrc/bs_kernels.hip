@@ -70,10 +70,12 @@ struct Coef {
 __device__ __forceinline__ bool skipped(const double *cgs) { return cgs && cgs[kDone] != 0.0; }
 
 // Launch shape of a vector kernel: 16-byte loads per lane per array per loop
-// iteration, and blocks per compute unit (0: one tile per block, no loop).
+// iteration, blocks per compute unit (0: one tile per block, no loop) and
+// threads per block.
 struct VecShape {
     int unroll;
     int blocks_per_cu;
+    int threads = kBlock;
 };
 // Chosen by sweeps of unroll {1,2,4,8,16} x blocks/CU {flat,1,2,4,8,16} x block
 // size {256,512,1024} x non-temporal on/off x occupancy hint on cold data
@@ -82,7 +84,7 @@ struct VecShape {
 // streams narrow, which the multi-stream kernels prefer.
 constexpr VecShape kCopyShape{1, 0};
 constexpr VecShape kAxpyShape{1, 2};
-constexpr VecShape kDotShape{4, 1};
+constexpr VecShape kDotShape{2, 1, 512};
 constexpr VecShape kNormShape{4, 2};
 constexpr VecShape kCgShape{4, 1};
 
@@ -158,9 +160,10 @@ __device__ __forceinline__ double wave_sum(double v)
 }
 
 // Sum over the block; the result is valid in thread 0.
+template <int NT = kBlock>
 __device__ __forceinline__ double block_sum(double v)
 {
-    __shared__ double wsum[kBlock / kWave];
+    __shared__ double wsum[NT / kWave];
     v = wave_sum(v);
     const int w = threadIdx.x / kWave;
     if ((threadIdx.x & (kWave - 1)) == 0) wsum[w] = v;
@@ -168,7 +171,7 @@ __device__ __forceinline__ double block_sum(double v)
     double s = 0.0;
     if (threadIdx.x == 0) {
 #pragma unroll
-        for (int i = 0; i < kBlock / kWave; ++i) s += wsum[i];
+        for (int i = 0; i < NT / kWave; ++i) s += wsum[i];
     }
     return s;
 }
@@ -281,16 +284,17 @@ __device__ __forceinline__ bool last_arrival(double part, const Fin &f)
 // its partials in the same order either way (a +0.0 past the end changes no
 // bits: the running sum starts at +0.0 and never becomes -0.0).
 constexpr int kFinishLoads = 4;
+template <int NT = kBlock>
 __device__ __forceinline__ void finish_last(const Fin &f)
 {
-    __shared__ double wsum[kBlock / kWave];
+    __shared__ double wsum[NT / kWave];
     const unsigned nb = gridDim.x;
     double s = 0.0;
-    for (unsigned i0 = threadIdx.x; i0 < nb; i0 += kFinishLoads * kBlock) {
+    for (unsigned i0 = threadIdx.x; i0 < nb; i0 += kFinishLoads * NT) {
         double v[kFinishLoads];
 #pragma unroll
         for (int k = 0; k < kFinishLoads; ++k) {
-            const unsigned i = i0 + k * kBlock;
+            const unsigned i = i0 + k * NT;
             v[k] = i < nb ? __hip_atomic_load(&f.partials[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.0;
         }
 #pragma unroll
@@ -298,12 +302,12 @@ __device__ __forceinline__ void finish_last(const Fin &f)
     }
     s = wave_sum(s);
     if ((threadIdx.x & (kWave - 1)) == 0) wsum[threadIdx.x / kWave] = s;
-    if (f.mode == kFinCg && f.cg == kStart) cg_hist_init(f.hist, f.iters, kBlock);
+    if (f.mode == kFinCg && f.cg == kStart) cg_hist_init(f.hist, f.iters, NT);
     __syncthreads();
     if (threadIdx.x != 0) return;
     double t = 0.0;
 #pragma unroll
-    for (int i = 0; i < kBlock / kWave; ++i) t += wsum[i];
+    for (int i = 0; i < NT / kWave; ++i) t += wsum[i];
     if (f.mode == kFinOut)
         *f.out = t;
     else if (f.mode == kFinSqrt)
@@ -312,9 +316,10 @@ __device__ __forceinline__ void finish_last(const Fin &f)
         cg_apply(f.cg, t, f.cgs, f.hist, f.k, f.tol2);
 }
 
+template <int NT = kBlock>
 __device__ __forceinline__ void finish_block(double part, const Fin &f)
 {
-    if (last_arrival(part, f)) finish_last(f);
+    if (last_arrival(part, f)) finish_last<NT>(f);
 }
 
 // Two-kernel reductions (the gather's folded dot, whose grid has one block
@@ -517,24 +522,27 @@ __global__ __launch_bounds__(kBlock) void k_scale_scalar(int64_t n, const double
 
 // ------------------------------------------------- BS3 norm, BS4 dot ----
 // First stage of both: with kSquare it sums x[i]^2 (y is ignored). The grid
-// holds one or two blocks per CU, so the kernel never needs more than two
-// waves per SIMD: the occupancy hint lets the compiler keep every load of a
-// lane in flight instead of trading registers for waves it will not get.
-template <int U, bool kSquare>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_dot(
+// holds two 256-thread blocks (norm) or one 512-thread block (dot) per CU,
+// so the kernel never needs more than two waves per SIMD: the occupancy hint
+// lets the compiler keep every load of a lane in flight instead of trading
+// registers for waves it will not get. The dot's single block per CU carries
+// the same bytes in flight as two smaller ones with half the partials, and
+// measured 0.4 us faster at 11.4M doubles; the norm measured no gain from it.
+template <int U, bool kSquare, int NT>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_dot(
     Split sp, const double *__restrict__ x, const double *__restrict__ y, Fin f)
 {
     const d2 *xv = reinterpret_cast<const d2 *>(x + sp.head);
     const d2 *yv = reinterpret_cast<const d2 *>((kSquare ? x : y) + sp.head);
-    const int64_t stride = (int64_t)gridDim.x * kBlock * U;
-    int64_t i = (int64_t)blockIdx.x * kBlock * U + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * NT * U;
+    int64_t i = (int64_t)blockIdx.x * NT * U + threadIdx.x;
     double acc0 = 0.0, acc1 = 0.0;
-    for (; i + (U - 1) * kBlock < sp.n2; i += stride) {
+    for (; i + (U - 1) * NT < sp.n2; i += stride) {
         d2 vx[U], vy[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            vx[u] = ld2(xv + i + u * kBlock);
-            vy[u] = kSquare ? vx[u] : ld2(yv + i + u * kBlock);
+            vx[u] = ld2(xv + i + u * NT);
+            vy[u] = kSquare ? vx[u] : ld2(yv + i + u * NT);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -544,7 +552,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 2))) 
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int64_t k = i + u * kBlock;
+        const int64_t k = i + u * NT;
         if (k < sp.n2) {
             const d2 a = ld2(xv + k);
             const d2 b = kSquare ? a : ld2(yv + k);
@@ -557,7 +565,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 2))) 
         if (sp.head) acc0 = __builtin_fma(x[0], yy[0], acc0);
         if (sp.tail >= 0) acc1 = __builtin_fma(x[sp.tail], yy[sp.tail], acc1);
     }
-    finish_block(block_sum(acc0 + acc1), f);
+    finish_block<NT>(block_sum<NT>(acc0 + acc1), f);
 }
 
 // -------------------------------------------------- BS5 fused CG update ----
@@ -978,7 +986,7 @@ void launch(bs_ctx *c, K kernel, dim3 grid, dim3 block, unsigned shmem, hipStrea
 // (the kernels loop over whatever a smaller grid leaves).
 inline unsigned vector_grid(const bs_ctx *c, int64_t n2, VecShape s, bool reduction)
 {
-    const int64_t per = (int64_t)kBlock * s.unroll;
+    const int64_t per = (int64_t)s.threads * s.unroll;
     int64_t g = (n2 + per - 1) / per;
     if (s.blocks_per_cu > 0 && g > (int64_t)c->cus * s.blocks_per_cu) g = (int64_t)c->cus * s.blocks_per_cu;
     const int64_t cap = reduction ? (int64_t)c->max_partials : (int64_t)1 << 22;
@@ -1098,11 +1106,11 @@ int dot_launch(bs_ctx *c, int64_t n, const double *x, const double *y, bool squa
     if (common_head(ptrs, 2, &head)) {
         const Split sp = split_of(n, head);
         if (square)
-            launch(c, (k_dot<kNormShape.unroll, true>), dim3(vector_grid(c, sp.n2, kNormShape, true)),
-                               dim3(kBlock), 0, st, sp, x, x, f);
+            launch(c, (k_dot<kNormShape.unroll, true, kNormShape.threads>), dim3(vector_grid(c, sp.n2, kNormShape, true)),
+                               dim3(kNormShape.threads), 0, st, sp, x, x, f);
         else
-            launch(c, (k_dot<kDotShape.unroll, false>), dim3(vector_grid(c, sp.n2, kDotShape, true)),
-                               dim3(kBlock), 0, st, sp, x, y, f);
+            launch(c, (k_dot<kDotShape.unroll, false, kDotShape.threads>), dim3(vector_grid(c, sp.n2, kDotShape, true)),
+                               dim3(kDotShape.threads), 0, st, sp, x, y, f);
         return launch_status();
     }
     const unsigned nb = scalar_grid(c, n);
