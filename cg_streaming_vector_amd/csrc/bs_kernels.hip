@@ -90,8 +90,8 @@ constexpr VecShape kCopyShape{1, 0};
 constexpr VecShape kAxpyShape{1, 2};
 constexpr VecShape kDotShape{2, 1, 512};
 constexpr VecShape kNormShape{4, 2};
-constexpr VecShape kCgShape{2, 1};  // two passes: unroll of the x pass (the r pass: kCgRUnroll)
-constexpr int kCgRUnroll = 4;
+constexpr VecShape kCgShape{1, 1, 512};  // two passes: unroll of the x pass (the r pass: kCgRUnroll)
+constexpr int kCgRUnroll = 2;
 constexpr VecShape kCgOnePassShape{4, 1};
 
 constexpr int kScatterPairs = 32;  // index pairs per lane in the scatter kernel
@@ -594,6 +594,7 @@ __device__ __forceinline__ d2 minus_aq(d2 r, double a, d2 q)
 
 // Scalar head and tail elements of the update (one thread), and the block's
 // share of r.r to the reduction.
+template <int NT = kBlock>
 __device__ __forceinline__ void cg_update_finish(Split sp, double a, const double *p, const double *q, double *x,
                                                  double *r, double acc0, double acc1, const Fin &f)
 {
@@ -612,7 +613,7 @@ __device__ __forceinline__ void cg_update_finish(Split sp, double a, const doubl
             acc1 = __builtin_fma(nr, nr, acc1);
         }
     }
-    finish_block(block_sum(acc0 + acc1), f);
+    finish_block<NT>(block_sum<NT>(acc0 + acc1), f);
 }
 
 // Two forms of the update, the same bits either way. p, q, x and r are
@@ -627,8 +628,10 @@ __device__ __forceinline__ void cg_update_finish(Split sp, double a, const doubl
 // streams open (two reads, one write) instead of six, which this memory system
 // serves faster when all four arrays come from HBM: 86.4 against 88.7 us at
 // 11.4M doubles, the same bytes. The x pass loads U1 pairs per array per lane
-// and loop, the r pass U2.
-template <int U1, int U2, int P>
+// and loop, the r pass U2. One 512-thread block per CU (two waves per SIMD)
+// at unroll 1 and 2 took it to 85.4 us; 256 threads at unroll 2 and 4 keep
+// the same bytes in flight with half the waves.
+template <int U1, int U2, int NT, int P>
 __device__ __forceinline__ void cg_update_two_pass(Split sp, Coef ca, const double *__restrict__ p,
                                                    const double *__restrict__ q, double *__restrict__ x,
                                                    double *__restrict__ r, const Fin &f, const double *cgs)
@@ -640,46 +643,46 @@ __device__ __forceinline__ void cg_update_two_pass(Split sp, Coef ca, const doub
     d2 *xv = reinterpret_cast<d2 *>(x + sp.head);
     d2 *rv = reinterpret_cast<d2 *>(r + sp.head);
     {
-        const int64_t stride = (int64_t)gridDim.x * kBlock * U1;
-        int64_t i = (int64_t)blockIdx.x * kBlock * U1 + threadIdx.x;
-        for (; i + (U1 - 1) * kBlock < sp.n2; i += stride) {
+        const int64_t stride = (int64_t)gridDim.x * NT * U1;
+        int64_t i = (int64_t)blockIdx.x * NT * U1 + threadIdx.x;
+        for (; i + (U1 - 1) * NT < sp.n2; i += stride) {
             d2 vp[U1], vx[U1];
 #pragma unroll
             for (int u = 0; u < U1; ++u) {
-                vp[u] = ldp<P>(pv + i + u * kBlock);
-                vx[u] = ldp<P>(xv + i + u * kBlock);
+                vp[u] = ldp<P>(pv + i + u * NT);
+                vx[u] = ldp<P>(xv + i + u * NT);
             }
 #pragma unroll
-            for (int u = 0; u < U1; ++u) stp<P>(xv + i + u * kBlock, plus_ap(vx[u], a, vp[u]));
+            for (int u = 0; u < U1; ++u) stp<P>(xv + i + u * NT, plus_ap(vx[u], a, vp[u]));
         }
 #pragma unroll
         for (int u = 0; u < U1; ++u) {
-            const int64_t k = i + u * kBlock;
+            const int64_t k = i + u * NT;
             if (k < sp.n2) stp<P>(xv + k, plus_ap(ldp<P>(xv + k), a, ldp<P>(pv + k)));
         }
     }
     double acc0 = 0.0, acc1 = 0.0;
     {
-        const int64_t stride = (int64_t)gridDim.x * kBlock * U2;
-        int64_t i = (int64_t)blockIdx.x * kBlock * U2 + threadIdx.x;
-        for (; i + (U2 - 1) * kBlock < sp.n2; i += stride) {
+        const int64_t stride = (int64_t)gridDim.x * NT * U2;
+        int64_t i = (int64_t)blockIdx.x * NT * U2 + threadIdx.x;
+        for (; i + (U2 - 1) * NT < sp.n2; i += stride) {
             d2 vq[U2], vr[U2];
 #pragma unroll
             for (int u = 0; u < U2; ++u) {
-                vq[u] = ldp<P>(qv + i + u * kBlock);
-                vr[u] = ldp<P>(rv + i + u * kBlock);
+                vq[u] = ldp<P>(qv + i + u * NT);
+                vr[u] = ldp<P>(rv + i + u * NT);
             }
 #pragma unroll
             for (int u = 0; u < U2; ++u) {
                 const d2 nr = minus_aq(vr[u], a, vq[u]);
-                stp<P>(rv + i + u * kBlock, nr);
+                stp<P>(rv + i + u * NT, nr);
                 acc0 = __builtin_fma(nr.x, nr.x, acc0);
                 acc1 = __builtin_fma(nr.y, nr.y, acc1);
             }
         }
 #pragma unroll
         for (int u = 0; u < U2; ++u) {
-            const int64_t k = i + u * kBlock;
+            const int64_t k = i + u * NT;
             if (k < sp.n2) {
                 const d2 nr = minus_aq(ldp<P>(rv + k), a, ldp<P>(qv + k));
                 stp<P>(rv + k, nr);
@@ -688,7 +691,7 @@ __device__ __forceinline__ void cg_update_two_pass(Split sp, Coef ca, const doub
             }
         }
     }
-    cg_update_finish(sp, a, p, q, x, r, acc0, acc1, f);
+    cg_update_finish<NT>(sp, a, p, q, x, r, acc0, acc1, f);
 }
 
 // One pass over all four arrays, U pairs of each per lane and loop. Inside a
@@ -742,21 +745,21 @@ __device__ __forceinline__ void cg_update_one_pass(Split sp, Coef ca, const doub
     cg_update_finish(sp, a, p, q, x, r, acc0, acc1, f);
 }
 
-template <int U1, int U2>
-__global__ __launch_bounds__(kBlock) void k_cg_update(Split sp, Coef ca, const double *__restrict__ p,
-                                                      const double *__restrict__ q, double *__restrict__ x,
-                                                      double *__restrict__ r, Fin f, const double *cgs)
+template <int U1, int U2, int NT>
+__global__ __launch_bounds__(NT) void k_cg_update(Split sp, Coef ca, const double *__restrict__ p,
+                                                  const double *__restrict__ q, double *__restrict__ x,
+                                                  double *__restrict__ r, Fin f, const double *cgs)
 {
-    cg_update_two_pass<U1, U2, kStream>(sp, ca, p, q, x, r, f, cgs);
+    cg_update_two_pass<U1, U2, NT, kStream>(sp, ca, p, q, x, r, f, cgs);
 }
 
 // The same with the cache-keeping policy, for the CG iteration.
-template <int U1, int U2>
-__global__ __launch_bounds__(kBlock) void k_cg_update_keep(Split sp, Coef ca, const double *__restrict__ p,
-                                                           const double *__restrict__ q, double *__restrict__ x,
-                                                           double *__restrict__ r, Fin f, const double *cgs)
+template <int U1, int U2, int NT>
+__global__ __launch_bounds__(NT) void k_cg_update_keep(Split sp, Coef ca, const double *__restrict__ p,
+                                                       const double *__restrict__ q, double *__restrict__ x,
+                                                       double *__restrict__ r, Fin f, const double *cgs)
 {
-    cg_update_two_pass<U1, U2, kKeep>(sp, ca, p, q, x, r, f, cgs);
+    cg_update_two_pass<U1, U2, NT, kKeep>(sp, ca, p, q, x, r, f, cgs);
 }
 
 // One pass, non-temporal: the CG iteration's update when its vectors do not
@@ -1476,7 +1479,8 @@ int bs_cg_update(bs_ctx *c, int64_t n, double alpha, const double *p, const doub
     int64_t head;
     if (common_head(ptrs, 4, &head)) {
         const Split sp = split_of(n, head);
-        launch(c, k_cg_update<kCgShape.unroll, kCgRUnroll>, dim3(vector_grid(c, sp.n2, kCgShape, true)), dim3(kBlock),
+        launch(c, k_cg_update<kCgShape.unroll, kCgRUnroll, kCgShape.threads>,
+               dim3(vector_grid(c, sp.n2, kCgShape, true)), dim3(kCgShape.threads),
                            0, st, sp, Coef{alpha, nullptr}, p, q, x, r, fin_out(c, rr, false), nullptr);
         return launch_status();
     }
@@ -1596,7 +1600,8 @@ int bs_cg_solve(bs_ctx *c, int64_t n_global, int64_t n_local, const int32_t *l2g
         // Two passes when the iteration is cache-resident; otherwise one pass,
         // which overlaps the cached part of p (left by the scatter) with HBM.
         if (keep)
-            launch(c, k_cg_update_keep<kCgShape.unroll, kCgRUnroll>, dim3(cg_nb), dim3(kBlock), 0, st, sp,
+            launch(c, k_cg_update_keep<kCgShape.unroll, kCgRUnroll, kCgShape.threads>, dim3(cg_nb),
+                   dim3(kCgShape.threads), 0, st, sp,
                    Coef{0.0, cgs + kAlpha}, p, q, x, r, fin_cg(c, kSetBeta, rr_hist, k, iters, 0.0), cgs);
         else
             launch(c, k_cg_update_one_pass<kCgOnePassShape.unroll>, dim3(cg1_nb), dim3(kBlock), 0, st, sp,
