@@ -51,7 +51,7 @@ PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 METRIC = "effective GB/s and % of HBM peak per BS op (fp64, N=7 hex mesh, 1 GPU)"
 OPS = ["copy", "axpy", "norm", "dot", "cg_update", "scatter", "gather"]
 KERNEL_NAME = {  # op -> its kernels as rocprofv3 names them (namespace and arguments stripped)
-    "copy": ["k_copy<1>"], "axpy": ["k_axpy<1>"], "norm": ["k_dot<4, true, 256>"],
+    "copy": ["k_copy<1, 768>"], "axpy": ["k_axpy<1>"], "norm": ["k_dot<4, true, 256>"],
     "dot": ["k_dot<2, false, 512>"], "cg_update": ["k_cg_update<1, 2, 512>"],
     "scatter": ["k_scatter"], "gather": ["k_gather_plan<false>"],
 }

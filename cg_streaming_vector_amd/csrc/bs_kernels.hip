@@ -85,8 +85,14 @@ struct VecShape {
 // size {256,512,1024} x non-temporal on/off x occupancy hint on cold data
 // (vectors of 11.4M and 67M doubles, buffers rotated through > 2 GB so no
 // operand is cache-resident). Fewer blocks keep the lockstep window of all
-// streams narrow, which the multi-stream kernels prefer.
-constexpr VecShape kCopyShape{1, 0};
+// streams narrow, which the multi-stream kernels prefer. The copy's flat
+// tiles of 768 threads (12 KB per array) beat every other tile of 256-1024
+// threads up to 2^25 pairs (28.6 against 30.3 us at 11.4M doubles, 114.1
+// against 117.0 us at 47M) and tie at 2^25 pairs; beyond that 256-thread
+// tiles are faster (by 0.8% at 2^27 doubles, 2.1% at 2^28).
+constexpr VecShape kCopyShape{1, 0, 768};
+constexpr VecShape kCopyLargeShape{1, 0, 256};
+constexpr int64_t kCopyLargePairs = 1LL << 25;  // pairs above which kCopyLargeShape runs
 constexpr VecShape kAxpyShape{1, 2};
 constexpr VecShape kDotShape{2, 1, 512};
 constexpr VecShape kNormShape{4, 2};
@@ -406,24 +412,24 @@ __host__ __device__ inline Split split_of(int64_t n, int64_t head)
 }
 
 // ------------------------------------------------------------ BS1 copy ----
-template <int U>
-__global__ __launch_bounds__(kBlock) void k_copy(Split sp, const double *__restrict__ x,
+template <int U, int NT>
+__global__ __launch_bounds__(NT) void k_copy(Split sp, const double *__restrict__ x,
                                                  double *__restrict__ y)
 {
     const d2 *xv = reinterpret_cast<const d2 *>(x + sp.head);
     d2 *yv = reinterpret_cast<d2 *>(y + sp.head);
-    const int64_t stride = (int64_t)gridDim.x * kBlock * U;
-    int64_t i = (int64_t)blockIdx.x * kBlock * U + threadIdx.x;
-    for (; i + (U - 1) * kBlock < sp.n2; i += stride) {
+    const int64_t stride = (int64_t)gridDim.x * NT * U;
+    int64_t i = (int64_t)blockIdx.x * NT * U + threadIdx.x;
+    for (; i + (U - 1) * NT < sp.n2; i += stride) {
         d2 v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) v[u] = ld2(xv + i + u * kBlock);
+        for (int u = 0; u < U; ++u) v[u] = ld2(xv + i + u * NT);
 #pragma unroll
-        for (int u = 0; u < U; ++u) st2(yv + i + u * kBlock, v[u]);
+        for (int u = 0; u < U; ++u) st2(yv + i + u * NT, v[u]);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
-        if (i + u * kBlock < sp.n2) st2(yv + i + u * kBlock, ld2(xv + i + u * kBlock));
+        if (i + u * NT < sp.n2) st2(yv + i + u * NT, ld2(xv + i + u * NT));
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         if (sp.head) y[0] = x[0];
         if (sp.tail >= 0) y[sp.tail] = x[sp.tail];
@@ -1390,8 +1396,13 @@ int bs_copy(bs_ctx *c, int64_t n, const double *x, double *y, void *stream)
     int64_t head;
     if (common_head(ptrs, 2, &head)) {
         const Split sp = split_of(n, head);
-        launch(c, k_copy<kCopyShape.unroll>, dim3(vector_grid(c, sp.n2, kCopyShape, false)), dim3(kBlock),
-                           0, st, sp, x, y);
+        if (sp.n2 <= kCopyLargePairs)
+            launch(c, k_copy<kCopyShape.unroll, kCopyShape.threads>, dim3(vector_grid(c, sp.n2, kCopyShape, false)),
+                   dim3(kCopyShape.threads), 0, st, sp, x, y);
+        else
+            launch(c, k_copy<kCopyLargeShape.unroll, kCopyLargeShape.threads>,
+                   dim3(vector_grid(c, sp.n2, kCopyLargeShape, false)), dim3(kCopyLargeShape.threads), 0, st, sp, x,
+                   y);
     } else {
         launch(c, k_copy_scalar, dim3(scalar_grid(c, n)), dim3(kBlock), 0, st, n, x, y);
     }

@@ -13,7 +13,7 @@ counter reports half the bytes of the copy and the write counter all of them.
 
 Usage:
   python -m cg_streaming_vector_amd.profiling --stats S.csv --fetch F.csv \\
-      --write W.csv --copy-kernel 'k_copy<1>' --copy-doubles 11390625 \\
+      --write W.csv --copy-kernel 'k_copy<1, 768>' --copy-doubles 11390625 \\
       --source cg_streaming_vector_amd/csrc/bs_kernels.hip --json out.json --md out.md
 """
 from __future__ import annotations
@@ -251,7 +251,7 @@ def main(argv=None):
     ap.add_argument("--remarks", help="hipcc -Rpass-analysis=kernel-resource-usage output: registers, occupancy")
     ap.add_argument("--fetch")
     ap.add_argument("--write")
-    ap.add_argument("--copy-kernel", default="k_copy<1>")
+    ap.add_argument("--copy-kernel", default="k_copy<1, 768>")
     ap.add_argument("--copy-doubles", type=int, default=11390625)
     ap.add_argument("--source")
     ap.add_argument("--title", default="BS kernels")
