@@ -32,7 +32,9 @@
 // beta, |r|^2, a done flag) stay in device memory between launches. When the
 // iteration's vectors and tables fit in the 256 MB last-level cache, it runs
 // twins of its kernels that use the ordinary cache policy instead of
-// non-temporal accesses, so each kernel finds the previous one's data there.
+// non-temporal accesses, so each kernel finds the previous one's data there;
+// above that, while r and p alone fit, the update passes them on to the
+// direction update through the cache.
 // No MFMA: nothing here is a dense contraction.
 //
 // Bit-exactness: the file is compiled with -ffp-contract=off and the pragma
@@ -105,6 +107,7 @@ constexpr int kScatterPairs = 32;  // index pairs per lane in the scatter kernel
 // 256 MB): a CG iteration whose working set fits uses the cache-keeping
 // kernels.
 constexpr int64_t kCacheResidentBytes = 256LL << 20;
+constexpr int64_t kHandoffBytes = 210LL << 20;  // r and p of a CG iteration passed on in the cache
 constexpr int kGatherCap = 1024;   // CSR entries and rows a gather block stages in LDS
 constexpr int kGatherRowM = 4;     // entries per row loaded up front (row kernel)
 constexpr int kGatherRowR = 2;     // rows per lane (row kernel)
@@ -700,12 +703,13 @@ __device__ __forceinline__ void cg_update_two_pass(Split sp, Coef ca, const doub
     cg_update_finish<NT>(sp, a, p, q, x, r, acc0, acc1, f);
 }
 
-// One pass over all four arrays, U pairs of each per lane and loop. Inside a
-// CG iteration p arrives partly in the last-level cache (the scatter has just
+// One pass over all four arrays, U pairs of each per lane and loop; PP is the
+// policy of the loads of p, PR of the stores of r, P of the other streams.
+// Inside a CG iteration p arrives partly in the last-level cache (the scatter has just
 // read it with the ordinary policy), and one pass overlaps those hits with the
 // HBM streams of q, x and r: 80.9 against 85.9 us for the two passes at
 // 11.4M doubles, 353.7 against 361.2 us at 47M.
-template <int U, int P>
+template <int U, int P, int PP = P, int PR = P>
 __device__ __forceinline__ void cg_update_one_pass(Split sp, Coef ca, const double *__restrict__ p,
                                                    const double *__restrict__ q, double *__restrict__ x,
                                                    double *__restrict__ r, const Fin &f, const double *cgs)
@@ -723,7 +727,7 @@ __device__ __forceinline__ void cg_update_one_pass(Split sp, Coef ca, const doub
         d2 vp[U], vq[U], vx[U], vr[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            vp[u] = ldp<P>(pv + i + u * kBlock);
+            vp[u] = ldp<PP>(pv + i + u * kBlock);
             vq[u] = ldp<P>(qv + i + u * kBlock);
             vx[u] = ldp<P>(xv + i + u * kBlock);
             vr[u] = ldp<P>(rv + i + u * kBlock);
@@ -732,7 +736,7 @@ __device__ __forceinline__ void cg_update_one_pass(Split sp, Coef ca, const doub
         for (int u = 0; u < U; ++u) {
             const d2 nr = minus_aq(vr[u], a, vq[u]);
             stp<P>(xv + i + u * kBlock, plus_ap(vx[u], a, vp[u]));
-            stp<P>(rv + i + u * kBlock, nr);
+            stp<PR>(rv + i + u * kBlock, nr);
             acc0 = __builtin_fma(nr.x, nr.x, acc0);
             acc1 = __builtin_fma(nr.y, nr.y, acc1);
         }
@@ -742,8 +746,8 @@ __device__ __forceinline__ void cg_update_one_pass(Split sp, Coef ca, const doub
         const int64_t k = i + u * kBlock;
         if (k < sp.n2) {
             const d2 nr = minus_aq(ldp<P>(rv + k), a, ldp<P>(qv + k));
-            stp<P>(xv + k, plus_ap(ldp<P>(xv + k), a, ldp<P>(pv + k)));
-            stp<P>(rv + k, nr);
+            stp<P>(xv + k, plus_ap(ldp<P>(xv + k), a, ldp<PP>(pv + k)));
+            stp<PR>(rv + k, nr);
             acc0 = __builtin_fma(nr.x, nr.x, acc0);
             acc1 = __builtin_fma(nr.y, nr.y, acc1);
         }
@@ -777,6 +781,19 @@ __global__ __launch_bounds__(kBlock) void k_cg_update_one_pass(Split sp, Coef ca
                                                                Fin f, const double *cgs)
 {
     cg_update_one_pass<U, kStream>(sp, ca, p, q, x, r, f, cgs);
+}
+
+// The same, for a CG iteration whose vectors do not fit in the last-level
+// cache but whose r and p do: p is read and r stored with the ordinary
+// policy, so the direction update p = r + beta p that follows finds both
+// there.
+template <int U>
+__global__ __launch_bounds__(kBlock) void k_cg_update_handoff(Split sp, Coef ca, const double *__restrict__ p,
+                                                              const double *__restrict__ q,
+                                                              double *__restrict__ x, double *__restrict__ r,
+                                                              Fin f, const double *cgs)
+{
+    cg_update_one_pass<U, kStream, kKeep, kKeep>(sp, ca, p, q, x, r, f, cgs);
 }
 
 // --------------------------------------------------------- BS7 scatter ----
@@ -1597,6 +1614,10 @@ int bs_cg_solve(bs_ctx *c, int64_t n_global, int64_t n_local, const int32_t *l2g
     const int64_t working_set = 8 * (4 * n_global + n_local) + 4 * (2 * n_local + n_global + 1) +
                                 (block_starts ? 4 * (n_blocks + 1) : 0);
     const bool keep = working_set <= kCacheResidentBytes;
+    // Otherwise, while r and p alone fit, the update hands them to the
+    // direction update through the cache (1-3% per iteration at 24^3-32^3,
+    // order 7).
+    const bool handoff = !keep && 16 * n_global <= kHandoffBytes;
     for (int k = 0; k < iters; ++k) {
         // q = Z^T Z p and p.q in the gather's pass; alpha = rr / p.q
         if (keep)
@@ -1614,11 +1635,14 @@ int bs_cg_solve(bs_ctx *c, int64_t n_global, int64_t n_local, const int32_t *l2g
             launch(c, k_cg_update_keep<kCgShape.unroll, kCgRUnroll, kCgShape.threads>, dim3(cg_nb),
                    dim3(kCgShape.threads), 0, st, sp,
                    Coef{0.0, cgs + kAlpha}, p, q, x, r, fin_cg(c, kSetBeta, rr_hist, k, iters, 0.0), cgs);
+        else if (handoff)
+            launch(c, k_cg_update_handoff<kCgOnePassShape.unroll>, dim3(cg1_nb), dim3(kBlock), 0, st, sp,
+                   Coef{0.0, cgs + kAlpha}, p, q, x, r, fin_cg(c, kSetBeta, rr_hist, k, iters, 0.0), cgs);
         else
             launch(c, k_cg_update_one_pass<kCgOnePassShape.unroll>, dim3(cg1_nb), dim3(kBlock), 0, st, sp,
                    Coef{0.0, cgs + kAlpha}, p, q, x, r, fin_cg(c, kSetBeta, rr_hist, k, iters, 0.0), cgs);
         // p = (1 r) + (beta p)
-        if (keep)
+        if (keep || handoff)
             launch(c, k_axpy_keep<kAxpyShape.unroll>, dim3(ax_nb), dim3(kBlock), 0, st, sp, Coef{1.0, nullptr}, r,
                    Coef{0.0, cgs + kBeta}, p, cgs);
         else

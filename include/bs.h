@@ -192,8 +192,10 @@ int bs_gather_dot(bs_ctx *ctx, int64_t n_global, const int32_t *off, const int32
  * tables together fit in the device's 256 MB last-level cache, its kernels
  * read and write them with the ordinary cache policy so that each kernel
  * finds what the previous one left there; larger working sets stream
- * non-temporally, like the standalone operations. The results are the same
- * bits either way. */
+ * non-temporally, like the standalone operations, except that while r and p
+ * alone fit (16 n_global bytes up to 210 MB) the update passes them to the
+ * direction update p = r + beta p through the cache. The results are the
+ * same bits either way. */
 int bs_cg_solve(bs_ctx *ctx, int64_t n_global, int64_t n_local, const int32_t *l2g,
                 const int32_t *off, const int32_t *ids, const int32_t *block_starts,
                 int64_t n_blocks, double *x, double *r, double *p, double *q, double *p_local,

@@ -619,12 +619,14 @@ def test_cg_solve_cache_resident_slab(env):
 
 
 @pytest.mark.parametrize("ex,ey,ez,N", [(1, 1, 1, 1), (3, 2, 5, 2), (7, 4, 3, 5), (10, 11, 9, 4), (13, 9, 12, 6),
-                                         (24, 24, 24, 7)])
+                                         (24, 24, 24, 7), (24, 24, 24, 10)])
 def test_cg_solve_boxes(env, ex, ey, ez, N):
-    """The device CG on boxes of several shapes and orders, on both sides of
-    the cache-resident switch (the last box's vectors and tables exceed the
-    256 MB last-level cache, the others fit): residual history and x against
-    the oracle's CG, with and without a gather plan."""
+    """The device CG on boxes of several shapes and orders, in all three of
+    its cache regimes: the first boxes fit the 256 MB last-level cache whole;
+    at 24^3 order 7 only r and p fit (77 MB), which the update hands to the
+    direction update through the cache; at 24^3 order 10 (14.0M global
+    nodes) r and p take 224 MB and every stream is non-temporal. Residual
+    history and x against the oracle's CG, with and without a gather plan."""
     bs, orc, torch, d = env
     l2g = bs.bs_mesh_box_l2g(ex, ey, ez, N)
     ng = bs.bs_mesh_box_count(ex, ey, ez, N)[1]
