@@ -705,10 +705,10 @@ __device__ __forceinline__ void cg_update_two_pass(Split sp, Coef ca, const doub
 
 // One pass over all four arrays, U pairs of each per lane and loop; PP is the
 // policy of the loads of p, PR of the stores of r, P of the other streams.
-// Inside a CG iteration p arrives partly in the last-level cache (the scatter has just
-// read it with the ordinary policy), and one pass overlaps those hits with the
-// HBM streams of q, x and r: 80.9 against 85.9 us for the two passes at
-// 11.4M doubles, 353.7 against 361.2 us at 47M.
+// Inside a CG iteration p arrives partly in the last-level cache (the scatter
+// has just read it with the ordinary policy), and one pass overlaps those hits
+// with the HBM streams of q, x and r: 80.9 against 85.9 us for the two passes
+// at 11.4M doubles, 353.7 against 361.2 us at 47M.
 template <int U, int P, int PP = P, int PR = P>
 __device__ __forceinline__ void cg_update_one_pass(Split sp, Coef ca, const double *__restrict__ p,
                                                    const double *__restrict__ q, double *__restrict__ x,
@@ -1228,7 +1228,7 @@ int finish_two_stage(bs_ctx *c, unsigned nb, const Fin &f, hipStream_t st)
 {
     if (f.mode == kFinCg) {
         launch(c, k_cg_finish, dim3(1), dim3(kFinishBlock), 0, st, c->partials, (int)nb, c->cgs, f.hist,
-                           f.k, f.iters, f.tol2, f.cg);
+               f.k, f.iters, f.tol2, f.cg);
         return launch_status();
     }
     return finish_launch(c, nb, f.out, f.mode == kFinSqrt, st);
@@ -1242,11 +1242,11 @@ int dot_launch(bs_ctx *c, int64_t n, const double *x, const double *y, bool squa
     if (common_head(ptrs, 2, &head)) {
         const Split sp = split_of(n, head);
         if (square)
-            launch(c, (k_dot<kNormShape.unroll, true, kNormShape.threads>), dim3(vector_grid(c, sp.n2, kNormShape, true)),
-                               dim3(kNormShape.threads), 0, st, sp, x, x, f);
+            launch(c, (k_dot<kNormShape.unroll, true, kNormShape.threads>),
+                   dim3(vector_grid(c, sp.n2, kNormShape, true)), dim3(kNormShape.threads), 0, st, sp, x, x, f);
         else
-            launch(c, (k_dot<kDotShape.unroll, false, kDotShape.threads>), dim3(vector_grid(c, sp.n2, kDotShape, true)),
-                               dim3(kDotShape.threads), 0, st, sp, x, y, f);
+            launch(c, (k_dot<kDotShape.unroll, false, kDotShape.threads>),
+                   dim3(vector_grid(c, sp.n2, kDotShape, true)), dim3(kDotShape.threads), 0, st, sp, x, y, f);
         return launch_status();
     }
     const unsigned nb = scalar_grid(c, n);
@@ -1275,19 +1275,19 @@ int gather_launch(bs_ctx *c, int64_t ng, const int32_t *off, const int32_t *ids,
                    c->partials, cgs);
         else if (w)
             launch(c, k_gather_plan<true>, dim3(*nb), dim3(kBlock), 0, st, bstart, off, ids, vl, vg, w,
-                               c->partials, cgs);
+                   c->partials, cgs);
         else
             launch(c, k_gather_plan<false>, dim3(*nb), dim3(kBlock), 0, st, bstart, off, ids, vl, vg,
-                               nullptr, nullptr, cgs);
+                   nullptr, nullptr, cgs);
     } else {
         const int64_t per = (int64_t)kBlock * kGatherRowR;
         *nb = (unsigned)((ng + per - 1) / per);
         if (w)
             launch(c, k_gather_rows<true>, dim3(*nb), dim3(kBlock), 0, st, ng, off, ids, vl, vg, w,
-                               c->partials, cgs);
+                   c->partials, cgs);
         else
             launch(c, k_gather_rows<false>, dim3(*nb), dim3(kBlock), 0, st, ng, off, ids, vl, vg,
-                               nullptr, nullptr, cgs);
+                   nullptr, nullptr, cgs);
     }
     return launch_status();
 }
@@ -1304,7 +1304,8 @@ int gather_args(const bs_ctx *c, int64_t n_global, const int32_t *off, const int
         if (n_blocks < 1 || n_blocks > n_global || misaligned(block_starts, 4)) return BS_EINVAL;
     }
     // the fused dot writes one partial per block
-    int64_t nb = block_starts ? n_blocks : (n_global + (int64_t)kBlock * kGatherRowR - 1) / ((int64_t)kBlock * kGatherRowR);
+    const int64_t rows_per_block = (int64_t)kBlock * kGatherRowR;
+    const int64_t nb = block_starts ? n_blocks : (n_global + rows_per_block - 1) / rows_per_block;
     if (dot && nb > c->max_partials) return BS_ERANGE;
     return BS_OK;
 }
@@ -1440,7 +1441,7 @@ int bs_axpy(bs_ctx *c, int64_t n, double alpha, const double *x, double beta, do
     if (common_head(ptrs, 2, &head)) {
         const Split sp = split_of(n, head);
         launch(c, k_axpy<kAxpyShape.unroll>, dim3(vector_grid(c, sp.n2, kAxpyShape, false)), dim3(kBlock),
-                           0, st, sp, Coef{alpha, nullptr}, x, Coef{beta, nullptr}, y, nullptr);
+               0, st, sp, Coef{alpha, nullptr}, x, Coef{beta, nullptr}, y, nullptr);
     } else {
         launch(c, k_axpy_scalar, dim3(scalar_grid(c, n)), dim3(kBlock), 0, st, n, alpha, x, beta, y);
     }
@@ -1461,7 +1462,7 @@ int bs_scale(bs_ctx *c, int64_t n, const double *x, const double *d, double *y, 
     if (common_head(ptrs, 3, &head)) {
         const Split sp = split_of(n, head);
         launch(c, k_scale<kAxpyShape.unroll>, dim3(vector_grid(c, sp.n2, kAxpyShape, false)), dim3(kBlock),
-                           0, st, sp, x, d, y);
+               0, st, sp, x, d, y);
     } else {
         launch(c, k_scale_scalar, dim3(scalar_grid(c, n)), dim3(kBlock), 0, st, n, x, d, y);
     }
@@ -1509,7 +1510,7 @@ int bs_cg_update(bs_ctx *c, int64_t n, double alpha, const double *p, const doub
         const Split sp = split_of(n, head);
         launch(c, k_cg_update<kCgShape.unroll, kCgRUnroll, kCgShape.threads>,
                dim3(vector_grid(c, sp.n2, kCgShape, true)), dim3(kCgShape.threads),
-                           0, st, sp, Coef{alpha, nullptr}, p, q, x, r, fin_out(c, rr, false), nullptr);
+               0, st, sp, Coef{alpha, nullptr}, p, q, x, r, fin_out(c, rr, false), nullptr);
         return launch_status();
     }
     const unsigned nb = scalar_grid(c, n);
@@ -1532,11 +1533,11 @@ int bs_scatter(bs_ctx *c, int64_t n_local, const int32_t *l2g, const double *v_g
         const int64_t per = 2LL * kBlock * kScatterPairs;
         const int64_t nb = (n_local + per - 1) / per;
         launch(c, k_scatter, dim3((unsigned)nb), dim3(kBlock), 0, st, n_local, l2g, v_global, v_local,
-                           nullptr);
+               nullptr);
     } else {
         const int64_t nb = (n_local + kBlock - 1) / kBlock;
         launch(c, k_scatter_scalar, dim3((unsigned)nb), dim3(kBlock), 0, st, n_local, l2g, v_global,
-                           v_local);
+               v_local);
     }
     return launch_status();
 }
@@ -1627,7 +1628,7 @@ int bs_cg_solve(bs_ctx *c, int64_t n_global, int64_t n_local, const int32_t *l2g
         if (int s = gather_launch(c, n_global, off, ids, p_local, q, block_starts, n_blocks, p, cgs, st, &nb, keep))
             return s;
         launch(c, k_cg_finish, dim3(1), dim3(kFinishBlock), 0, st, c->partials, (int)nb, c->cgs,
-                           rr_hist, k, iters, 0.0, (int)kSetAlpha);
+               rr_hist, k, iters, 0.0, (int)kSetAlpha);
         // x += alpha p, r -= alpha q, r.r; beta = rr' / rr (the update's last block).
         // Two passes when the iteration is cache-resident; otherwise one pass,
         // which overlaps the cached part of p (left by the scatter) with HBM.
