@@ -471,8 +471,10 @@ def main():
                     help="time only this workload (repeatable; skips the step; for profiling one mesh at a time)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the BS operations here run on a single MI355X; "
-              "how they would shard is described in the design notes. Use --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the BS operations here run on a single MI355X. Across GPUs "
+              "each global vector would split into per-GPU slices and the mesh into z-slabs, with one "
+              "partial per reduction and the slab-plane interface nodes exchanged; that exchange is not "
+              "built. Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
