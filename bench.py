@@ -26,9 +26,11 @@ reads cold data), the roofline of the dominant operation (HIP events around
 it in every timed step), and the CPU oracle timed on a bounded sample of the
 same step. Optional: --sweep fits the latency-plus-bandwidth model
 T(B) = T0 + B/W_max (eq. 8) over n = 2^10 .. 2^28 and reports
-B_0.8 = 4 T0 W_max (eq. 10); --workloads times the shuffled 40^3 order-5 and
-24^3 order-15 meshes and the CG streaming sequence (host-driven and
-device-resident). Their results go to --out (JSON), not stdout.
+B_0.8 = 4 T0 W_max (eq. 10); --workloads times the shuffled 40^3 order-5,
+tet-split and 24^3 order-15 meshes and one GPU's slab share of the 32^3
+order-7 mesh, and the CG streaming sequence (host-driven and
+device-resident) on the slab, the 24^3 order-15 mesh and the whole 32^3
+order-7 mesh. Their results go to --out (JSON), not stdout.
 """
 from __future__ import annotations
 
@@ -328,7 +330,7 @@ def tet_split_tables(bs, cubes, N, seed):
     return bs.bs_mesh_hex_l2g(ev, N, nv)
 
 
-WORKLOADS = ["shuffled40_N5", "tetsplit11_N7", "slab32x32x4_N7", "box24_N15"]
+WORKLOADS = ["shuffled40_N5", "tetsplit11_N7", "slab32x32x4_N7", "box24_N15", "cg_box32_N7"]
 
 
 def workloads(bs, torch, dev, gather_lds, steps=30, only=None):
@@ -336,13 +338,17 @@ def workloads(bs, torch, dev, gather_lds, steps=30, only=None):
     tet-split mesh of 11^3 cubes (31944 hexahedra) at order 7 (scatter,
     gather), one GPU's share of the 32^3 order-7 mesh cut into eight z-slabs
     (32 x 32 x 4 elements, all 7 ops, and the CG streaming sequence, whose
-    device-resident iteration there fits in the last-level cache) and the 24^3
-    order-15 mesh (all 7 ops, and the CG streaming sequence)."""
+    device-resident iteration there fits in the last-level cache), the 24^3
+    order-15 mesh (all 7 ops, and the CG streaming sequence) and the CG
+    streaming sequence alone on the 32^3 order-7 mesh (whose r and p, but not
+    the whole iteration, fit in the last-level cache; the step already times
+    its seven operations)."""
     out = {}
     for name, E, N, ops in [("shuffled40_N5", 40, 5, ["scatter", "gather"]),
                             ("tetsplit11_N7", 11, 7, ["scatter", "gather"]),
                             ("slab32x32x4_N7", 32, 7, OPS),
-                            ("box24_N15", 24, 15, OPS)]:
+                            ("box24_N15", 24, 15, OPS),
+                            ("cg_box32_N7", 32, 7, [])]:
         if only and name not in only:
             continue
         tables = None
@@ -350,21 +356,22 @@ def workloads(bs, torch, dev, gather_lds, steps=30, only=None):
             tables = tet_split_tables(bs, E, N, bs_inputs.base_seed(name) + bs_inputs.SEED_ELEM)
         elif name.startswith("slab"):
             tables = (bs.bs_mesh_box_l2g(E, E, 4, N), bs.bs_mesh_box_count(E, E, 4, N)[1])
-        m = Mesh(bs, torch, dev, name, E, N, gather_lds, tables=tables)
+        # the CG-only workload runs on the step's own mesh and inputs
+        m = Mesh(bs, torch, dev, "box32_N7" if name == "cg_box32_N7" else name, E, N, gather_lds, tables=tables)
         if tables is not None:
             out[name + "_mesh"] = {"elements": 24 * E ** 3 if name.startswith("tetsplit") else E * E * 4, "order": N,
                                    "n_local": m.nl, "n_global": m.ng}
-        stream = torch.cuda.current_stream().cuda_stream
-        # rotated sets: >= 1 GB through the cache between two touches
-        R = 3 if name.startswith("box24") else 48 if name.startswith("slab") else 5
-        sets = [m] + [m.clone() for _ in range(R - 1)]
-        per_op = time_ops_native(bs, sets, ops, max(3 * R, 96))
-        del sets
-        res = {op: {"bytes": m.bytes(op), "us": round(per_op[op] * 1e6, 2),
-                    "GBps": round(m.bytes(op) / per_op[op] / 1e9, 1),
-                    "pct_peak": round(100 * m.bytes(op) / per_op[op] / 1e9 / PEAK_GBPS, 1)} for op in ops}
-        out[name] = res
-        if name in ("box24_N15", "slab32x32x4_N7"):
+        if ops:
+            # rotated sets: >= 1 GB through the cache between two touches
+            R = 3 if name.startswith("box24") else 48 if name.startswith("slab") else 5
+            sets = [m] + [m.clone() for _ in range(R - 1)]
+            per_op = time_ops_native(bs, sets, ops, max(3 * R, 96))
+            del sets
+            res = {op: {"bytes": m.bytes(op), "us": round(per_op[op] * 1e6, 2),
+                        "GBps": round(m.bytes(op) / per_op[op] / 1e9, 1),
+                        "pct_peak": round(100 * m.bytes(op) / per_op[op] / 1e9 / PEAK_GBPS, 1)} for op in ops}
+            out[name] = res
+        if name in ("box24_N15", "slab32x32x4_N7", "cg_box32_N7"):
             out["cg_sequence_" + name] = cg_sequence(bs, torch, dev, m)
         del m
         torch.cuda.empty_cache()
