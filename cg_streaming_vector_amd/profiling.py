@@ -151,6 +151,12 @@ def summarize(stats_csv, fetch_csv, write_csv, copy_kernel, copy_doubles, source
     if copy_kernel in fetch and copy_kernel in write:
         f_scale = known / (statistics.median(fetch[copy_kernel]) * 1024.0)
         w_scale = known / (statistics.median(write[copy_kernel]) * 1024.0)
+        # a copy writes its bytes once: WRITE_SIZE of a copy of the stated
+        # size reads back within a few percent, so a scale far from 1 means
+        # copy_doubles is not the size the run copied
+        if not 0.8 <= w_scale <= 1.25:
+            raise ValueError(f"{copy_kernel}: WRITE_SIZE scale {w_scale:.3g} for {copy_doubles} doubles; "
+                             "pass the run's copy size (--copy-doubles)")
     reused = False
     if f_scale is None and calibration:
         f_scale, w_scale = calibration

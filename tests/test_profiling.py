@@ -43,6 +43,9 @@ def test_calibrated_traffic(tmp_path):
     k = s["kernels"]["k_scatter"]
     assert k["hbm_bytes_per_launch"] == pytest.approx(30 * 1024 * 2 + 20 * 1024)
     assert k["calls"] == 7 and k["avg_ns"] == 1500.0
+    # a wrong copy size (the run copied n doubles, the caller says 8 n) is refused
+    with pytest.raises(ValueError, match="copy-doubles"):
+        profiling.summarize(tmp_path / "s.csv", tmp_path / "f.csv", tmp_path / "w.csv", "k_copy<1>", 8 * n)
     md = profiling.to_markdown(s, "t", ["rocprofv3 ..."])
     assert "k_scatter" in md and "rocprofv3 ..." in md
 
