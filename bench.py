@@ -24,13 +24,14 @@ step, whole job), with per-operation times (HIP events around loops of
 back-to-back launches that cycle through distinct array sets, so every launch
 reads cold data), the roofline of the dominant operation (HIP events around
 it in every fourth timed step), and the CPU oracle timed on a bounded sample of the
-same step. Optional: --sweep fits the latency-plus-bandwidth model
-T(B) = T0 + B/W_max (eq. 8) over n = 2^10 .. 2^28 and reports
-B_0.8 = 4 T0 W_max (eq. 10); --workloads times the shuffled 40^3 order-5,
-tet-split and 24^3 order-15 meshes and one GPU's slab share of the 32^3
-order-7 mesh, and the CG streaming sequence (host-driven and
-device-resident) on the slab, the 24^3 order-15 mesh and the whole 32^3
-order-7 mesh. Their results go to --out (JSON), not stdout.
+same step. After the timed region (skipped with --no-extras): the size
+sweep n = 2^10 .. 2^28 fitted to the latency-plus-bandwidth model
+T(B) = T0 + B/W_max (eq. 8) with B_0.8 = 4 T0 W_max (eq. 10), and the other
+workloads: the shuffled 40^3 order-5, tet-split and 24^3 order-15 meshes, one
+GPU's slab share of the 32^3 order-7 mesh, and the CG streaming sequence
+(host-driven and device-resident) on the slab, the 24^3 order-15 mesh and the
+whole 32^3 order-7 mesh. Their compact figures join the line; --out writes
+everything (JSON).
 """
 from __future__ import annotations
 
@@ -58,6 +59,7 @@ KERNEL_NAME = {  # op -> its kernels as rocprofv3 names them (namespace and argu
     "scatter": ["k_scatter"], "gather": ["k_gather_plan<false>"],
 }
 GATHER_NPB = 1024
+PER_OP_FIELDS = ["bytes", "us", "us_best", "GBps", "pct_peak", "pct_copy_ceiling", "hot_us"]
 EVENT_STRIDE = 4  # timed steps per step whose dominant kernel records events
 
 
@@ -280,47 +282,94 @@ def cpu_baseline(mesh_host, budget_s=12.0, budget_1_thread_s=4.0):
                 break
     except OSError:
         pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
     return {"value": round(nb * reps / t / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{reps} full step(s) of the 32^3 order-7 mesh (all 7 ops, oracle tables), "
-                      f"{t:.1f} s of wall time on {threads} OpenMP threads of {model}",
+            "sample": f"{reps} steps of 32^3 N=7 (7 ops), {t:.1f} s on {threads} OpenMP threads, {model[:24]}",
+            "omp_threads": threads, "affinity_cpus": affinity,
             "value_1_thread": round(nb * reps1 / t1 / 1e9, 3),
-            "sample_1_thread": f"{reps1} full step(s), {t1:.1f} s of wall time on 1 thread"}
+            "sample_1_thread": f"{reps1} steps, {t1:.1f} s, 1 thread"}
 
 
-def sweep(bs, torch, dev, reps_min=100, min_seconds=0.05):
-    """The size sweep: each vector op over n = 2^10 .. 2^28, fitted to T(B) = T0 + B/W_max.
-    The launches of each point are issued by the library's C++ loop
-    (bs_bench_loop), timed on the host around the whole run as the pages
-    time it; at least reps_min launches and min_seconds per point."""
+SWEEP_OPS = ["copy", "axpy", "norm", "dot", "cg_update"]
+SWEEP_ARITY = {"copy": 2, "axpy": 2, "norm": 1, "dot": 2, "cg_update": 4}
+
+
+def sweep_sets(torch, dev, n, R, layout):
+    """R sets of four vectors of n doubles, uniform [-1, 1). "arena": each
+    set is one allocation whose arrays sit on 2 MB boundaries, each followed
+    by one unused 2 MB granule, so that no two operands of power-of-two
+    length are a power of two apart (the step's own arrays sit on 2 MB
+    boundaries at distances of 92 MB). "torch": each vector a separate torch
+    allocation."""
+    from cg_streaming_vector_amd.arena import Arena
+    sets = []
+    for _ in range(R):
+        if layout == "arena":
+            a = Arena(4 * (Arena.slot(8 * n) + Arena.slot(1)), dev)
+            vs = [a.empty(n, torch.float64, pad=1) for _ in range(4)]
+        else:
+            vs = [torch.empty(n, dtype=torch.float64, device=dev) for _ in range(4)]
+        for v in vs:
+            v.uniform_(-1, 1)
+        sets.append(vs)
+    return sets
+
+
+def sweep(bs, torch, dev, reps_min=100, min_seconds=0.05, ks=range(10, 29), layout="arena"):
+    """The size sweep: each vector op over n = 2^k, fitted to T(B) = T0 + B/W_max
+    (eq. 8). The launches of each point are issued by the library's C++ loop
+    (bs_bench_loop), timed on the host around the whole run as the pages time
+    it; at least reps_min launches and min_seconds per point, cycling through
+    enough sets (>= 1 GiB of footprint) that every launch reads cold data.
+    Returns per op: the points, the fit (T0, W_max, B_0.8, R^2 of the
+    bandwidth), each point's relative bandwidth residual (measured - model) /
+    measured, and the measured plateau (median GB/s of the points of at least
+    0.5 GB)."""
     stream = torch.cuda.current_stream().cuda_stream
-    res = {op: [] for op in ["copy", "axpy", "norm", "dot", "cg_update"]}
-    arity = {"copy": 2, "axpy": 2, "norm": 1, "dot": 2, "cg_update": 4}
+    res = {op: [] for op in SWEEP_OPS}
     out = torch.zeros(1, dtype=torch.float64, device=dev)
-    for k in range(10, 29):
+    for k in ks:
         n = 1 << k
-        per = 48 * n
-        R = max(2, int(np.ceil(2 ** 30 / per)))  # rotate sets: >= 1 GiB of footprint
-        R = min(R, 64)
-        sets = [[torch.empty(n, dtype=torch.float64, device=dev).uniform_(-1, 1) for _ in range(4)]
-                for _ in range(R)]
+        R = min(64, max(2, int(np.ceil(2 ** 30 / (32 * n)))))
+        sets = sweep_sets(torch, dev, n, R, layout)
         for op in res:
-            groups = [tuple(s[:arity[op]]) for s in sets]
-            bs.bs_bench_loop(op, n, groups, max(R, 8), out, stream=stream)  # warm-up
-            t_one = bs.bs_bench_loop(op, n, groups, max(R, 8), out, stream=stream) / max(R, 8)
+            groups = [tuple(s[:SWEEP_ARITY[op]]) for s in sets]
+            w = max(R, 8)
+            bs.bs_bench_loop(op, n, groups, w, out, stream=stream)  # warm-up
+            t_one = bs.bs_bench_loop(op, n, groups, w, out, stream=stream) / w
             reps = max(reps_min, R, int(np.ceil(min_seconds / max(t_one, 1e-7))))
             T = bs.bs_bench_loop(op, n, groups, reps, out, stream=stream) / reps
             res[op].append((op_bytes(op, n), T))
         del sets
         torch.cuda.empty_cache()
-    from cg_streaming_vector_amd.model import fit_streaming_model
-    out = {}
+    from cg_streaming_vector_amd.model import fit_streaming_model, w_eff
+    fits = {}
     for op, pts in res.items():
         B = np.array([p[0] for p in pts], dtype=np.float64)
         T = np.array([p[1] for p in pts], dtype=np.float64)
         f = fit_streaming_model(B, T)
-        out[op] = {"points": [[int(b), t] for b, t in pts], **f}
-    return out
+        W = B / T
+        resid = (W - w_eff(B, f["T0_s"], f["W_max"])) / W
+        big = W[B >= 0.5e9]
+        fits[op] = {"points": [[int(b), t] for b, t in pts], **f,
+                    "rel_residuals": [round(float(x), 4) for x in resid],
+                    "plateau_GBps": round(float(np.median(big)) / 1e9, 1) if big.size else None}
+    return fits
+
+
+SWEEP_FIELDS = ["T0_us", "W_max_GBps", "B_08_MB", "r2", "max_abs_rel_residual", "plateau_GBps"]
+
+
+def sweep_summary(fits):
+    """The compact per-op figures of a sweep for the benchmark's JSON line
+    (values in the order of SWEEP_FIELDS)."""
+    return {op: [round(f["T0_s"] * 1e6, 2), round(f["W_max_GBps"], 1), round(f["B_08_bytes"] / 1e6, 1),
+                 round(f["r2_bandwidth"], 4), round(max(abs(x) for x in f["rel_residuals"]), 3),
+                 f["plateau_GBps"]] for op, f in fits.items()}
 
 
 def tet_split_tables(bs, cubes, N, seed):
@@ -459,6 +508,26 @@ def cg_sequence(bs, torch, dev, m, iters=100):
             "device_cg_rel_residual_after_4": float(np.sqrt(h4[4] / h4[0]))}
 
 
+def workload_summary(wl):
+    """Compact figures of the other workloads for the JSON line: per mesh and
+    operation [us, % of 8 TB/s]; per CG sequence [device-resident, host-driven
+    with fixed scalars, true CG with readbacks] in us per iteration, and the
+    device-resident iteration's GB/s of bytes actually moved. The slab share's
+    per-operation figures stay in --out."""
+    out = {}
+    for name, r in wl.items():
+        if name.endswith("_mesh") or name.startswith("slab"):
+            continue
+        if name.startswith("cg_sequence_"):
+            out["cg_" + name[len("cg_sequence_"):].replace("cg_", "")] = [
+                r["device_cg_us_per_iter"], r["fixed_scalars_us_per_iter"], r["true_cg_us_per_iter"],
+                r["device_cg_GBps_moved"]]
+        else:
+            out[name] = {op: [v["us"], v["pct_peak"]] for op, v in r.items()}
+    out["fields"] = "mesh: op -> [us, pct_peak]; cg_*: [device us/iter, fixed-scalar us/iter, true-CG us/iter, device GB/s]"
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -472,8 +541,10 @@ def main():
                     help="arena: each set's arrays packed in one allocation on 2 MB boundaries")
     ap.add_argument("--per-op-reps", type=int, default=96)
     ap.add_argument("--trials", type=int, default=5, help="per-op loops repeated; the median is reported")
-    ap.add_argument("--sweep", action="store_true")
-    ap.add_argument("--workloads", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the size sweep and the other workloads (profiling runs of the step)")
+    ap.add_argument("--sweep-layout", choices=["arena", "torch"], default="arena",
+                    help="arena: each sweep set in one allocation, arrays 2 MB-aligned and staggered")
     ap.add_argument("--out", default=None)
     ap.add_argument("--workload", action="append", choices=WORKLOADS, default=[],
                     help="time only this workload (repeatable; skips the step; for profiling one mesh at a time)")
@@ -555,10 +626,9 @@ def main():
     for op in OPS:
         t = per_op[op]
         gbps = mesh.bytes(op) / t / 1e9
-        ops_out[op] = {"bytes": mesh.bytes(op), "us": round(t * 1e6, 2), "us_best": round(min(trials[op]) * 1e6, 2),
-                       "GBps": round(gbps, 1), "pct_peak": round(100 * gbps / PEAK_GBPS, 1),
-                       "pct_copy_ceiling": round(100 * gbps / ceiling, 1) if ceiling else None,
-                       "hot_us": round(hot[op] * 1e6, 2)}
+        ops_out[op] = [mesh.bytes(op), round(t * 1e6, 2), round(min(trials[op]) * 1e6, 2), round(gbps, 1),
+                       round(100 * gbps / PEAK_GBPS, 1), round(100 * gbps / ceiling, 1) if ceiling else None,
+                       round(hot[op] * 1e6, 2)]
     achieved = mesh.bytes(dom) / dom_live / 1e9
     traffic = traffic_for(KERNEL_NAME[dom])
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
@@ -594,22 +664,30 @@ def main():
                    "cu_count": ctx.info()["cu_count"]},
         "pct_peak": round(100 * value / PEAK_GBPS, 1),
         "per_op": ops_out,
+        "per_op_fields": PER_OP_FIELDS,
         "runtime_copy_GBps": round(rt_copy, 1),
         "copy_ceiling_GBps": round(ceiling, 1) if ceiling else None,
-        "per_op_note": f"us: median of {args.trials} trials of {args.per_op_reps} back-to-back launches (issued by "
-                       f"the library's C++ loop, host-timed) over {args.rotate} rotated array sets (cold); us_best: "
-                       "best trial; hot_us: the same loop on one set (the vector kernels' non-temporal "
-                       "accesses do not allocate in the last-level cache, so only the scatter's and gather's "
-                       "ordinary-policy reads can find cached data); pct_copy_ceiling: against "
-                       "copy_ceiling_GBps, the library's copy of 2^28 doubles",
+        "per_op_note": f"us: median of {args.trials} x {args.per_op_reps} launches (C++ loop, host clock) over "
+                       f"{args.rotate} rotated sets; hot_us: one set; ceiling: our copy of 2^28 doubles",
         "roofline": roofline,
     }
 
+    # Outside the timed region: the size sweep with its eq. 8 fit, and the
+    # other meshes and the CG sequence. Their compact figures join the line;
+    # --out keeps everything.
     extra = {}
-    if args.sweep:
-        extra["sweep"] = sweep(bs, torch, dev)
-    if args.workloads:
-        extra["workloads"] = workloads(bs, torch, dev, args.gather == "lds")
+    if not args.no_extras:
+        t_x = time.perf_counter()
+        fits = sweep(bs, torch, dev, layout=args.sweep_layout)
+        extra["sweep"] = fits
+        line["sweep_fit"] = sweep_summary(fits)
+        line["sweep_fit_fields"] = SWEEP_FIELDS
+        line["sweep_fit_note"] = (f"n=2^10..2^28 ({args.sweep_layout} layout); eq. 8 fit by relative error; "
+                                  "plateau: median GB/s of points >= 0.5 GB")
+        wl = workloads(bs, torch, dev, args.gather == "lds")
+        extra["workloads"] = wl
+        line["workloads"] = workload_summary(wl)
+        line["extras_s"] = round(time.perf_counter() - t_x, 1)
 
     if not args.no_cpu_baseline:
         import oracle

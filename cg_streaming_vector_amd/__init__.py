@@ -146,16 +146,31 @@ class Context:
 
 
 _contexts = {}
+_ctx_lock = threading.Lock()  # not _lock: creating a Context may load the library under _lock
 
 
-def context(device=None) -> Context:
-    """The shared per-device context (created on first use)."""
+def _shared_context(dev: int, stream_handle: int) -> Context:
+    """The shared context of one (device, stream) pair, created on first use.
+
+    A context's reduction scratch (partials, arrival tickets, CG scalars) is
+    ordered only by the stream its calls are enqueued on: two reductions on
+    different streams sharing one context would race on it and could leave a
+    ticket counter nonzero for every later call. Keying the shared contexts
+    by stream as well as device gives each stream its own scratch."""
+    key = (int(dev), int(stream_handle or 0))
+    with _ctx_lock:
+        ctx = _contexts.get(key)
+        if ctx is None:
+            ctx = _contexts[key] = Context(key[0])
+    return ctx
+
+
+def context(device=None, stream=None) -> Context:
+    """The shared context of a device and stream (default: the current device
+    and its current torch stream), created on first use."""
     import torch
     dev = torch.cuda.current_device() if device is None else int(device)
-    ctx = _contexts.get(dev)
-    if ctx is None:
-        ctx = _contexts[dev] = Context(dev)
-    return ctx
+    return _shared_context(dev, _stream(stream, dev))
 
 
 # ------------------------------------------------------------ marshalling --
@@ -180,9 +195,11 @@ def _stream(stream, device):
     return stream.cuda_stream
 
 
-def _ctx_dev(t, ctx):
+def _ctx_dev(t, ctx, stream=None):
+    """The context a call on tensor t's device and `stream` uses: the one
+    given, else the shared context of that device and stream."""
     if ctx is None:
-        ctx = context(t.device.index)
+        ctx = _shared_context(t.device.index, _stream(stream, t.device))
     return ctx
 
 
@@ -203,7 +220,7 @@ def bs_copy(x, y, *, ctx=None, stream=None):
     import torch
     if x.numel() != y.numel():
         raise ValueError("x and y differ in length")
-    ctx = _ctx_dev(x, ctx)
+    ctx = _ctx_dev(x, ctx, stream)
     _check(_lib().bs_copy(ctx.handle, x.numel(), _dev_tensor(x, torch.float64, "x"),
                           _dev_tensor(y, torch.float64, "y"), _stream(stream, x.device)), "bs_copy")
     return y
@@ -214,7 +231,7 @@ def bs_axpy(alpha, x, beta, y, *, ctx=None, stream=None):
     import torch
     if x.numel() != y.numel():
         raise ValueError("x and y differ in length")
-    ctx = _ctx_dev(x, ctx)
+    ctx = _ctx_dev(x, ctx, stream)
     _check(_lib().bs_axpy(ctx.handle, x.numel(), float(alpha), _dev_tensor(x, torch.float64, "x"),
                           float(beta), _dev_tensor(y, torch.float64, "y"), _stream(stream, x.device)),
            "bs_axpy")
@@ -224,7 +241,7 @@ def bs_axpy(alpha, x, beta, y, *, ctx=None, stream=None):
 def bs_norm(x, out=None, *, ctx=None, stream=None):
     """BS3: out[0] = sqrt(sum x^2) on the device; returns out."""
     import torch
-    ctx = _ctx_dev(x, ctx)
+    ctx = _ctx_dev(x, ctx, stream)
     out = _scalar_out(out, x)
     _check(_lib().bs_norm(ctx.handle, x.numel(), _dev_tensor(x, torch.float64, "x"), out.data_ptr(),
                           _stream(stream, x.device)), "bs_norm")
@@ -236,7 +253,7 @@ def bs_dot(x, y, out=None, *, ctx=None, stream=None):
     import torch
     if x.numel() != y.numel():
         raise ValueError("x and y differ in length")
-    ctx = _ctx_dev(x, ctx)
+    ctx = _ctx_dev(x, ctx, stream)
     out = _scalar_out(out, x)
     _check(_lib().bs_dot(ctx.handle, x.numel(), _dev_tensor(x, torch.float64, "x"),
                          _dev_tensor(y, torch.float64, "y"), out.data_ptr(), _stream(stream, x.device)),
@@ -250,7 +267,7 @@ def bs_cg_update(alpha, p, q, x, r, out=None, *, ctx=None, stream=None):
     n = p.numel()
     if not (q.numel() == x.numel() == r.numel() == n):
         raise ValueError("p, q, x, r differ in length")
-    ctx = _ctx_dev(p, ctx)
+    ctx = _ctx_dev(p, ctx, stream)
     out = _scalar_out(out, p)
     _check(_lib().bs_cg_update(ctx.handle, n, float(alpha), _dev_tensor(p, torch.float64, "p"),
                                _dev_tensor(q, torch.float64, "q"), _dev_tensor(x, torch.float64, "x"),
@@ -264,7 +281,7 @@ def bs_scatter(l2g, v_global, v_local, *, ctx=None, stream=None):
     import torch
     if l2g.numel() != v_local.numel():
         raise ValueError("l2g and v_local differ in length")
-    ctx = _ctx_dev(v_local, ctx)
+    ctx = _ctx_dev(v_local, ctx, stream)
     _check(_lib().bs_scatter(ctx.handle, l2g.numel(), _dev_tensor(l2g, torch.int32, "l2g"),
                              _dev_tensor(v_global, torch.float64, "v_global"),
                              _dev_tensor(v_local, torch.float64, "v_local"),
@@ -278,7 +295,7 @@ def bs_gather(off, ids, v_local, v_global, block_starts=None, *, ctx=None, strea
     ng = v_global.numel()
     if off.numel() != ng + 1:
         raise ValueError("off must hold n_global + 1 entries")
-    ctx = _ctx_dev(v_global, ctx)
+    ctx = _ctx_dev(v_global, ctx, stream)
     bp, nb = None, 0
     if block_starts is not None:
         bp = _dev_tensor(block_starts, torch.int32, "block_starts")
@@ -296,7 +313,7 @@ def bs_scale(x, d, y, *, ctx=None, stream=None):
     import torch
     if not (x.numel() == d.numel() == y.numel()):
         raise ValueError("x, d, y differ in length")
-    ctx = _ctx_dev(x, ctx)
+    ctx = _ctx_dev(x, ctx, stream)
     _check(_lib().bs_scale(ctx.handle, x.numel(), _dev_tensor(x, torch.float64, "x"),
                            _dev_tensor(d, torch.float64, "d"), _dev_tensor(y, torch.float64, "y"),
                            _stream(stream, x.device)), "bs_scale")
@@ -325,7 +342,7 @@ def bs_gather_dot(off, ids, v_local, v_global, w, block_starts=None, out=None, *
     ng = v_global.numel()
     if off.numel() != ng + 1 or w.numel() != ng:
         raise ValueError("off must hold n_global + 1 entries and w n_global")
-    ctx = _ctx_dev(v_global, ctx)
+    ctx = _ctx_dev(v_global, ctx, stream)
     out = _scalar_out(out, v_global)
     bp, nb = None, 0
     if block_starts is not None:
@@ -343,12 +360,19 @@ def bs_gather_dot(off, ids, v_local, v_global, w, block_starts=None, out=None, *
 def bs_cg_solve(l2g, off, ids, x, r, p, q, p_local, iters, tol=0.0, block_starts=None, rr_hist=None, *,
                 ctx=None, stream=None):
     """Device-resident CG on Z^T Z: runs up to `iters` iterations on the
-    device (x, r, p updated in place); returns rr_hist (device, iters+1)."""
+    device (x, r, p updated in place); returns rr_hist (device, iters+1).
+    A caller-supplied rr_hist must hold at least iters + 1 entries (the
+    device writes that many; ValueError before anything is enqueued)."""
     import torch
     ng, nl = x.numel(), l2g.numel()
     if not (r.numel() == p.numel() == q.numel() == ng) or p_local.numel() != nl or off.numel() != ng + 1:
         raise ValueError("inconsistent sizes")
-    ctx = _ctx_dev(x, ctx)
+    if int(iters) < 0:
+        raise ValueError("iters must be >= 0")
+    if rr_hist is not None and rr_hist.numel() < int(iters) + 1:
+        # the device writes rr_hist[0 .. iters]; the C ABI cannot see its length
+        raise ValueError(f"rr_hist holds {rr_hist.numel()} entries; {int(iters) + 1} are written")
+    ctx = _ctx_dev(x, ctx, stream)
     if rr_hist is None:
         rr_hist = torch.empty(int(iters) + 1, dtype=torch.float64, device=x.device)
     bp, nb = None, 0
@@ -495,7 +519,7 @@ def bs_bench_loop(op, n, sets, reps, result=None, alpha=0.37, beta=1.0, *, n_blo
     first = sets[0][0]
     if op in ("norm", "dot", "cg_update"):
         result = _scalar_out(result, first)
-    ctx = _ctx_dev(first, ctx)
+    ctx = _ctx_dev(first, ctx, stream)
     sec = _dbl()
     _check(_lib().bs_bench_loop(ctx.handle, BS_OP[op], int(n), float(alpha), float(beta), int(n_blocks), len(sets),
                                 ptrs, None if result is None else result.data_ptr(), int(reps),

@@ -16,6 +16,8 @@ SOURCES = [os.path.join(CSRC, "bs_kernels.hip"), os.path.join(CSRC, "bs_host.cpp
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-ffp-contract=off",
+    # the leading kernel arguments arrive in SGPRs at wave launch
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     # no packed fp32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-command-line-argument",

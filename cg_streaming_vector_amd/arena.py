@@ -28,15 +28,18 @@ class Arena:
         """Bytes an array of nbytes occupies in an arena."""
         return (int(nbytes) + align - 1) // align * align
 
-    def empty(self, n: int, dtype):
-        """An uninitialised 1-D tensor of n elements at the next aligned slot."""
+    def empty(self, n: int, dtype, pad: int = 0):
+        """An uninitialised 1-D tensor of n elements at the next aligned slot;
+        `pad` more granules of `align` bytes are left unused after it (so that
+        arrays whose sizes are powers of two do not sit a power of two
+        apart)."""
         import torch
         itemsize = torch.empty(0, dtype=dtype).element_size()
         nbytes = int(n) * itemsize
         if self.pos + nbytes > self.cap:
             raise MemoryError("arena exhausted")
         t = self.buf[self.pos:self.pos + nbytes].view(dtype)
-        self.pos += self.slot(max(nbytes, 1), self.align)
+        self.pos += self.slot(max(nbytes, 1), self.align) + int(pad) * self.align
         return t
 
     def put(self, src):

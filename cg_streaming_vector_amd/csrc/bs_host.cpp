@@ -99,14 +99,23 @@ extern "C" {
 int bs_mesh_box_count(int ex, int ey, int ez, int order, int64_t *n_local, int64_t *n_global)
 {
     if (ex < 1 || ey < 1 || ez < 1 || order < 1) return BS_EINVAL;
-    const int64_t nq = (int64_t)order + 1;
-    const int64_t K = (int64_t)ex * ey * ez;
-    // guard the products against overflow before forming them
-    if (nq > 2048 || K > (int64_t)INT32_MAX) return BS_ERANGE;
-    const int64_t nl = K * nq * nq * nq;
+    // Every product below is bounded before it is formed, so none can
+    // overflow int64: a dimension times the order stays within int32, and
+    // each running product is compared with INT32_MAX divided by the next
+    // factor.
+    const int64_t lim = INT32_MAX;
+    if (order > 2047) return BS_ERANGE;
+    if (ex > lim / order || ey > lim / order || ez > lim / order) return BS_ERANGE;
+    const int64_t nq = (int64_t)order + 1, np = nq * nq * nq;  // np < 2^33
+    const int64_t exy = (int64_t)ex * ey;                       // < 2^62
+    if (exy > lim / ez) return BS_ERANGE;
+    const int64_t K = exy * ez;  // <= INT32_MAX
+    if (K > lim / np) return BS_ERANGE;
+    const int64_t nl = K * np;
     const int64_t gx = (int64_t)ex * order + 1, gy = (int64_t)ey * order + 1, gz = (int64_t)ez * order + 1;
-    const int64_t ng = gx * gy * gz;
-    if (nl > INT32_MAX || ng > INT32_MAX) return BS_ERANGE;
+    const int64_t gxy = gx * gy;  // each factor <= 2^31, so < 2^62
+    if (gxy > lim / gz) return BS_ERANGE;
+    const int64_t ng = gxy * gz;
     if (n_local) *n_local = nl;
     if (n_global) *n_global = ng;
     return BS_OK;

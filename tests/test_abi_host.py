@@ -89,6 +89,26 @@ def test_box_counts(bs):
     assert e.value.status == bs.BS_ERANGE
 
 
+@pytest.mark.parametrize("dims", [(2 ** 21, 2 ** 21, 2 ** 21, 1), (2 ** 31 - 1, 2 ** 31 - 1, 2 ** 31 - 1, 1),
+                                  (2 ** 16, 2 ** 16, 2 ** 16, 1), (2 ** 31 - 1, 1, 1, 1), (1, 1, 1, 2048),
+                                  (1, 1, 1, 2 ** 31 - 1), (2 ** 30, 1, 1, 3), (1, 46341, 46341, 1),
+                                  (1, 1, 1, 1290)])
+def test_box_count_products_that_would_overflow(bs, dims):
+    """Sizes whose element, local or global counts pass int32 (or whose
+    products would pass int64 if formed) are refused, with nothing written."""
+    L = bs._lib()
+    nl, ng = ctypes.c_int64(-7), ctypes.c_int64(-7)
+    assert L.bs_mesh_box_count(*dims, ctypes.byref(nl), ctypes.byref(ng)) == bs.BS_ERANGE
+    assert nl.value == -7 and ng.value == -7
+
+
+def test_box_count_at_the_int32_edge(bs):
+    # boxes at the edge of int32 counts still fit
+    assert bs.bs_mesh_box_count(1, 1, 1, 1289) == (1290 ** 3, 1290 ** 3)
+    assert bs.bs_mesh_box_count(268435455, 1, 1, 1) == (8 * 268435455, 2 * 2 * 268435456)
+    assert bs.bs_mesh_box_count(16383, 16383, 1, 1) == (8 * 16383 ** 2, 2 * 16384 ** 2)
+
+
 # ------------------------------------------- tables against the oracle ----
 
 @pytest.mark.parametrize("dims,N", [((1, 1, 1), 1), ((2, 2, 2), 2), ((3, 2, 4), 3), ((8, 8, 8), 3),

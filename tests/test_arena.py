@@ -14,9 +14,20 @@ def test_arena_alignment_and_order():
     assert y.data_ptr() - x.data_ptr() == ALIGN
     assert z.data_ptr() - y.data_ptr() == 2 * ALIGN
     assert torch.equal(z, torch.arange(10, dtype=torch.int32))
+    # the slots are distinct memory: filling one leaves its neighbours alone
+    y.fill_(-2.0)
     x.fill_(1.5)
-    assert float(y[0].item()) != 1.5 or True  # distinct memory
+    assert float(y[0].item()) == -2.0 and float(y[-1].item()) == -2.0
+    assert torch.equal(z, torch.arange(10, dtype=torch.int32))
+    assert float(x[-1].item()) == 1.5
     assert Arena.slot(1) == ALIGN and Arena.slot(ALIGN) == ALIGN and Arena.slot(ALIGN + 1) == 2 * ALIGN
+
+
+def test_arena_padding():
+    a = Arena(8 * ALIGN, "cpu")
+    x = a.empty(4 * ALIGN // 8, torch.float64, pad=1)  # a power-of-two size, one granule of padding
+    y = a.empty(10, torch.float64)
+    assert y.data_ptr() - x.data_ptr() == 5 * ALIGN
 
 
 def test_arena_exhausted():

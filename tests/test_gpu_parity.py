@@ -973,6 +973,18 @@ def test_contexts_on_concurrent_streams(env):
         assert_rel(got[0], want, f"stream {k}")
     for c in ctxs:
         c.close()
+    # without explicit contexts the binding gives each stream its own shared one
+    outs = [torch.zeros(8, dtype=torch.float64, device=d) for _ in range(2)]
+    torch.cuda.synchronize()
+    for rep in range(8):
+        for k in range(2):
+            bs.bs_norm(X[k], outs[k][rep:rep + 1], stream=streams[k])
+    torch.cuda.synchronize()
+    assert bs.context(0, streams[0]) is not bs.context(0, streams[1])
+    for k in range(2):
+        got = host(outs[k])
+        assert np.all(got == got[0])
+        assert_rel(got[0], orc.norm(xs[k]), f"shared context, stream {k}")
 
 
 def test_unstructured_lumped_mass(env):
