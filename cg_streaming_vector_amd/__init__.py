@@ -66,6 +66,8 @@ SIGNATURES = {
     "bs_mesh_box_mass": ([_int, _int, _int, _int, _ptr], _int),
     "bs_cg_solve": ([_ptr, _i64, _i64, _ptr, _ptr, _ptr, _ptr, _i64, _ptr, _ptr, _ptr, _ptr, _ptr, _int, _dbl,
                      _ptr, _ptr], _int),
+    "bs_cg_solve_static": ([_i64, _i64, _ptr, _ptr, _ptr, _ptr, _i64, _ptr, _ptr, _ptr, _ptr, _ptr, _int, _dbl, _ptr,
+                            _ptr], _int),
     "bs_mesh_box_count": ([_int, _int, _int, _int, ctypes.POINTER(_i64), ctypes.POINTER(_i64)], _int),
     "bs_mesh_box_l2g": ([_int, _int, _int, _int, _ptr, _ptr, _ptr], _int),
     "bs_mesh_hex_l2g": ([_i64, _int, _i64, _ptr, _ptr, ctypes.POINTER(_i64)], _int),
@@ -389,6 +391,34 @@ def bs_cg_solve(l2g, off, ids, x, r, p, q, p_local, iters, tol=0.0, block_starts
     return rr_hist
 
 
+def bs_cg_solve_static(l2g, off, ids, x, r, p, q, p_local, iters, rr_hist, tol=0.0, block_starts=None, *,
+                       stream=None):
+    """bs_cg_solve without a context or any allocation (the library's static
+    device scratch; on the current device): for callers that cannot allocate,
+    e.g. under graph capture. The caller passes rr_hist (iters + 1 entries).
+    Overlapping calls on one GPU race on the shared scratch."""
+    import torch
+    ng, nl = x.numel(), l2g.numel()
+    if not (r.numel() == p.numel() == q.numel() == ng) or p_local.numel() != nl or off.numel() != ng + 1:
+        raise ValueError("inconsistent sizes")
+    if int(iters) < 0:
+        raise ValueError("iters must be >= 0")
+    if rr_hist.numel() < int(iters) + 1:
+        raise ValueError(f"rr_hist holds {rr_hist.numel()} entries; {int(iters) + 1} are written")
+    bp, nb = None, 0
+    if block_starts is not None:
+        bp = _dev_tensor(block_starts, torch.int32, "block_starts")
+        nb = block_starts.numel() - 1
+    _check(_lib().bs_cg_solve_static(ng, nl, _dev_tensor(l2g, torch.int32, "l2g"),
+                                     _dev_tensor(off, torch.int32, "off"), _dev_tensor(ids, torch.int32, "ids"), bp,
+                                     nb, _dev_tensor(x, torch.float64, "x"), _dev_tensor(r, torch.float64, "r"),
+                                     _dev_tensor(p, torch.float64, "p"), _dev_tensor(q, torch.float64, "q"),
+                                     _dev_tensor(p_local, torch.float64, "p_local"), int(iters), float(tol),
+                                     _dev_tensor(rr_hist, torch.float64, "rr_hist"), _stream(stream, x.device)),
+           "bs_cg_solve_static")
+    return rr_hist
+
+
 # ------------------------------------------------------------ host tables --
 
 def _host_i32(a, name):
@@ -530,7 +560,7 @@ def bs_bench_loop(op, n, sets, reps, result=None, alpha=0.37, beta=1.0, *, n_blo
 __all__ = [
     "BSError", "Context", "context", "LIB_PATH", "SIGNATURES",
     "bs_copy", "bs_axpy", "bs_norm", "bs_dot", "bs_cg_update", "bs_scatter", "bs_gather",
-    "bs_gather_dot", "bs_cg_solve", "bs_scale", "bs_gll", "bs_mesh_box_mass",
+    "bs_gather_dot", "bs_cg_solve", "bs_cg_solve_static", "bs_scale", "bs_gll", "bs_mesh_box_mass",
     "bs_bench_loop", "BS_OP", "BS_BENCH_SET",
     "bs_mesh_box_count", "bs_mesh_box_l2g", "bs_mesh_hex_l2g", "bs_mesh_hex_mass", "bs_validate_l2g", "bs_index_g2l", "bs_gather_plan",
 ]

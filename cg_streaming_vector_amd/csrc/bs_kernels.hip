@@ -48,6 +48,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
+#include <mutex>
 #include <new>
 
 #include "bs.h"
@@ -1108,6 +1109,14 @@ __global__ __launch_bounds__(kBlock) void k_cg_update_scalar(int64_t n, double a
     if (threadIdx.x == 0) partials[blockIdx.x] = part;
 }
 
+// Sets the arrival counters of the one-kernel reductions to zero (the
+// allocation-free CG solve clears its static counters this way at the start
+// of every call: a kernel, so the call stays capturable in a HIP graph).
+__global__ __launch_bounds__(kBlock) void k_zero_tickets(unsigned *tickets)
+{
+    for (int i = threadIdx.x; i < kTickets; i += kBlock) tickets[i] = 0u;
+}
+
 }  // namespace
 
 // =================================================================== ABI ====
@@ -1600,12 +1609,18 @@ int bs_gather_dot(bs_ctx *c, int64_t n_global, const int32_t *off, const int32_t
     return finish_launch(c, nb, result, false, st);
 }
 
-int bs_cg_solve(bs_ctx *c, int64_t n_global, int64_t n_local, const int32_t *l2g, const int32_t *off,
-                const int32_t *ids, const int32_t *block_starts, int64_t n_blocks, double *x, double *r,
-                double *p, double *q, double *p_local, int iters, double tol, double *rr_hist, void *stream)
+}  // extern "C"
+
+namespace {
+
+// The device-resident CG iteration on the scratch of `c` (a context, or the
+// static scratch of bs_cg_solve_static, which asks for its ticket counters to
+// be cleared first). The device of `c` is current.
+int cg_solve_run(bs_ctx *c, int64_t n_global, int64_t n_local, const int32_t *l2g, const int32_t *off,
+                 const int32_t *ids, const int32_t *block_starts, int64_t n_blocks, double *x, double *r, double *p,
+                 double *q, double *p_local, int iters, double tol, double *rr_hist, void *stream,
+                 bool zero_tickets)
 {
-    DeviceScope scope;
-    if (int s = scope.enter(c)) return s;
     if (n_global < 1 || n_local < 1 || iters < 0 || !(tol >= 0.0) || !l2g || !x || !r || !p || !q || !p_local ||
         !rr_hist)
         return BS_EINVAL;
@@ -1626,6 +1641,10 @@ int bs_cg_solve(bs_ctx *c, int64_t n_global, int64_t n_local, const int32_t *l2g
     hipStream_t st = static_cast<hipStream_t>(stream);
     const Split sp = split_of(n_global, 0);
     const double *cgs = c->cgs;
+    if (zero_tickets) {
+        launch(c, k_zero_tickets, dim3(1), dim3(kBlock), 0, st, c->tickets);
+        if (hipGetLastError() != hipSuccess) return BS_EHIP;
+    }
     // rr0 = r.r, history, threshold
     if (int s = dot_launch(c, n_global, r, r, true, fin_cg(c, kStart, rr_hist, 0, iters, tol * tol), st)) return s;
     unsigned nb;
@@ -1680,6 +1699,93 @@ int bs_cg_solve(bs_ctx *c, int64_t n_global, int64_t n_local, const int32_t *l2g
         if (hipGetLastError() != hipSuccess) return BS_EHIP;
     }
     return BS_OK;
+}
+
+// ------------------------------------------------ allocation-free solve ----
+// Scratch of bs_cg_solve_static: the ticket counters, the CG scalars and up
+// to kStaticPartials reduction partials, in one static device array. Each GPU
+// the library runs on holds its own copy for the life of the process; its
+// address there is taken once per device with hipGetSymbolAddress (in host
+// code the array's name is not a device address).
+constexpr int kStaticPartials = 1 << 17;  // 1 MiB: gathers of up to 131072 blocks
+constexpr int kStaticTicketDoubles = kTickets * (int)sizeof(unsigned) / (int)sizeof(double);
+constexpr int kStaticCgDoubles = 32;  // kCgSlots doubles, padded to 256 bytes
+constexpr int kStaticDoubles = kStaticTicketDoubles + kStaticCgDoubles + kStaticPartials;
+static_assert(kTickets * sizeof(unsigned) % 256 == 0, "tickets fill whole 256-byte lines");
+static_assert(kCgSlots <= kStaticCgDoubles, "CG scalars fit their slot");
+
+}  // namespace
+
+static __device__ __align__(256) double scratch[kStaticDoubles];
+
+namespace {
+
+constexpr int kMaxStaticDevices = 64;
+struct StaticScratch {
+    double *base = nullptr;  // device address of `scratch` on this device
+    int cus = 0;
+};
+StaticScratch g_static[kMaxStaticDevices];
+std::mutex g_static_mutex;
+
+// Set-up on first use on a device (the device is current): its copy's
+// address and its compute-unit count. Allocates nothing.
+int static_scratch(int device, StaticScratch *out)
+{
+    if (device < 0 || device >= kMaxStaticDevices) return BS_EINVAL;
+    std::lock_guard<std::mutex> lock(g_static_mutex);
+    StaticScratch &s = g_static[device];
+    if (!s.base) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus < 1)
+            return BS_EHIP;
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return BS_EHIP;
+        s.cus = cus;
+        s.base = static_cast<double *>(ptr);
+    }
+    *out = s;
+    return BS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bs_cg_solve(bs_ctx *c, int64_t n_global, int64_t n_local, const int32_t *l2g, const int32_t *off,
+                const int32_t *ids, const int32_t *block_starts, int64_t n_blocks, double *x, double *r,
+                double *p, double *q, double *p_local, int iters, double tol, double *rr_hist, void *stream)
+{
+    DeviceScope scope;
+    if (int s = scope.enter(c)) return s;
+    return cg_solve_run(c, n_global, n_local, l2g, off, ids, block_starts, n_blocks, x, r, p, q, p_local, iters,
+                        tol, rr_hist, stream, false);
+}
+
+int bs_cg_solve_static(int64_t n_global, int64_t n_local, const int32_t *l2g, const int32_t *off,
+                       const int32_t *ids, const int32_t *block_starts, int64_t n_blocks, double *x, double *r,
+                       double *p, double *q, double *p_local, int iters, double tol, double *rr_hist,
+                       void *stream)
+{
+    // the checks that need no device first, so that they fail without a HIP call
+    if (n_global < 1 || n_local < 1 || iters < 0 || !(tol >= 0.0) || !l2g || !off || !ids || !x || !r || !p || !q ||
+        !p_local || !rr_hist)
+        return BS_EINVAL;
+    int device = -1;
+    if (hipGetDevice(&device) != hipSuccess) return BS_EHIP;
+    StaticScratch ss;
+    if (int s = static_scratch(device, &ss)) return s;
+    // a context on the stack whose scratch is this device's static array
+    bs_ctx c{};
+    c.device = device;
+    c.cus = ss.cus;
+    c.max_partials = kStaticPartials;
+    c.tickets = reinterpret_cast<unsigned *>(ss.base);
+    c.cgs = ss.base + kStaticTicketDoubles;
+    c.partials = c.cgs + kStaticCgDoubles;
+    c.time_start = c.time_stop = nullptr;
+    return cg_solve_run(&c, n_global, n_local, l2g, off, ids, block_starts, n_blocks, x, r, p, q, p_local, iters,
+                        tol, rr_hist, stream, true);
 }
 
 }  // extern "C"

@@ -201,6 +201,27 @@ int bs_cg_solve(bs_ctx *ctx, int64_t n_global, int64_t n_local, const int32_t *l
                 int64_t n_blocks, double *x, double *r, double *p, double *q, double *p_local,
                 int iters, double tol, double *rr_hist, void *stream);
 
+/* bs_cg_solve without a context and without any allocation, for callers
+ * that cannot allocate device memory: code under HIP stream or graph
+ * capture, tight solver or serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results (the same bits) and errors as bs_cg_solve, on the
+ * calling thread's current HIP device. Its reduction scratch (ticket
+ * counters, CG scalars and up to 131072 partials, about 1 MiB) is a static
+ * device array of the library that every GPU it runs on holds until the
+ * process ends; the first call on a device looks up that array's address,
+ * later calls allocate and look up nothing. Each call first clears the
+ * counters with a small kernel on `stream` (no memset, so the call can be
+ * captured). All calls on one GPU share that one array: calls that overlap
+ * in time on a GPU (different streams, or host threads racing) race on it
+ * and give wrong results; order them. A gather with more than 131072 blocks
+ * (block_starts with n_blocks > 131072, or n_global > 67108864 without a
+ * plan) is BS_ERANGE, with nothing enqueued. BS_EHIP if the device or the
+ * array's address cannot be queried. */
+int bs_cg_solve_static(int64_t n_global, int64_t n_local, const int32_t *l2g, const int32_t *off,
+                       const int32_t *ids, const int32_t *block_starts, int64_t n_blocks, double *x, double *r,
+                       double *p, double *q, double *p_local, int iters, double tol, double *rr_hist,
+                       void *stream);
+
 /* ---------------------------------------------------- host-side tables --
  * These run on the host, need no GPU, and write caller-allocated host arrays.
  */

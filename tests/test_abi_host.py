@@ -66,6 +66,8 @@ def test_null_context_is_einval_before_any_hip_call(bs):
     assert L.bs_gather_dot(None, 10, None, None, None, None, None, 0, None, None, None) == bs.BS_EINVAL
     assert L.bs_cg_solve(None, 10, 10, None, None, None, None, 0, None, None, None, None, None, 4, 0.0, None,
                          None) == bs.BS_EINVAL
+    assert L.bs_cg_solve_static(10, 10, None, None, None, None, 0, None, None, None, None, None, 4, 0.0, None,
+                                None) == bs.BS_EINVAL
     assert L.bs_bench_loop(None, 0, 10, 1.0, 1.0, 0, 1, None, None, 1, None, None) == bs.BS_EINVAL
     assert L.bs_ctx_create(0, None) == bs.BS_EINVAL
     assert L.bs_ctx_info(None, None, None, None) == bs.BS_EINVAL
