@@ -63,7 +63,11 @@ _H = Decimal("1e-40")
 def class_data(m, b):
     """Distinct multiplicities lam (ascending), the class of each node, and
     the class sums S_c of b_i^2."""
-    lam, inv = np.unique(np.asarray(m), return_inverse=True)
+    m = np.asarray(m, dtype=np.int64)
+    lam = np.nonzero(np.bincount(m))[0]
+    lut = np.zeros(int(lam[-1]) + 1, dtype=np.int64)
+    lut[lam] = np.arange(lam.size)
+    inv = lut[m]
     b = np.asarray(b, dtype=np.float64)
     S = np.bincount(inv, weights=b * b, minlength=lam.size)
     return [float(v) for v in lam], inv, [float(s) for s in S]
@@ -220,6 +224,19 @@ class CgBounds:
     def significant(self, k, limit=1e-3):
         """Is step k's relative comparison inside the first-order regime?"""
         return self.rel_tol[k] <= limit
+
+
+def check_cg(h, ohist, x, ox, m, b, iters, what=""):
+    """The whole comparison of a GPU CG run (history h, solution x) with the
+    oracle's (ohist, ox) on A = diag(m) from r0 = p0 = b: every step inside
+    the first-order regime relatively, the converged ones against the
+    rounding floor, and x per class. Returns the bounds."""
+    lam, cls, S = class_data(m, b)
+    bounds = CgBounds(lam, S, iters)
+    compared = check_history(h, ohist, bounds, what)
+    assert compared and compared == list(range(len(compared))), f"{what}: steps compared {compared}"
+    check_x(x, ox, b, cls, bounds, what)
+    return bounds
 
 
 def check_history(h, ohist, bounds, what=""):

@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 
 import bs_inputs
+from cg_bounds import check_cg
 
 pytestmark = pytest.mark.gpu
 
@@ -492,10 +493,7 @@ def test_cg_sequence_matches_oracle(env):
         bs.bs_axpy(1.0, r, rr_new / rr, p)
         rr = rr_new
         hist.append(rr)
-    for h, oh in zip(hist[:2], ohist[:2]):
-        assert_rel(h, oh, "rr")
-    assert math.sqrt(hist[-1] / hist[0]) < 1e-13
-    assert np.allclose(host(x), ox, rtol=1e-12, atol=1e-14)
+    check_cg(hist, ohist, host(x), ox, np.diff(off), b, 4, "host-driven CG")
 
 
 # ----------------------------------------- gather + dot, device-resident CG ----
@@ -568,22 +566,18 @@ def cg_setup(env, name):
 
 @pytest.mark.parametrize("name", ["box8_N3", "box32_N7"])
 def test_cg_solve_matches_oracle(env, name):
-    """Four device-resident CG iterations on Z^T Z against the oracle's CG:
-    same residual history to 1e-12 while it is significant, same x, and
-    convergence (A = diag(m), m in {1,2,4,8}: at most 4 steps)."""
+    """Four device-resident CG iterations on Z^T Z against the oracle's CG
+    (A = diag(m), m in {1,2,4,8}: exact CG converges in 4 steps): each
+    residual within the first-order rounding bound of its own size, the
+    converged one below the rounding floor, x per class (cg_bounds)."""
     bs, orc, torch, d = env
     t, ol2g, ng, b = cg_setup(env, name)
     ox, orr_, ohist = orc.cg_sequence(ol2g, ng, b, 4)
+    m = np.diff(host(t["off"]))
     for plan in (None, t["plan"]):
         x, r, p = t["x"].clone(), t["r"].clone(), t["p"].clone()
         hist = bs.bs_cg_solve(t["l2g"], t["off"], t["ids"], x, r, p, t["q"], t["pl"], 4, 0.0, plan)
-        h = host(hist)
-        assert_rel(h[0], ohist[0], "rr0")
-        assert_rel(h[1], ohist[1], "rr1")
-        assert math.sqrt(h[4] / h[0]) < 1e-13
-        m = np.diff(host(t["off"]))
-        assert np.allclose(host(x), ox, rtol=1e-12, atol=1e-14)
-        assert np.allclose(host(x), b / m, rtol=1e-12, atol=1e-14)
+        check_cg(host(hist), ohist, host(x), ox, m, b, 4, f"{name} plan={plan is not None}")
 
 
 def test_cg_solve_cache_resident_slab(env):
@@ -610,12 +604,7 @@ def test_cg_solve_cache_resident_slab(env):
     q = torch.empty(ng, dtype=torch.float64, device=d)
     pl = torch.empty(l2g.size, dtype=torch.float64, device=d)
     h = host(bs.bs_cg_solve(dl2g, doff, dids, x, r, p, q, pl, 4, 0.0, plan))
-    assert_rel(h[0], ohist[0], "rr0")
-    assert_rel(h[1], ohist[1], "rr1")
-    assert math.sqrt(h[4] / h[0]) < 1e-13
-    m = np.diff(off)
-    assert np.allclose(host(x), ox, rtol=1e-12, atol=1e-14)
-    assert np.allclose(host(x), b / m, rtol=1e-12, atol=1e-14)
+    check_cg(h, ohist, host(x), ox, np.diff(off), b, 4, "slab")
 
 
 @pytest.mark.parametrize("ex,ey,ez,N", [(1, 1, 1, 1), (3, 2, 5, 2), (7, 4, 3, 5), (10, 11, 9, 4), (13, 9, 12, 6),
@@ -643,11 +632,33 @@ def test_cg_solve_boxes(env, ex, ey, ez, N):
         x = torch.zeros(ng, dtype=torch.float64, device=d)
         r, p = dev(torch, d, b), dev(torch, d, b)
         h = host(bs.bs_cg_solve(dl2g, doff, dids, x, r, p, q, pl, iters, 0.0, plan))
-        assert_rel(h[0], ohist[0], "rr0")
-        assert abs(h[1] - ohist[1]) <= 1e-12 * ohist[0]
-        assert math.sqrt(h[iters] / h[0]) < 1e-12
-        assert np.allclose(host(x), ox, rtol=1e-11, atol=1e-13)
-        assert np.allclose(host(x), b / m, rtol=1e-11, atol=1e-13)
+        check_cg(h, ohist, host(x), ox, m, b, iters, f"box {ex}x{ey}x{ez} order {N} plan={plan is not None}")
+
+
+def test_cg_solve_box24_N15(env):
+    """The device CG on the 24^3 order-15 box (47.0M global nodes, 56.6M local
+    entries), the mesh on which the benchmark times the CG iteration, in the
+    benchmark's launch configuration (plan of 1024 entries per block; only
+    r and p would not fit the last-level cache, so every stream is
+    non-temporal). Four iterations against the oracle's CG within the derived
+    bounds."""
+    bs, orc, torch, d = env
+    l2g, off, ids, ol2g, ng = mesh_case(env, "box24_N15")
+    m = np.diff(off)
+    assert sorted(set(m.tolist())) == [1, 2, 4, 8]
+    b = bs_inputs.uniform_pm1(bs_inputs.base_seed("box24_N15") + 3, ng)
+    print(f"box24_N15 CG: oracle ({ng} nodes)", flush=True)
+    ox, _, ohist = orc.cg_sequence(ol2g, ng, b, 4)
+    del ol2g
+    dl2g, doff, dids = dev(torch, d, l2g), dev(torch, d, off), dev(torch, d, ids)
+    plan = dev(torch, d, bs.bs_gather_plan(off, 1024))
+    x = torch.zeros(ng, dtype=torch.float64, device=d)
+    r, p = dev(torch, d, b), dev(torch, d, b)
+    q = torch.empty(ng, dtype=torch.float64, device=d)
+    pl = torch.empty(l2g.size, dtype=torch.float64, device=d)
+    print("box24_N15 CG: device", flush=True)
+    h = host(bs.bs_cg_solve(dl2g, doff, dids, x, r, p, q, pl, 4, 0.0, plan))
+    check_cg(h, ohist, host(x), ox, m, b, 4, "box24_N15")
 
 
 def test_cg_solve_early_exit_and_zero_iterations(env):
@@ -735,12 +746,7 @@ def test_unstructured_cg_solve(env):
     q = torch.empty(ng, dtype=torch.float64, device=d)
     pl = torch.empty(l2g.size, dtype=torch.float64, device=d)
     h = host(bs.bs_cg_solve(t["l2g"], t["off"], t["ids"], x, r, p, q, pl, iters, 0.0, t["plan"]))
-    assert_rel(h[0], ohist[0], "rr0")
-    assert_rel(h[1], ohist[1], "rr1")
-    assert abs(h[2] - ohist[2]) <= 1e-9 * ohist[2]
-    assert math.sqrt(h[iters] / h[0]) < 1e-10
-    assert np.allclose(host(x), b / m, rtol=1e-9, atol=1e-12)
-    assert np.allclose(ox, b / m, rtol=1e-9, atol=1e-12)
+    check_cg(h, ohist, host(x), ox, m, b, iters, "tet-split")
 
 
 def test_unstructured_cg_solve_handoff(env):
@@ -769,12 +775,7 @@ def test_unstructured_cg_solve_handoff(env):
     q = torch.empty(ng, dtype=torch.float64, device=d)
     pl = torch.empty(l2g.size, dtype=torch.float64, device=d)
     h = host(bs.bs_cg_solve(t["l2g"], t["off"], t["ids"], x, r, p, q, pl, iters, 0.0, t["plan"]))
-    assert_rel(h[0], ohist[0], "rr0")
-    assert_rel(h[1], ohist[1], "rr1")
-    assert abs(h[2] - ohist[2]) <= 1e-9 * ohist[2]
-    assert math.sqrt(h[iters] / h[0]) < 1e-10
-    assert np.allclose(host(x), b / m, rtol=1e-9, atol=1e-12)
-    assert np.allclose(host(x), ox, rtol=1e-9, atol=1e-12)
+    check_cg(h, ohist, host(x), ox, m, b, iters, "tet-split 11^3")
 
 
 # -------------------------------------------------------- launch loop -----
