@@ -73,6 +73,8 @@ SIGNATURES = {
     "bs_mesh_hex_l2g": ([_i64, _int, _i64, _ptr, _ptr, ctypes.POINTER(_i64)], _int),
     "bs_mesh_hex_mass": ([_i64, _int, _ptr, _ptr], _int),
     "bs_validate_l2g": ([_i64, _i64, _ptr], _int),
+    "bs_validate_g2l": ([_i64, _i64, _ptr, _ptr, _ptr], _int),
+    "bs_validate_plan": ([_i64, _ptr, _i64], _int),
     "bs_index_g2l": ([_i64, _i64, _ptr, _ptr, _ptr], _int),
     "bs_gather_plan": ([_i64, _ptr, _int, _ptr, ctypes.POINTER(_i64)], _int),
     "bs_bench_loop": ([_ptr, _int, _i64, _dbl, _dbl, _i64, _int, _ptr, _ptr, _int, _ptr, ctypes.POINTER(_dbl)],
@@ -482,6 +484,34 @@ def bs_validate_l2g(l2g, n_global):
     _check(_lib().bs_validate_l2g(l2g.size, int(n_global), l2g.ctypes.data), "bs_validate_l2g")
 
 
+def bs_validate_g2l(off, ids, n_local, l2g=None):
+    """Raise BSError unless (off, ids) is a well-formed CSR of I_g->l for
+    n_local local entries (and, given l2g, exactly its transpose)."""
+    off = _host_i32(off, "off")
+    ids = _host_i32(ids, "ids")
+    ng = off.size - 1
+    if ng < 0:
+        raise ValueError("off must hold n_global + 1 entries")
+    if ids.size < max(int(off[-1]), 0):
+        raise ValueError("ids must hold off[-1] entries")
+    lp = None
+    if l2g is not None:
+        l2g = _host_i32(l2g, "l2g")
+        if l2g.size != int(n_local):
+            raise ValueError("l2g must hold n_local entries")
+        lp = l2g.ctypes.data
+    _check(_lib().bs_validate_g2l(ng, int(n_local), off.ctypes.data, ids.ctypes.data if ids.size else None, lp),
+           "bs_validate_g2l")
+
+
+def bs_validate_plan(block_starts, n_global):
+    """Raise BSError unless block_starts is a well-formed gather plan."""
+    bs_ = _host_i32(block_starts, "block_starts")
+    if bs_.size < 1:
+        raise ValueError("block_starts needs n_blocks + 1 >= 1 entries")
+    _check(_lib().bs_validate_plan(int(n_global), bs_.ctypes.data, bs_.size - 1), "bs_validate_plan")
+
+
 def bs_index_g2l(l2g, n_global):
     """CSR of I_g->l: (off int32[n_global+1], ids int32[entries])."""
     l2g = _host_i32(l2g, "l2g")
@@ -562,5 +592,5 @@ __all__ = [
     "bs_copy", "bs_axpy", "bs_norm", "bs_dot", "bs_cg_update", "bs_scatter", "bs_gather",
     "bs_gather_dot", "bs_cg_solve", "bs_cg_solve_static", "bs_scale", "bs_gll", "bs_mesh_box_mass",
     "bs_bench_loop", "BS_OP", "BS_BENCH_SET",
-    "bs_mesh_box_count", "bs_mesh_box_l2g", "bs_mesh_hex_l2g", "bs_mesh_hex_mass", "bs_validate_l2g", "bs_index_g2l", "bs_gather_plan",
+    "bs_mesh_box_count", "bs_mesh_box_l2g", "bs_mesh_hex_l2g", "bs_mesh_hex_mass", "bs_validate_l2g", "bs_validate_g2l", "bs_validate_plan", "bs_index_g2l", "bs_gather_plan",
 ]

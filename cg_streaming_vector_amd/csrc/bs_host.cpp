@@ -420,6 +420,47 @@ int bs_validate_l2g(int64_t n_local, int64_t n_global, const int32_t *l2g)
     return BS_OK;
 }
 
+int bs_validate_g2l(int64_t n_global, int64_t n_local, const int32_t *off, const int32_t *ids, const int32_t *l2g)
+{
+    if (n_global < 0 || n_local < 0 || !off) return BS_EINVAL;
+    if (n_global >= INT32_MAX || n_local > INT32_MAX) return BS_ERANGE;
+    if (off[0] != 0) return BS_EINVAL;
+    for (int64_t g = 0; g < n_global; ++g)
+        if (off[g + 1] < off[g]) return BS_EINVAL;
+    const int64_t nnz = off[n_global];
+    if (nnz > n_local) return BS_EINVAL;
+    if (nnz > 0 && !ids) return BS_EINVAL;
+    for (int64_t g = 0; g < n_global; ++g) {
+        for (int64_t j = off[g]; j < off[g + 1]; ++j) {
+            const int32_t i = ids[j];
+            // in range, and strictly ascending inside the row (the order the
+            // gather adds in; a repeated id would count an entry twice)
+            if (i < 0 || i >= n_local) return BS_EINVAL;
+            if (j > off[g] && i <= ids[j - 1]) return BS_EINVAL;
+            if (l2g && l2g[i] != g) return BS_EINVAL;
+        }
+    }
+    if (l2g) {
+        // every unmasked local entry appears: the CSR is the whole transpose
+        int64_t unmasked = 0;
+        for (int64_t i = 0; i < n_local; ++i) unmasked += l2g[i] >= 0;
+        if (unmasked != nnz) return BS_EINVAL;
+    }
+    return BS_OK;
+}
+
+int bs_validate_plan(int64_t n_global, const int32_t *block_starts, int64_t n_blocks)
+{
+    if (n_global < 0 || n_blocks < 0 || !block_starts) return BS_EINVAL;
+    if (n_global >= INT32_MAX) return BS_ERANGE;
+    if (n_global == 0) return n_blocks == 0 && block_starts[0] == 0 ? BS_OK : BS_EINVAL;
+    if (n_blocks < 1 || n_blocks > n_global) return BS_EINVAL;
+    if (block_starts[0] != 0 || block_starts[n_blocks] != n_global) return BS_EINVAL;
+    for (int64_t b = 0; b < n_blocks; ++b)
+        if (block_starts[b + 1] <= block_starts[b]) return BS_EINVAL;
+    return BS_OK;
+}
+
 int bs_index_g2l(int64_t n_local, int64_t n_global, const int32_t *l2g, int32_t *off, int32_t *ids)
 {
     if (n_local < 0 || n_global < 0 || !off || (n_local > 0 && (!l2g || !ids))) return BS_EINVAL;

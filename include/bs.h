@@ -154,7 +154,8 @@ int bs_scatter(bs_ctx *ctx, int64_t n_local, const int32_t *l2g, const double *v
  * selects the row-per-lane kernel; otherwise int32[n_blocks+1] from
  * bs_gather_plan selects the LDS-staged kernel (same bits). Neither the CSR
  * nor the plan is range-checked on the device: pass tables built by
- * bs_index_g2l and bs_gather_plan (or equally well formed). n_global >=
+ * bs_index_g2l and bs_gather_plan, or check others once with
+ * bs_validate_g2l and bs_validate_plan. n_global >=
  * INT32_MAX is BS_ERANGE. */
 int bs_gather(bs_ctx *ctx, int64_t n_global, const int32_t *off, const int32_t *ids,
               const double *v_local, double *v_global, const int32_t *block_starts,
@@ -304,6 +305,24 @@ int bs_mesh_hex_mass(int64_t n_elements, int order, const double *xe, double *w_
 /* Check that every id is < n_global (negative ids are masks): BS_OK or
  * BS_EINVAL. */
 int bs_validate_l2g(int64_t n_local, int64_t n_global, const int32_t *l2g);
+
+/* Check a CSR form of I_g->l before a gather trusts it (the device reads it
+ * unchecked): off[0] == 0, off nondecreasing, off[n_global] <= n_local,
+ * every id in [0, n_local) and ids strictly ascending inside each row (the
+ * order the gather adds in; a repeated id would count an entry twice). With
+ * l2g (int32[n_local], may be NULL) also that the CSR is exactly its
+ * transpose: l2g[ids[j]] == g for every entry j of row g, and every unmasked
+ * local entry appears once. off int32[n_global+1], ids int32[off[n_global]].
+ * BS_OK or BS_EINVAL; BS_ERANGE for sizes beyond int32 indices. */
+int bs_validate_g2l(int64_t n_global, int64_t n_local, const int32_t *off, const int32_t *ids, const int32_t *l2g);
+
+/* Check a blockStarts plan before a gather trusts it: block_starts[0] == 0,
+ * strictly increasing, block_starts[n_blocks] == n_global, 1 <= n_blocks <=
+ * n_global (n_global == 0: n_blocks == 0 and block_starts[0] == 0). Blocks
+ * above the LDS stage's capacity are allowed (the kernel reads them from
+ * global memory). block_starts int32[n_blocks+1]. BS_OK or BS_EINVAL;
+ * BS_ERANGE for n_global >= INT32_MAX. */
+int bs_validate_plan(int64_t n_global, const int32_t *block_starts, int64_t n_blocks);
 
 /* CSR form of I_g->l: a stable counting-sort transpose of l2g. off receives
  * int32[n_global+1]; ids receives the off[n_global] local indices (at most

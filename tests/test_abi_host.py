@@ -410,3 +410,83 @@ def test_hex_mass_errors(bs):
     L = bs._lib()
     assert L.bs_mesh_hex_mass(1, 3, None, None) == bs.BS_EINVAL
     assert bs.bs_mesh_hex_mass(np.zeros((0, 8, 3)), 3).size == 0
+
+
+# ------------------------------------------------------- table validators --
+
+def _tables(bs, dims=(5, 4, 3), N=4):
+    l2g = bs.bs_mesh_box_l2g(*dims, N)
+    ng = bs.bs_mesh_box_count(*dims, N)[1]
+    off, ids = bs.bs_index_g2l(l2g, ng)
+    return l2g, ng, off, ids
+
+
+def test_validate_g2l_accepts_built_tables(bs):
+    l2g, ng, off, ids = _tables(bs)
+    bs.bs_validate_g2l(off, ids, l2g.size)
+    bs.bs_validate_g2l(off, ids, l2g.size, l2g)
+    masked = l2g.copy()
+    masked[::5] = -1
+    moff, mids = bs.bs_index_g2l(masked, ng)
+    bs.bs_validate_g2l(moff, mids, masked.size, masked)
+    # an empty mesh
+    bs.bs_validate_g2l(np.zeros(1, dtype=np.int32), np.zeros(0, dtype=np.int32), 0)
+
+
+@pytest.mark.parametrize("fault", ["first_offset", "decreasing", "too_many", "id_negative", "id_high",
+                                   "descending", "repeated", "wrong_row", "missing"])
+def test_validate_g2l_rejects(bs, fault):
+    l2g, ng, off, ids = _tables(bs)
+    off, ids, nl = off.copy(), ids.copy(), l2g.size
+    row = 37  # a row with several entries
+    a, b = int(off[row]), int(off[row + 1])
+    assert b - a >= 2
+    use_l2g = False
+    if fault == "first_offset":
+        off[0] = 1
+    elif fault == "decreasing":
+        off[row + 1] = off[row] - 1
+    elif fault == "too_many":
+        nl = int(off[-1]) - 1
+    elif fault == "id_negative":
+        ids[a] = -1
+    elif fault == "id_high":
+        ids[a] = nl
+    elif fault == "descending":
+        ids[a], ids[a + 1] = ids[a + 1], ids[a]
+    elif fault == "repeated":
+        ids[a + 1] = ids[a]
+    elif fault == "wrong_row":
+        # a well-formed CSR that is not the transpose of this l2g
+        j = int(off[row + 1])
+        ids[a], ids[j] = ids[j], ids[a]
+        ids[a:b] = np.sort(ids[a:b])
+        use_l2g = True
+    elif fault == "missing":
+        # drop the last entry of the last row: still well formed, but not the whole transpose
+        off[-1] -= 1
+        use_l2g = True
+    with pytest.raises(bs.BSError) as e:
+        bs.bs_validate_g2l(off, ids, nl, l2g if use_l2g else None)
+    assert e.value.status == bs.BS_EINVAL
+
+
+def test_validate_plan(bs):
+    l2g, ng, off, ids = _tables(bs)
+    for npb in (1, 5, 300, 1024):
+        bs.bs_validate_plan(bs.bs_gather_plan(off, npb), ng)
+    plan = bs.bs_gather_plan(off, 64)
+    bad = [plan.copy() for _ in range(4)]
+    bad[0][0] = 1
+    bad[1][-1] = ng - 1
+    bad[2][3] = bad[2][2]
+    bad[3][2], bad[3][3] = bad[3][3], bad[3][2]
+    for p in bad:
+        with pytest.raises(bs.BSError):
+            bs.bs_validate_plan(p, ng)
+    with pytest.raises(bs.BSError):
+        bs.bs_validate_plan(plan, ng + 1)
+    bs.bs_validate_plan(np.zeros(1, dtype=np.int32), 0)
+    L = bs._lib()
+    assert L.bs_validate_plan(2 ** 31 - 1, plan.ctypes.data, 1) == bs.BS_ERANGE
+    assert L.bs_validate_plan(ng, None, 1) == bs.BS_EINVAL
