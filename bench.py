@@ -372,21 +372,32 @@ def sweep_summary(fits):
                  f["plateau_GBps"]] for op, f in fits.items()}
 
 
-def tet_split_tables(bs, cubes, N, seed):
+def tet_split_tables(bs, cubes, N, seed, order="gen"):
     """I_l->g of the unstructured tet-split mesh (cubes^3 unit cubes, 24
-    hexahedra each, every element in a random orientation)."""
-    ev, nv, _ = bs_inputs.hex_tet_split(cubes, cubes, cubes)
+    hexahedra each, every element in a random orientation), with its elements
+    stored in the generator's order (cube by cube, x fastest: "gen"), in a
+    random order, as a mesh file might present them ("shuffled"), or in that
+    random order put back along the library's Hilbert curve through the
+    element centroids (bs_mesh_hex_order: "curve"). Global ids are numbered by
+    first appearance in storage order, so they follow the element order."""
+    ev, nv, coords = bs_inputs.hex_tet_split(cubes, cubes, cubes)
     ev, _ = bs_inputs.hex_orient(ev, seed)
+    if order in ("shuffled", "curve"):
+        ev = np.ascontiguousarray(ev[bs_inputs.permutation(seed + 1, len(ev))])
+    if order == "curve":
+        ev = np.ascontiguousarray(ev[bs.bs_mesh_hex_order(coords[ev])])
     return bs.bs_mesh_hex_l2g(ev, N, nv)
 
 
-WORKLOADS = ["shuffled40_N5", "tetsplit11_N7", "slab32x32x4_N7", "box24_N15", "cg_box32_N7"]
+WORKLOADS = ["shuffled40_N5", "tetsplit11_N7", "tetsplit11_N7_shuffled", "tetsplit11_N7_curve", "slab32x32x4_N7",
+             "box24_N15", "cg_box32_N7"]
 
 
 def workloads(bs, torch, dev, gather_lds, steps=30, only=None):
     """The shuffled 40^3 order-5 mesh (scatter, gather), the unstructured
     tet-split mesh of 11^3 cubes (31944 hexahedra) at order 7 (scatter,
-    gather), one GPU's share of the 32^3 order-7 mesh cut into eight z-slabs
+    gather) with its elements in the generator's order, in a random order,
+    and in that random order put back along the Hilbert curve, one GPU's share of the 32^3 order-7 mesh cut into eight z-slabs
     (32 x 32 x 4 elements, all 7 ops, and the CG streaming sequence, whose
     device-resident iteration there fits in the last-level cache), the 24^3
     order-15 mesh (all 7 ops, and the CG streaming sequence) and the CG
@@ -396,6 +407,8 @@ def workloads(bs, torch, dev, gather_lds, steps=30, only=None):
     out = {}
     for name, E, N, ops in [("shuffled40_N5", 40, 5, ["scatter", "gather"]),
                             ("tetsplit11_N7", 11, 7, ["scatter", "gather"]),
+                            ("tetsplit11_N7_shuffled", 11, 7, ["scatter", "gather"]),
+                            ("tetsplit11_N7_curve", 11, 7, ["scatter", "gather"]),
                             ("slab32x32x4_N7", 32, 7, OPS),
                             ("box24_N15", 24, 15, OPS),
                             ("cg_box32_N7", 32, 7, [])]:
@@ -403,11 +416,14 @@ def workloads(bs, torch, dev, gather_lds, steps=30, only=None):
             continue
         tables = None
         if name.startswith("tetsplit"):
-            tables = tet_split_tables(bs, E, N, bs_inputs.base_seed(name) + bs_inputs.SEED_ELEM)
+            tables = tet_split_tables(bs, E, N, bs_inputs.base_seed("tetsplit11_N7") + bs_inputs.SEED_ELEM,
+                                      order={"tetsplit11_N7_shuffled": "shuffled",
+                                             "tetsplit11_N7_curve": "curve"}.get(name, "gen"))
         elif name.startswith("slab"):
             tables = (bs.bs_mesh_box_l2g(E, E, 4, N), bs.bs_mesh_box_count(E, E, 4, N)[1])
         # the CG-only workload runs on the step's own mesh and inputs
-        m = Mesh(bs, torch, dev, "box32_N7" if name == "cg_box32_N7" else name, E, N, gather_lds, tables=tables)
+        src = "box32_N7" if name == "cg_box32_N7" else "tetsplit11_N7" if name.startswith("tetsplit") else name
+        m = Mesh(bs, torch, dev, src, E, N, gather_lds, tables=tables)
         if tables is not None:
             out[name + "_mesh"] = {"elements": 24 * E ** 3 if name.startswith("tetsplit") else E * E * 4, "order": N,
                                    "n_local": m.nl, "n_global": m.ng}

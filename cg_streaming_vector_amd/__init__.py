@@ -72,6 +72,7 @@ SIGNATURES = {
     "bs_mesh_box_l2g": ([_int, _int, _int, _int, _ptr, _ptr, _ptr], _int),
     "bs_mesh_hex_l2g": ([_i64, _int, _i64, _ptr, _ptr, ctypes.POINTER(_i64)], _int),
     "bs_mesh_hex_mass": ([_i64, _int, _ptr, _ptr], _int),
+    "bs_mesh_hex_order": ([_i64, _ptr, _ptr], _int),
     "bs_validate_l2g": ([_i64, _i64, _ptr], _int),
     "bs_validate_g2l": ([_i64, _i64, _ptr, _ptr, _ptr], _int),
     "bs_validate_plan": ([_i64, _ptr, _i64], _int),
@@ -479,6 +480,19 @@ def bs_mesh_hex_mass(xe, order):
     return w
 
 
+def bs_mesh_hex_order(xe):
+    """Element storage order along a Hilbert curve through the centroids of
+    hexahedra given by corner coordinates xe (float64[n_elements, 8, 3]):
+    int32 perm, perm[s] = the element for slot s."""
+    xe = np.ascontiguousarray(xe)
+    if xe.dtype != np.float64 or xe.size % 24:
+        raise TypeError("xe must be float64 with 8 x 3 coordinates per element")
+    E = xe.size // 24
+    perm = np.empty(max(E, 1), dtype=np.int32)
+    _check(_lib().bs_mesh_hex_order(E, xe.ctypes.data, perm.ctypes.data), "bs_mesh_hex_order")
+    return perm[:E]
+
+
 def bs_validate_l2g(l2g, n_global):
     l2g = _host_i32(l2g, "l2g")
     _check(_lib().bs_validate_l2g(l2g.size, int(n_global), l2g.ctypes.data), "bs_validate_l2g")
@@ -592,5 +606,5 @@ __all__ = [
     "bs_copy", "bs_axpy", "bs_norm", "bs_dot", "bs_cg_update", "bs_scatter", "bs_gather",
     "bs_gather_dot", "bs_cg_solve", "bs_cg_solve_static", "bs_scale", "bs_gll", "bs_mesh_box_mass",
     "bs_bench_loop", "BS_OP", "BS_BENCH_SET",
-    "bs_mesh_box_count", "bs_mesh_box_l2g", "bs_mesh_hex_l2g", "bs_mesh_hex_mass", "bs_validate_l2g", "bs_validate_g2l", "bs_validate_plan", "bs_index_g2l", "bs_gather_plan",
+    "bs_mesh_box_count", "bs_mesh_box_l2g", "bs_mesh_hex_l2g", "bs_mesh_hex_mass", "bs_mesh_hex_order", "bs_validate_l2g", "bs_validate_g2l", "bs_validate_plan", "bs_index_g2l", "bs_gather_plan",
 ]

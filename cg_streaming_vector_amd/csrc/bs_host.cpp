@@ -92,9 +92,87 @@ FaceKey face_key(const int32_t *v, int f)
     return k;
 }
 
+// Bits per axis of the Hilbert curve that orders elements: 3 x 21 = 63 bits.
+constexpr int kHilbertBits = 21;
+
+// Position along the 3D Hilbert curve of the cell with integer coordinates
+// X (each below 2^kHilbertBits), after J. Skilling, "Programming the Hilbert
+// curve" (AIP Conf. Proc. 707, 2004): the coordinates are transformed in
+// place into the "transposed" curve index (a sequence of inversions and
+// exchanges of their low bits, level by level from the top, then a Gray
+// code), whose bits, read across the three words from the most significant
+// level down, form the index.
+uint64_t hilbert_index(uint32_t X[3])
+{
+    constexpr uint32_t top = 1u << (kHilbertBits - 1);
+    for (uint32_t Q = top; Q > 1; Q >>= 1) {
+        const uint32_t P = Q - 1;
+        for (int i = 0; i < 3; ++i) {
+            if (X[i] & Q) {
+                X[0] ^= P;  // invert the low bits of the first axis
+            } else {
+                const uint32_t t = (X[0] ^ X[i]) & P;  // exchange low bits with it
+                X[0] ^= t;
+                X[i] ^= t;
+            }
+        }
+    }
+    for (int i = 1; i < 3; ++i) X[i] ^= X[i - 1];
+    uint32_t t = 0;
+    for (uint32_t Q = top; Q > 1; Q >>= 1)
+        if (X[2] & Q) t ^= Q - 1;
+    for (int i = 0; i < 3; ++i) X[i] ^= t;
+    uint64_t key = 0;
+    for (int j = kHilbertBits - 1; j >= 0; --j)
+        for (int i = 0; i < 3; ++i) key = key << 1 | ((X[i] >> j) & 1u);
+    return key;
+}
+
 }  // namespace
 
 extern "C" {
+
+int bs_mesh_hex_order(int64_t n_elements, const double *xe, int32_t *perm)
+{
+    if (n_elements < 0 || (n_elements > 0 && (!xe || !perm))) return BS_EINVAL;
+    if (n_elements > INT32_MAX) return BS_ERANGE;
+    const int64_t E = n_elements;
+    try {
+        std::vector<double> c((size_t)E * 3);
+        double lo[3] = {INFINITY, INFINITY, INFINITY}, hi[3] = {-INFINITY, -INFINITY, -INFINITY};
+        for (int64_t e = 0; e < E; ++e) {
+            for (int a = 0; a < 3; ++a) {
+                double s = 0.0;
+                for (int k = 0; k < 8; ++k) s += xe[24 * e + 3 * k + a];
+                s /= 8.0;
+                if (!std::isfinite(s)) return BS_EINVAL;
+                c[(size_t)(3 * e + a)] = s;
+                lo[a] = std::min(lo[a], s);
+                hi[a] = std::max(hi[a], s);
+            }
+        }
+        // one scale for all axes (cubic cells) over the widest extent
+        double extent = 0.0;
+        for (int a = 0; a < 3; ++a) extent = std::max(extent, hi[a] - lo[a]);
+        const double cells = (double)((1u << kHilbertBits) - 1);
+        const double scale = extent > 0.0 ? cells / extent : 0.0;
+        std::vector<std::pair<uint64_t, int32_t>> key((size_t)E);
+        for (int64_t e = 0; e < E; ++e) {
+            uint32_t X[3];
+            for (int a = 0; a < 3; ++a) {
+                const double q = std::floor((c[(size_t)(3 * e + a)] - lo[a]) * scale);
+                X[a] = (uint32_t)std::min(std::max(q, 0.0), cells);
+            }
+            key[(size_t)e] = {hilbert_index(X), (int32_t)e};
+        }
+        // ties (equal cells) keep the elements' own order
+        std::sort(key.begin(), key.end());
+        for (int64_t s = 0; s < E; ++s) perm[s] = key[(size_t)s].second;
+    } catch (const std::bad_alloc &) {
+        return BS_ENOMEM;
+    }
+    return BS_OK;
+}
 
 int bs_mesh_box_count(int ex, int ey, int ez, int order, int64_t *n_local, int64_t *n_global)
 {

@@ -270,6 +270,21 @@ int bs_mesh_box_l2g(int ex, int ey, int ez, int order, const int32_t *elem_perm,
 int bs_mesh_hex_l2g(int64_t n_elements, int order, int64_t n_vertices, const int32_t *ev,
                     int32_t *l2g, int64_t *n_global);
 
+/* A storage order for the elements of an unstructured hex mesh that keeps
+ * neighbours near in memory (arXiv 2009.10917, the gather paragraph: local
+ * spatial locality of the elements helps the reads of the local vector;
+ * arXiv 1506.05996, the mesh-setup tables): the elements sorted along a 3D
+ * Hilbert curve through their centroids (J. Skilling, "Programming the
+ * Hilbert curve", AIP Conf. Proc. 707, 2004), on a grid of 2^21 cells per
+ * axis over the centroids' bounding cube; elements in one cell keep their
+ * order. perm receives int32[n_elements]: perm[s] is the element to store in
+ * slot s. Reorder the corner vertices (and coordinates) by it before
+ * bs_mesh_hex_l2g, whose first-appearance numbering then makes the global
+ * ids follow the curve too. xe as for bs_mesh_hex_mass. BS_EINVAL: NULL with
+ * n_elements > 0, n_elements < 0, a non-finite coordinate; BS_ERANGE:
+ * n_elements > INT32_MAX; BS_ENOMEM: no host memory. */
+int bs_mesh_hex_order(int64_t n_elements, const double *xe, int32_t *perm);
+
 /* Gauss-Lobatto-Legendre points and weights of degree `order` on [-1, 1]:
  * nodes double[order+1] ascending (the end points and the roots of P_order'),
  * weights double[order+1], w_i = 2 / (order (order+1) P_order(r_i)^2). These

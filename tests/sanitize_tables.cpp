@@ -143,6 +143,13 @@ void hex_mesh(const std::string &dir, const std::string &name, int64_t E, int64_
     CHECK(or_mesh_hex(E, p, nv, ev.data(), ol2g.data()) == ng);
     CHECK(l2g == ol2g);
     check_tables(l2g, ng);
+    // the Hilbert order of the elements is a permutation
+    std::vector<int32_t> order((size_t)E), seen((size_t)E, 0);
+    CHECK(bs_mesh_hex_order(E, xe.data(), order.data()) == BS_OK);
+    for (int32_t e : order) {
+        CHECK(e >= 0 && e < E && !seen[(size_t)e]);
+        seen[(size_t)e] = 1;
+    }
     std::vector<double> w((size_t)nl), ow((size_t)nl);
     CHECK(bs_mesh_hex_mass(E, p, xe.data(), w.data()) == BS_OK);
     CHECK(or_mesh_hex_mass(E, p, xe.data(), ow.data()) == 0);

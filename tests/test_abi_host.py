@@ -490,3 +490,50 @@ def test_validate_plan(bs):
     L = bs._lib()
     assert L.bs_validate_plan(2 ** 31 - 1, plan.ctypes.data, 1) == bs.BS_ERANGE
     assert L.bs_validate_plan(ng, None, 1) == bs.BS_EINVAL
+
+
+# --------------------------------------------- element order along a curve --
+
+@pytest.mark.parametrize("n", [2, 4, 8, 16])
+def test_hex_order_is_a_hilbert_walk_on_power_of_two_lattices(bs, n):
+    """On a lattice of 2^k unit cubes the Hilbert curve visits the cubes one
+    face neighbour after another (a Z-order curve would jump); the order is a
+    permutation."""
+    xe = bs_inputs.hex_box_coords(n, n, n)
+    perm = bs.bs_mesh_hex_order(xe)
+    assert np.array_equal(np.sort(perm), np.arange(n ** 3))
+    c = xe.mean(axis=1)[perm]
+    steps = np.abs(np.diff(c, axis=0)).sum(axis=1)
+    assert np.all(steps == 1.0)
+
+
+def test_hex_order_depends_only_on_the_centroids(bs):
+    ev, nv, coords = bs_inputs.hex_tet_split(3, 3, 2)
+    xe = coords[ev]
+    perm = bs.bs_mesh_hex_order(xe)
+    c = xe.mean(axis=1)
+    # corners presented in other orders, elements shuffled: the same walk
+    ev2, sym = bs_inputs.hex_orient(ev, 77)
+    shuffle = bs_inputs.permutation(78, len(ev))
+    xe2 = bs_inputs.reorder_corners(xe, sym)[shuffle]
+    perm2 = bs.bs_mesh_hex_order(xe2)
+    assert np.allclose(xe2.mean(axis=1)[perm2], c[perm], rtol=0, atol=1e-12)
+    # it keeps neighbours closer than the generator's order does
+    step = lambda cc: np.sqrt((np.diff(cc, axis=0) ** 2).sum(axis=1)).mean()  # noqa: E731
+    assert step(c[perm]) < step(c)
+
+
+def test_hex_order_edge_cases(bs):
+    assert bs.bs_mesh_hex_order(np.zeros((0, 8, 3))).size == 0
+    one = bs_inputs.hex_box_coords(1, 1, 1)
+    assert list(bs.bs_mesh_hex_order(one)) == [0]
+    same = np.repeat(one, 5, axis=0)  # all in one cell: the input order stays
+    assert list(bs.bs_mesh_hex_order(same)) == [0, 1, 2, 3, 4]
+    bad = bs_inputs.hex_box_coords(2, 1, 1)
+    bad[1, 3, 2] = np.nan
+    with pytest.raises(bs.BSError) as e:
+        bs.bs_mesh_hex_order(bad)
+    assert e.value.status == bs.BS_EINVAL
+    L = bs._lib()
+    assert L.bs_mesh_hex_order(3, None, None) == bs.BS_EINVAL
+    assert L.bs_mesh_hex_order(-1, None, None) == bs.BS_EINVAL

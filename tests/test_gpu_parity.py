@@ -689,15 +689,19 @@ def unstructured_case(env, kind):
     """A mesh with arbitrary element orientation: the library builds the
     tables it runs on, the oracle builds its own from the same corners."""
     bs, orc, torch, d = env
-    if kind == "tet_split":
-        ev, nv, _ = bs_inputs.hex_tet_split(6, 5, 6)  # 4320 hexahedra, not a lattice
+    if kind in ("tet_split", "tet_split_curve"):
+        ev, nv, coords = bs_inputs.hex_tet_split(6, 5, 6)  # 4320 hexahedra, not a lattice
         N = 5
     else:
         ev, nv = bs_inputs.hex_box(16, 16, 12, periodic=(True, True, True))
         N = 7
     ev, _ = bs_inputs.hex_orient(ev, 701)
+    if kind == "tet_split_curve":
+        # stored along the library's Hilbert curve; both builders get the same corners
+        ev = np.ascontiguousarray(ev[bs.bs_mesh_hex_order(coords[ev])])
     ev, nv = bs_inputs.hex_relabel(ev, nv, 702, spare=5)
-    ev = ev[bs_inputs.permutation(703, len(ev))]
+    if kind != "tet_split_curve":
+        ev = ev[bs_inputs.permutation(703, len(ev))]
     l2g, ng = bs.bs_mesh_hex_l2g(ev, N, nv)
     off, ids = bs.bs_index_g2l(l2g, ng)
     ol2g, ong = orc.mesh_hex(ev, N, nv)
@@ -705,7 +709,7 @@ def unstructured_case(env, kind):
     return l2g, off, ids, ol2g, ng
 
 
-@pytest.mark.parametrize("kind", ["tet_split", "torus"])
+@pytest.mark.parametrize("kind", ["tet_split", "tet_split_curve", "torus"])
 def test_unstructured_scatter_gather(env, kind):
     bs, orc, torch, d = env
     l2g, off, ids, ol2g, ng = unstructured_case(env, kind)
@@ -749,7 +753,8 @@ def test_unstructured_cg_solve(env):
     check_cg(h, ohist, host(x), ox, m, b, iters, "tet-split")
 
 
-def test_unstructured_cg_solve_handoff(env):
+@pytest.mark.parametrize("curve", [False, True])
+def test_unstructured_cg_solve_handoff(env, curve):
     """The device CG on the benchmark's tet-split mesh (11^3 cubes, 31944
     randomly oriented hexahedra, order 7: 11.1M global nodes). Its vectors and
     tables exceed the 256 MB last-level cache while r and p (177 MB) fit, so
@@ -757,8 +762,10 @@ def test_unstructured_cg_solve_handoff(env):
     and oracle build their own tables from the same corners; the residual
     history follows the oracle's CG and x reaches b / m."""
     bs, orc, torch, d = env
-    ev, nv, _ = bs_inputs.hex_tet_split(11, 11, 11)
+    ev, nv, coords = bs_inputs.hex_tet_split(11, 11, 11)
     ev, _ = bs_inputs.hex_orient(ev, 731)
+    if curve:  # the element order the benchmark's tet-split workload uses
+        ev = np.ascontiguousarray(ev[bs.bs_mesh_hex_order(coords[ev])])
     N = 7
     l2g, ng = bs.bs_mesh_hex_l2g(ev, N, nv)
     ol2g, ong = orc.mesh_hex(ev, N, nv)
@@ -775,7 +782,16 @@ def test_unstructured_cg_solve_handoff(env):
     q = torch.empty(ng, dtype=torch.float64, device=d)
     pl = torch.empty(l2g.size, dtype=torch.float64, device=d)
     h = host(bs.bs_cg_solve(t["l2g"], t["off"], t["ids"], x, r, p, q, pl, iters, 0.0, t["plan"]))
-    check_cg(h, ohist, host(x), ox, m, b, iters, "tet-split 11^3")
+    check_cg(h, ohist, host(x), ox, m, b, iters, f"tet-split 11^3 curve={curve}")
+    # scatter and gather on the same tables, as the benchmark launches them
+    vgv = bs_inputs.uniform_pm1(733, ng)
+    vl = torch.empty(l2g.size, dtype=torch.float64, device=d)
+    bs.bs_scatter(t["l2g"], dev(torch, d, vgv), vl)
+    assert_bits(host(vl), orc.scatter(ol2g, vgv), "scatter")
+    vlv = bs_inputs.uniform_pm1(734, l2g.size)
+    vg = torch.full((ng,), np.nan, dtype=torch.float64, device=d)
+    bs.bs_gather(t["off"], t["ids"], dev(torch, d, vlv), vg, t["plan"])
+    assert_bits(host(vg), orc.gather(ol2g, vlv, ng), "gather")
 
 
 # -------------------------------------------------------- launch loop -----
