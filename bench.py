@@ -288,10 +288,8 @@ def cpu_baseline(mesh_host, budget_s=12.0, budget_1_thread_s=4.0):
         affinity = None
     return {"value": round(nb * reps / t / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{reps} steps of 32^3 N=7 (7 ops), {t:.1f} s on {threads} OpenMP threads, {model[:24]}",
-            "omp_threads": threads, "affinity_cpus": affinity,
-            "value_1_thread": round(nb * reps1 / t1 / 1e9, 3),
-            "sample_1_thread": f"{reps1} steps, {t1:.1f} s, 1 thread"}
+            "sample": f"{reps} steps (7 ops, 32^3 N=7), {t:.1f} s, {threads} OpenMP threads, {model[:16]}",
+            "affinity_cpus": affinity, "value_1_thread": round(nb * reps1 / t1 / 1e9, 3)}
 
 
 SWEEP_OPS = ["copy", "axpy", "norm", "dot", "cg_update"]
@@ -528,11 +526,11 @@ def workload_summary(wl):
     """Compact figures of the other workloads for the JSON line: per mesh and
     operation [us, % of 8 TB/s]; per CG sequence [device-resident, host-driven
     with fixed scalars, true CG with readbacks] in us per iteration, and the
-    device-resident iteration's GB/s of bytes actually moved. The slab share's
-    per-operation figures stay in --out."""
+    device-resident iteration's GB/s of bytes actually moved."""
     out = {}
     for name, r in wl.items():
-        if name.endswith("_mesh") or name.startswith("slab"):
+        # the slab share and the tet-split mesh in other element orders stay in --out
+        if name.endswith("_mesh") or "slab" in name or name.endswith(("_shuffled", "_curve")):
             continue
         if name.startswith("cg_sequence_"):
             out["cg_" + name[len("cg_sequence_"):].replace("cg_", "")] = [
@@ -540,7 +538,7 @@ def workload_summary(wl):
                 r["device_cg_GBps_moved"]]
         else:
             out[name] = {op: [v["us"], v["pct_peak"]] for op, v in r.items()}
-    out["fields"] = "mesh: op -> [us, pct_peak]; cg_*: [device us/iter, fixed-scalar us/iter, true-CG us/iter, device GB/s]"
+    out["fields"] = "op: [us, %peak]; cg_*: [device, fixed-scalar, true-CG us/iter, device GB/s]"
     return out
 
 
@@ -683,8 +681,7 @@ def main():
         "per_op_fields": PER_OP_FIELDS,
         "runtime_copy_GBps": round(rt_copy, 1),
         "copy_ceiling_GBps": round(ceiling, 1) if ceiling else None,
-        "per_op_note": f"us: median of {args.trials} x {args.per_op_reps} launches (C++ loop, host clock) over "
-                       f"{args.rotate} rotated sets; hot_us: one set; ceiling: our copy of 2^28 doubles",
+        "per_op_note": f"median of {args.trials}x{args.per_op_reps} launches, {args.rotate} cold sets; hot: 1 set",
         "roofline": roofline,
     }
 
@@ -698,8 +695,7 @@ def main():
         extra["sweep"] = fits
         line["sweep_fit"] = sweep_summary(fits)
         line["sweep_fit_fields"] = SWEEP_FIELDS
-        line["sweep_fit_note"] = (f"n=2^10..2^28 ({args.sweep_layout} layout); eq. 8 fit by relative error; "
-                                  "plateau: median GB/s of points >= 0.5 GB")
+        line["sweep_fit_note"] = f"n=2^10..2^28 ({args.sweep_layout}); eq. 8; plateau: median of >= 0.5 GB"
         wl = workloads(bs, torch, dev, args.gather == "lds")
         extra["workloads"] = wl
         line["workloads"] = workload_summary(wl)
