@@ -70,6 +70,78 @@ def op_bytes(op, n=0, nl=0, ng=0):
     }[op]
 
 
+class TimingEvents:
+    """Pairs of HIP events for timing kernels only, created through the HIP
+    runtime the process has loaded (the one torch and libbs share) with
+    hipEventDisableSystemFence: recording such an event performs no
+    system-scope fence, so the timed kernel pays no cache write-back or
+    invalidation for being measured. (torch.cuda.Event has no such flag;
+    fence="system" uses its events instead, for comparison.)"""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence
+
+    def __init__(self, torch, count, fence="none"):
+        import ctypes
+        self.torch, self.fence = torch, fence
+        if fence == "system":
+            self.pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                          for _ in range(count)]
+            cur = torch.cuda.current_stream()
+            for a, b in self.pairs:  # create them
+                a.record(cur)
+                b.record(cur)
+            return
+        path = next(line.split()[-1] for line in open("/proc/self/maps") if "libamdhip64" in line)
+        self.hip = ctypes.CDLL(path)
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        self.pairs = []
+        for _ in range(count):
+            pair = []
+            for _ in range(2):
+                h = ctypes.c_void_p()
+                if self.hip.hipEventCreateWithFlags(ctypes.byref(h), self.DISABLE_SYSTEM_FENCE) != 0:
+                    raise RuntimeError("hipEventCreateWithFlags failed")
+                # recorded once here, so that the runtime's first-use work on
+                # an event happens before the timed region, not inside it
+                if self.hip.hipEventRecord(h, stream) != 0:
+                    raise RuntimeError("hipEventRecord failed")
+                pair.append(h)
+            self.pairs.append(tuple(pair))
+
+    def arm(self, ctx, i):
+        """The next kernel ctx launches records pair i at its start and end."""
+        a, b = self.pairs[i]
+        if self.fence == "system":
+            ctx.time_next(a, b)
+        else:
+            import cg_streaming_vector_amd as bs
+            bs._check(bs._lib().bs_ctx_time_next(ctx.handle, a, b), "bs_ctx_time_next")
+
+    def mean_seconds(self):
+        """Average kernel time over the pairs (call after the stream has synchronised)."""
+        import ctypes
+        if self.fence == "system":
+            return float(np.mean([a.elapsed_time(b) for a, b in self.pairs])) * 1e-3
+        ms = []
+        for a, b in self.pairs:
+            f = ctypes.c_float()
+            if self.hip.hipEventElapsedTime(ctypes.byref(f), a, b) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            ms.append(f.value)
+        return float(np.mean(ms)) * 1e-3
+
+    def close(self):
+        if self.fence != "system":
+            for pair in self.pairs:
+                for h in pair:
+                    self.hip.hipEventDestroy(h)
+        self.pairs = []
+
+
 def kernel_source_sha():
     path = os.path.join(ROOT, "cg_streaming_vector_amd", "csrc", "bs_kernels.hip")
     return hashlib.sha256(open(path, "rb").read()).hexdigest()
@@ -555,6 +627,9 @@ def main():
                     help="arena: each set's arrays packed in one allocation on 2 MB boundaries")
     ap.add_argument("--per-op-reps", type=int, default=96)
     ap.add_argument("--trials", type=int, default=5, help="per-op loops repeated; the median is reported")
+    ap.add_argument("--event-fence", choices=["none", "system"], default="none",
+                    help="timing events of the dominant kernel: none = created with hipEventDisableSystemFence, "
+                         "system = torch's events (a system-scope fence each)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the size sweep and the other workloads (profiling runs of the step)")
     ap.add_argument("--sweep-layout", choices=["arena", "torch"], default="arena",
@@ -613,24 +688,22 @@ def main():
         for op in OPS:
             step_launch[w % len(sets)][op]()
     cur = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range((args.steps + EVENT_STRIDE - 1) // EVENT_STRIDE)]
-    for a, b in ev:  # create them
-        a.record(cur)
-        b.record(cur)
+    ev = TimingEvents(torch, (args.steps + EVENT_STRIDE - 1) // EVENT_STRIDE, args.event_fence)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
         run = step_launch[k % len(sets)]
         for op in OPS:
             if op == dom and k % EVENT_STRIDE == 0:
-                ctx.time_next(*ev[k // EVENT_STRIDE])
+                ev.arm(ctx, k // EVENT_STRIDE)
             run[op]()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     del step_launch, sets
     torch.cuda.empty_cache()
-    dom_live = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    dom_live = ev.mean_seconds()
+    n_timed = len(ev.pairs)
+    ev.close()
     ms_step = dt / args.steps * 1e3
     value = step_bytes / (dt / args.steps) / 1e9
 
@@ -648,7 +721,8 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
                 "op": dom, "kernel": " + ".join(KERNEL_NAME[dom]), "bytes_per_launch": mesh.bytes(dom),
-                "us_per_launch": round(dom_live * 1e6, 2), "launches_timed": len(ev)}
+                "us_per_launch": round(dom_live * 1e6, 2), "launches_timed": n_timed,
+                "event_fence": args.event_fence}
 
     # the runtime's own device-to-device copy at this size, on rotated buffers
     R = args.rotate
