@@ -217,7 +217,9 @@ int bs_cg_solve(bs_ctx *ctx, int64_t n_global, int64_t n_local, const int32_t *l
  * and give wrong results; order them. A gather with more than 131072 blocks
  * (block_starts with n_blocks > 131072, or n_global > 67108864 without a
  * plan) is BS_ERANGE, with nothing enqueued. BS_EHIP if the device or the
- * array's address cannot be queried. */
+ * array's address cannot be queried; BS_EINVAL on a device numbered 64 or
+ * above. Make the first call on a device outside stream capture, or accept
+ * that its one-time address lookup happens inside it. */
 int bs_cg_solve_static(int64_t n_global, int64_t n_local, const int32_t *l2g, const int32_t *off,
                        const int32_t *ids, const int32_t *block_starts, int64_t n_blocks, double *x, double *r,
                        double *p, double *q, double *p_local, int iters, double tol, double *rr_hist,

@@ -95,3 +95,39 @@ def test_static_solve_refuses_more_gather_blocks_than_it_holds(env):
     want, got = solve(bs, torch, d, small, False, True, 3), solve(bs, torch, d, small, True, True, 3)
     assert got[0] == 0
     same_bits(got[4], want[4], "rr_hist after a refused call")
+
+
+def test_static_solve_under_graph_capture(env):
+    """What the allocation-free solve is for: a caller that captures the solve
+    into a HIP graph (nothing in it allocates, and its counters are cleared by
+    a kernel, not a memset). The graph is replayed several times, with eager
+    work (resetting x, r, p) and synchronisations between the replays; every
+    replay matches the eager solve bit for bit."""
+    bs, torch, d = env
+    for dims, N, seed, iters in [((8, 8, 8), 3, 3201, 4), ((16, 16, 12), 5, 3202, 5)]:
+        m = mesh(bs, torch, d, dims, N, seed)
+        want = solve(bs, torch, d, m, True, True, iters)  # eager; also the first call's set-up
+        assert want[0] == 0
+        s = torch.cuda.Stream()
+        x = torch.zeros(m["ng"], dtype=torch.float64, device=d)
+        r, p = m["b"].clone(), m["b"].clone()
+        q = torch.empty(m["ng"], dtype=torch.float64, device=d)
+        pl = torch.empty(m["nl"], dtype=torch.float64, device=d)
+        h = torch.empty(iters + 1, dtype=torch.float64, device=d)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            bs.bs_cg_solve_static(m["l2g"], m["off"], m["ids"], x, r, p, q, pl, iters, h,
+                                  block_starts=m["plan"], stream=torch.cuda.current_stream())
+        for rep in range(3):
+            x.zero_()
+            r.copy_(m["b"])
+            p.copy_(m["b"])
+            h.fill_(np.nan)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            same_bits(h.cpu().numpy(), want[4], f"rr_hist replay {rep} {dims}")
+            same_bits(x.cpu().numpy(), want[1], f"x replay {rep} {dims}")
+            same_bits(r.cpu().numpy(), want[2], f"r replay {rep} {dims}")
+        del g
