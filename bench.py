@@ -60,7 +60,7 @@ KERNEL_NAME = {  # op -> its kernels as rocprofv3 names them (namespace and argu
 }
 GATHER_NPB = 1024
 PER_OP_FIELDS = ["bytes", "us", "us_best", "GBps", "pct_peak", "pct_copy_ceiling", "hot_us"]
-EVENT_STRIDE = 4  # timed steps per step whose dominant kernel records events
+EVENT_STRIDE = 4  # default: timed steps per step whose dominant kernel records events
 
 
 def op_bytes(op, n=0, nl=0, ng=0):
@@ -630,6 +630,8 @@ def main():
     ap.add_argument("--event-fence", choices=["none", "system"], default="none",
                     help="timing events of the dominant kernel: none = created with hipEventDisableSystemFence, "
                          "system = torch's events (a system-scope fence each)")
+    ap.add_argument("--event-stride", type=int, default=EVENT_STRIDE,
+                    help="the dominant kernel records its timing events in every this many timed steps")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the size sweep and the other workloads (profiling runs of the step)")
     ap.add_argument("--sweep-layout", choices=["arena", "torch"], default="arena",
@@ -680,22 +682,23 @@ def main():
     # as in the per-operation loops. In every EVENT_STRIDE-th step the
     # dominant kernel records a pair of HIP events at its own start and end
     # (the library launches it with them, as armed by time_next), on its
-    # stream. A launch that records events costs its step about 8 us more
-    # (318 against 326 us per step with events in every step), so only a
-    # sample of the steps carries them.
+    # stream. The events are fence-free (TimingEvents); even so a timed
+    # launch costs its step about 1 us (events in every step: 319.9 against
+    # 319.2 us per step), so by default every fourth step carries them.
     step_launch = [m.launchers(bs, stream) for m in sets]
     for w in range(args.warmup):
         for op in OPS:
             step_launch[w % len(sets)][op]()
     cur = torch.cuda.current_stream()
-    ev = TimingEvents(torch, (args.steps + EVENT_STRIDE - 1) // EVENT_STRIDE, args.event_fence)
+    stride = args.event_stride
+    ev = TimingEvents(torch, (args.steps + stride - 1) // stride, args.event_fence)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
         run = step_launch[k % len(sets)]
         for op in OPS:
-            if op == dom and k % EVENT_STRIDE == 0:
-                ev.arm(ctx, k // EVENT_STRIDE)
+            if op == dom and k % stride == 0:
+                ev.arm(ctx, k // stride)
             run[op]()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
