@@ -91,7 +91,9 @@ class TimingEvents:
                 a.record(cur)
                 b.record(cur)
             return
-        path = next(line.split()[-1] for line in open("/proc/self/maps") if "libamdhip64" in line)
+        path = next((line.split()[-1] for line in open("/proc/self/maps") if "libamdhip64" in line), None)
+        if path is None:
+            raise RuntimeError("no HIP runtime (libamdhip64) is loaded; use --event-fence system")
         self.hip = ctypes.CDLL(path)
         self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
