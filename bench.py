@@ -418,19 +418,23 @@ def sweep(bs, torch, dev, reps_min=100, min_seconds=0.05, ks=range(10, 29), layo
             res[op].append((op_bytes(op, n), T))
         del sets
         torch.cuda.empty_cache()
+    return {op: sweep_fit(pts) for op, pts in res.items()}
+
+
+def sweep_fit(pts):
+    """Eq. 8 fitted to one operation's (bytes, seconds) points, with each
+    point's relative bandwidth residual (measured - model) / measured and the
+    measured plateau: the median GB/s of the points of at least 0.5 GB."""
     from cg_streaming_vector_amd.model import fit_streaming_model, w_eff
-    fits = {}
-    for op, pts in res.items():
-        B = np.array([p[0] for p in pts], dtype=np.float64)
-        T = np.array([p[1] for p in pts], dtype=np.float64)
-        f = fit_streaming_model(B, T)
-        W = B / T
-        resid = (W - w_eff(B, f["T0_s"], f["W_max"])) / W
-        big = W[B >= 0.5e9]
-        fits[op] = {"points": [[int(b), t] for b, t in pts], **f,
-                    "rel_residuals": [round(float(x), 4) for x in resid],
-                    "plateau_GBps": round(float(np.median(big)) / 1e9, 1) if big.size else None}
-    return fits
+    B = np.array([p[0] for p in pts], dtype=np.float64)
+    T = np.array([p[1] for p in pts], dtype=np.float64)
+    f = fit_streaming_model(B, T)
+    W = B / T
+    resid = (W - w_eff(B, f["T0_s"], f["W_max"])) / W
+    big = W[B >= 0.5e9]
+    return {"points": [[int(b), float(t)] for b, t in pts], **f,
+            "rel_residuals": [round(float(x), 4) for x in resid],
+            "plateau_GBps": round(float(np.median(big)) / 1e9, 1) if big.size else None}
 
 
 SWEEP_FIELDS = ["T0_us", "W_max_GBps", "B_08_MB", "r2", "max_abs_rel_residual", "plateau_GBps"]
