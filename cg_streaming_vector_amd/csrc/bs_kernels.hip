@@ -25,7 +25,7 @@
 //  - gather: the balanced blockStarts scheme of the paper, each block staging
 //    at most 1024 CSR entries of v_L in LDS with coalesced index loads, then
 //    one lane per global node summing its entries from LDS in ascending order,
-//    plan blocks handed to the XCDs in runs of four; without a plan, one lane
+//    plan blocks handed to the XCDs in runs of eight; without a plan, one lane
 //    per node with all of its loads issued up front.
 // Built from the same kernels: the pointwise scale y = x / d of the lumped
 // mass, and a device-resident CG iteration on Z^T Z whose scalars (alpha,
@@ -966,9 +966,12 @@ __global__ __launch_bounds__(kBlock) void k_gather_rows(int64_t ng, const int32_
 // neighbouring node blocks read neighbouring lines of v_L; so each XCD gets
 // runs of kXcdRun consecutive node blocks, while the eight XCDs still work in
 // one narrow window of the arrays. Workgroups past the last whole round keep
-// their own index. (Runs of 4 measured best: a few percent on unstructured
-// meshes, neutral on the boxes; one contiguous range per XCD was slower.)
-constexpr unsigned kXcds = 8, kXcdRun = 4;
+// their own index. Longer runs leave fewer v_L lines to be fetched by two
+// XCDs, shorter ones keep the window narrow: runs of 8 measured best (against
+// 4: equal on the 32^3 order-7 box, 1% faster on the tet-split mesh, 0.4% at
+// 24^3 order 15; runs of 16 and one contiguous range per XCD were slower on
+// the boxes).
+constexpr unsigned kXcds = 8, kXcdRun = 8;
 __device__ __forceinline__ unsigned gather_block()
 {
     constexpr unsigned span = kXcds * kXcdRun;
