@@ -11,6 +11,9 @@ read and 8n bytes written, and the ratio of that to what each counter reports
 is the scale applied to every other kernel's reading. On MI355X the read
 counter reports half the bytes of the copy and the write counter all of them.
 
+Any other counters (``--pmc`` files of several runs) are summarised as plain
+per-kernel averages per dispatch.
+
 Usage:
   python -m cg_streaming_vector_amd.profiling --stats S.csv --fetch F.csv \\
       --write W.csv --copy-kernel 'k_copy<1, 768>' --copy-doubles 11390625 \\
@@ -60,6 +63,33 @@ def load_counter(path, counter):
                 continue
             out.setdefault(short_name(row["Kernel_Name"]), []).append(float(row["Counter_Value"]))
     return out
+
+
+def load_counters(paths, kernels=None):
+    """kernel -> counter -> list of per-dispatch values, over several
+    *_counter_collection.csv files (one counter set per rocprofv3 run);
+    kernels, if given, keeps only those short names."""
+    out = {}
+    for path in paths:
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                k = short_name(row["Kernel_Name"])
+                if kernels and k not in kernels:
+                    continue
+                out.setdefault(k, {}).setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+    return out
+
+
+def counters_markdown(table, title, commands):
+    """Average per dispatch of every counter, one table per kernel."""
+    lines = [f"# {title}", "", "Commands:", ""]
+    lines += [f"    {c}" for c in commands]
+    for k in sorted(table):
+        lines += ["", f"`{k}`:", "", "| counter | dispatches | average per dispatch |", "|---|---|---|"]
+        for c in sorted(table[k]):
+            v = table[k][c]
+            lines.append(f"| {c} | {len(v)} | {statistics.fmean(v):.6g} |")
+    return "\n".join(lines) + "\n"
 
 
 def load_resources(path):
@@ -266,9 +296,21 @@ def main(argv=None):
     ap.add_argument("--calibration", help="summary JSON whose counter calibration to reuse")
     ap.add_argument("--in-step", action="append", default=[],
                     help="NAME=before|kernel|after: average of kernel's launches between those neighbours")
+    ap.add_argument("--pmc", action="append", default=[],
+                    help="*_counter_collection.csv of any counters: with --md, write their per-kernel averages")
+    ap.add_argument("--kernel", action="append", default=[], help="with --pmc: the kernels to keep (short names)")
     ap.add_argument("--json")
     ap.add_argument("--md")
     a = ap.parse_args(argv)
+    if a.pmc:
+        table = load_counters(a.pmc, set(a.kernel) or None)
+        if a.json:
+            with open(a.json, "w") as f:
+                json.dump({k: {c: statistics.fmean(v) for c, v in d.items()} for k, d in table.items()}, f, indent=1)
+        if a.md:
+            with open(a.md, "w") as f:
+                f.write(counters_markdown(table, a.title, a.command))
+        return
     ops = {o.split("=", 1)[0]: o.split("=", 1)[1].split("+") for o in a.op}
     cal = None
     if a.calibration:

@@ -354,7 +354,10 @@ int bs_index_g2l(int64_t n_local, int64_t n_global, const int32_t *l2g, int32_t 
  * section, BS6): rows are cut into consecutive blocks so that each thread
  * block reads and writes about the same amount: greedily, a block takes rows
  * while it holds at most nodes_per_block rows and at most nodes_per_block CSR
- * entries (a single longer row gets a block of its own). block_starts
+ * entries (a single longer row gets a block of its own). Every block but the
+ * last then ends on a multiple of 16 rows, rounding its greedy end down,
+ * unless no multiple of 16 lies after its first row: so each block writes
+ * whole 128-byte lines of a 128-byte-aligned v_global. block_starts
  * receives n_blocks+1 row indices (capacity n_global+1 suffices),
  * block_starts[0] = 0 and block_starts[n_blocks] = n_global.
  * nodes_per_block must be in [1, 1024] (BS_EINVAL): the gather kernel stages

@@ -183,6 +183,23 @@ def test_g2l_rejects_out_of_range(bs):
     bs.bs_validate_l2g(np.array([-1, 2], dtype=np.int32), 3)
 
 
+def plan_rule(off, npb):
+    """blockStarts by the documented rule, written out row by row: the
+    greedy end under both caps, then, for every block but the last, rounded
+    down to a multiple of 16 rows when that keeps the block non-empty."""
+    ng = len(off) - 1
+    starts, a = [0], 0
+    while a < ng:
+        b = a + 1
+        while b < ng and b - a < npb and off[b + 1] - off[a] <= npb:
+            b += 1
+        if b < ng and (b // 16) * 16 > a:
+            b = (b // 16) * 16
+        starts.append(b)
+        a = b
+    return starts
+
+
 @pytest.mark.parametrize("npb", [1, 8, 256, 512, 1000, 1024])
 def test_gather_plan(bs, npb):
     l2g = bs.bs_mesh_box_l2g(6, 5, 4, 3)
@@ -196,9 +213,10 @@ def test_gather_plan(bs, npb):
     # never above the target unless the block is one long row
     assert np.all((ent <= npb) | (rows == 1))
     assert np.all(rows <= npb)
-    # greedy: adding the next row would have exceeded a cap
-    nxt = off[np.minimum(plan[1:-1] + 1, ng)] - off[plan[:-2]]
-    assert np.all((nxt > npb) | (rows[:-1] == npb))
+    # every inner boundary on a multiple of 16 rows where the block reaches one
+    inner = plan[1:-1]
+    assert np.all((inner % 16 == 0) | (inner // 16 * 16 <= plan[:-2]))
+    assert list(plan) == plan_rule(off, npb)
 
 
 def test_gather_plan_caps_rows(bs):
@@ -342,7 +360,7 @@ def test_g2l_property(bs, orc, n_local, n_global, seed, mask_mod):
 def test_gather_plan_property(bs, rows, npb):
     """blockStarts of any row-length profile: covers every row once, in
     order, each block within both caps unless it is a single row, and greedy
-    (the next row would have broken a cap)."""
+    up to the 16-row rounding of every inner boundary."""
     off = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
     plan = bs.bs_gather_plan(off, npb)
     ng = len(rows)
@@ -355,7 +373,13 @@ def test_gather_plan_property(bs, rows, npb):
         ent, nr = off[b] - off[a], b - a
         assert nr == 1 or (ent <= npb and nr <= npb)
         if b < ng:
-            assert nr + 1 > npb or off[b + 1] - off[a] > npb
+            # the greedy end g (the next row would break a cap) rounded down
+            # to b = 16 k, or kept where no multiple of 16 follows row a
+            g = b
+            while g < ng and g - a < npb and off[g + 1] - off[a] <= npb:
+                g += 1
+            assert (b % 16 == 0 and b <= g < b + 16) or (b == g and g // 16 * 16 <= a)
+    assert list(plan) == plan_rule(off, npb)
 
 
 @settings(max_examples=25, deadline=None, derandomize=True)

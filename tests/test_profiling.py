@@ -123,3 +123,25 @@ def test_in_step_launches(tmp_path):
         w.writerows(rows)
     d = profiling.load_in_step(tmp_path / "trace.csv", "k_dot<4, false>", "k_cg_update<4>", "k_scatter")
     assert d == [1200, 1400]
+
+
+def test_counter_averages(tmp_path):
+    """--pmc: plain per-kernel averages per dispatch over several counter
+    files, filtered to the kernels asked for."""
+    write_counters(tmp_path / "a.csv", [
+        ("void (anonymous namespace)::k_gather_plan<false>(x)", "SQ_WAVES", 8.0),
+        ("void (anonymous namespace)::k_gather_plan<false>(x)", "SQ_WAVES", 12.0),
+        ("(anonymous namespace)::k_scatter(y)", "SQ_WAVES", 4.0),
+        ("__amd_rocclr_copyBuffer", "SQ_WAVES", 99.0)])
+    write_counters(tmp_path / "b.csv", [
+        ("void (anonymous namespace)::k_gather_plan<false>(x)", "TCC_HIT_sum", 3.0)])
+    t = profiling.load_counters([tmp_path / "a.csv", tmp_path / "b.csv"], {"k_gather_plan<false>", "k_scatter"})
+    assert set(t) == {"k_gather_plan<false>", "k_scatter"}
+    assert t["k_gather_plan<false>"]["SQ_WAVES"] == [8.0, 12.0]
+    assert t["k_gather_plan<false>"]["TCC_HIT_sum"] == [3.0]
+    md_path = tmp_path / "c.md"
+    profiling.main(["--pmc", str(tmp_path / "a.csv"), "--pmc", str(tmp_path / "b.csv"), "--kernel",
+                    "k_gather_plan<false>", "--title", "t", "--command", "rocprofv3 --pmc ...", "--md", str(md_path)])
+    md = md_path.read_text()
+    assert "| SQ_WAVES | 2 | 10 |" in md and "| TCC_HIT_sum | 1 | 3 |" in md
+    assert "k_scatter" not in md and "rocprofv3 --pmc ..." in md
