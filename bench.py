@@ -219,7 +219,7 @@ class Mesh:
         P = lambda t: t.data_ptr()  # noqa: E731
         o = P(self.out)
         plan = P(self.plan) if self.gather_lds else None
-        nb = self.plan.numel() - 1 if self.gather_lds else 0
+        nb = self.plan.shape[0] - 1 if self.gather_lds else 0
         a = dict(
             copy=(L.bs_copy, (h, n, P(self.copy_x), P(self.copy_y), stream)),
             axpy=(L.bs_axpy, (h, n, 0.37, P(self.axpy_x), 1.0, P(self.axpy_y), stream)),
@@ -251,7 +251,7 @@ class Mesh:
             "cg_update": (self.ng, (self.cg_p, self.cg_q, self.cg_x, self.cg_r), 0),
             "scatter": (self.nl, (self.l2g, self.sc_vg, self.sc_vl), 0),
             "gather": (self.ng, (self.off, self.ids, self.ga_vl, self.ga_vg, plan),
-                       self.plan.numel() - 1 if self.gather_lds else 0),
+                       self.plan.shape[0] - 1 if self.gather_lds else 0),
         }[op]
 
     def bytes(self, op):
@@ -533,7 +533,7 @@ def cg_sequence(bs, torch, dev, m, iters=100):
     q, pl = torch.empty_like(b), m.sc_vl
     o = torch.zeros(2, dtype=torch.float64, device=dev)
     plan = P(m.plan) if m.gather_lds else None
-    nb = m.plan.numel() - 1 if m.gather_lds else 0
+    nb = m.plan.shape[0] - 1 if m.gather_lds else 0
 
     def it(alpha, beta):
         assert L.bs_scatter(h, nl, P(m.l2g), P(p), P(pl), st) == 0

@@ -75,7 +75,7 @@ SIGNATURES = {
     "bs_mesh_hex_order": ([_i64, _ptr, _ptr], _int),
     "bs_validate_l2g": ([_i64, _i64, _ptr], _int),
     "bs_validate_g2l": ([_i64, _i64, _ptr, _ptr, _ptr], _int),
-    "bs_validate_plan": ([_i64, _ptr, _i64], _int),
+    "bs_validate_plan": ([_i64, _ptr, _ptr, _i64], _int),
     "bs_index_g2l": ([_i64, _i64, _ptr, _ptr, _ptr], _int),
     "bs_gather_plan": ([_i64, _ptr, _int, _ptr, ctypes.POINTER(_i64)], _int),
     "bs_bench_loop": ([_ptr, _int, _i64, _dbl, _dbl, _i64, _int, _ptr, _ptr, _int, _ptr, ctypes.POINTER(_dbl)],
@@ -208,6 +208,18 @@ def _ctx_dev(t, ctx, stream=None):
     return ctx
 
 
+def _plan_dev(block_starts):
+    """(pointer, n_blocks) of a device gather plan, or (None, 0) for none: the
+    (n_blocks + 1, 2) int32 tensor of (row, first entry) pairs that
+    bs_gather_plan builds."""
+    import torch
+    if block_starts is None:
+        return None, 0
+    if block_starts.dim() != 2 or block_starts.shape[1] != 2 or block_starts.shape[0] < 1:
+        raise ValueError("block_starts must be the (n_blocks + 1, 2) pairs of bs_gather_plan")
+    return _dev_tensor(block_starts, torch.int32, "block_starts"), block_starts.shape[0] - 1
+
+
 def _scalar_out(out, like):
     import torch
     if out is None:
@@ -301,10 +313,7 @@ def bs_gather(off, ids, v_local, v_global, block_starts=None, *, ctx=None, strea
     if off.numel() != ng + 1:
         raise ValueError("off must hold n_global + 1 entries")
     ctx = _ctx_dev(v_global, ctx, stream)
-    bp, nb = None, 0
-    if block_starts is not None:
-        bp = _dev_tensor(block_starts, torch.int32, "block_starts")
-        nb = block_starts.numel() - 1
+    bp, nb = _plan_dev(block_starts)
     _check(_lib().bs_gather(ctx.handle, ng, _dev_tensor(off, torch.int32, "off"),
                             _dev_tensor(ids, torch.int32, "ids"),
                             _dev_tensor(v_local, torch.float64, "v_local"),
@@ -349,10 +358,7 @@ def bs_gather_dot(off, ids, v_local, v_global, w, block_starts=None, out=None, *
         raise ValueError("off must hold n_global + 1 entries and w n_global")
     ctx = _ctx_dev(v_global, ctx, stream)
     out = _scalar_out(out, v_global)
-    bp, nb = None, 0
-    if block_starts is not None:
-        bp = _dev_tensor(block_starts, torch.int32, "block_starts")
-        nb = block_starts.numel() - 1
+    bp, nb = _plan_dev(block_starts)
     _check(_lib().bs_gather_dot(ctx.handle, ng, _dev_tensor(off, torch.int32, "off"),
                                 _dev_tensor(ids, torch.int32, "ids"),
                                 _dev_tensor(v_local, torch.float64, "v_local"),
@@ -380,10 +386,7 @@ def bs_cg_solve(l2g, off, ids, x, r, p, q, p_local, iters, tol=0.0, block_starts
     ctx = _ctx_dev(x, ctx, stream)
     if rr_hist is None:
         rr_hist = torch.empty(int(iters) + 1, dtype=torch.float64, device=x.device)
-    bp, nb = None, 0
-    if block_starts is not None:
-        bp = _dev_tensor(block_starts, torch.int32, "block_starts")
-        nb = block_starts.numel() - 1
+    bp, nb = _plan_dev(block_starts)
     _check(_lib().bs_cg_solve(ctx.handle, ng, nl, _dev_tensor(l2g, torch.int32, "l2g"),
                               _dev_tensor(off, torch.int32, "off"), _dev_tensor(ids, torch.int32, "ids"), bp, nb,
                               _dev_tensor(x, torch.float64, "x"), _dev_tensor(r, torch.float64, "r"),
@@ -408,10 +411,7 @@ def bs_cg_solve_static(l2g, off, ids, x, r, p, q, p_local, iters, rr_hist, tol=0
         raise ValueError("iters must be >= 0")
     if rr_hist.numel() < int(iters) + 1:
         raise ValueError(f"rr_hist holds {rr_hist.numel()} entries; {int(iters) + 1} are written")
-    bp, nb = None, 0
-    if block_starts is not None:
-        bp = _dev_tensor(block_starts, torch.int32, "block_starts")
-        nb = block_starts.numel() - 1
+    bp, nb = _plan_dev(block_starts)
     _check(_lib().bs_cg_solve_static(ng, nl, _dev_tensor(l2g, torch.int32, "l2g"),
                                      _dev_tensor(off, torch.int32, "off"), _dev_tensor(ids, torch.int32, "ids"), bp,
                                      nb, _dev_tensor(x, torch.float64, "x"), _dev_tensor(r, torch.float64, "r"),
@@ -518,12 +518,19 @@ def bs_validate_g2l(off, ids, n_local, l2g=None):
            "bs_validate_g2l")
 
 
-def bs_validate_plan(block_starts, n_global):
-    """Raise BSError unless block_starts is a well-formed gather plan."""
-    bs_ = _host_i32(block_starts, "block_starts")
-    if bs_.size < 1:
-        raise ValueError("block_starts needs n_blocks + 1 >= 1 entries")
-    _check(_lib().bs_validate_plan(int(n_global), bs_.ctypes.data, bs_.size - 1), "bs_validate_plan")
+def bs_validate_plan(block_starts, off):
+    """Raise BSError unless block_starts is a well-formed gather plan for the
+    CSR offsets off (n_global + 1 entries): (n_blocks + 1, 2) int32 pairs of
+    (row, first entry)."""
+    bs_ = np.asarray(block_starts)
+    if bs_.ndim != 2 or bs_.shape[1] != 2 or bs_.shape[0] < 1:
+        raise ValueError("block_starts must be (n_blocks + 1, 2) pairs")
+    bs_ = _host_i32(bs_, "block_starts")
+    off = _host_i32(off, "off")
+    if off.size < 1:
+        raise ValueError("off needs n_global + 1 >= 1 entries")
+    _check(_lib().bs_validate_plan(off.size - 1, off.ctypes.data, bs_.ctypes.data, bs_.shape[0] - 1),
+           "bs_validate_plan")
 
 
 def bs_index_g2l(l2g, n_global):
@@ -537,10 +544,11 @@ def bs_index_g2l(l2g, n_global):
 
 
 def bs_gather_plan(off, nodes_per_block=1024):
-    """blockStarts for the LDS-staged gather (int32 numpy array)."""
+    """blockStarts for the LDS-staged gather: an int32 numpy array of shape
+    (n_blocks + 1, 2), each block's first row and its first CSR entry."""
     off = _host_i32(off, "off")
     ng = off.size - 1
-    bs = np.empty(ng + 1, dtype=np.int32)
+    bs = np.empty((ng + 1, 2), dtype=np.int32)
     nb = _i64()
     _check(_lib().bs_gather_plan(ng, off.ctypes.data, int(nodes_per_block), bs.ctypes.data, ctypes.byref(nb)),
            "bs_gather_plan")
@@ -559,7 +567,7 @@ def bs_bench_loop(op, n, sets, reps, result=None, alpha=0.37, beta=1.0, *, n_blo
     cycling through `sets` (a list of tuples of device tensors in the order
     the header lists for the op). Vector operations take n = their length,
     scatter n = n_local, gather n = n_global; a gather set's fifth tensor is
-    the blockStarts plan (n_blocks + 1 entries) or None."""
+    the blockStarts plan ((n_blocks + 1, 2) pairs) or None."""
     import torch
     if op not in BS_OP:
         raise ValueError(f"unknown op {op!r}")
@@ -579,8 +587,9 @@ def bs_bench_loop(op, n, sets, reps, result=None, alpha=0.37, beta=1.0, *, n_blo
         elif op == "gather":
             if group[0].numel() < n + 1 or group[3].numel() < n:
                 raise ValueError("gather: off needs n_global + 1 entries and v_global n_global")
-            if group[4] is not None and group[4].numel() < n_blocks + 1:
-                raise ValueError("gather: block_starts needs n_blocks + 1 entries")
+            if group[4] is not None and (group[4].dim() != 2 or group[4].shape[1] != 2 or
+                                         group[4].shape[0] < n_blocks + 1):
+                raise ValueError("gather: block_starts must be (>= n_blocks + 1, 2) pairs")
         for j, (t, kind) in enumerate(zip(group, slots)):
             if t is None:
                 if not (op == "gather" and j == 4):

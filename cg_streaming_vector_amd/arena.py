@@ -43,7 +43,7 @@ class Arena:
         return t
 
     def put(self, src):
-        """A copy of tensor src (any device) in the arena."""
+        """A copy of tensor src (any device) in the arena, of the same shape."""
         t = self.empty(src.numel(), src.dtype)
         t.copy_(src.reshape(-1))
-        return t
+        return t.view(src.shape)

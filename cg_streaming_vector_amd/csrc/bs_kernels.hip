@@ -981,16 +981,18 @@ __device__ __forceinline__ unsigned gather_block()
     return ((k / kXcdRun) * kXcds + x) * kXcdRun + k % kXcdRun;
 }
 
-// LDS-staged kernel after the blockStarts scheme of the paper: block b owns
-// rows bs[b] .. bs[b+1]), which bs_gather_plan caps at kGatherCap rows and
-// kGatherCap entries (a single longer row gets a block of its own). The
-// block's first and end entry come from two uniform (scalar) loads, so each
-// lane can then issue at once its CSR ids (consecutive lanes on consecutive
-// entries) and the two offsets of each row it will sum. The v_L values the
-// ids name are fetched, staged in LDS, and after the one barrier each lane
-// sums its rows from LDS in ascending entry order. (Offsets staged in LDS
-// instead, behind a barrier of their own, measured 0.7-2.8% slower.) Blocks
-// over capacity read global memory.
+// LDS-staged kernel after the blockStarts scheme of the paper: the plan
+// holds (row, first CSR entry) pairs, and block b owns rows bs[2b] ..
+// bs[2b+2]), which bs_gather_plan caps at kGatherCap rows and kGatherCap
+// entries (a single longer row gets a block of its own). The block reads its
+// rows and its first and end entry from the plan with uniform (scalar)
+// loads, so each lane can then issue at once its CSR ids (consecutive lanes
+// on consecutive entries) and the two offsets of each row it will sum. The
+// v_L values the ids name are fetched, staged in LDS, and after the one
+// barrier each lane sums its rows from LDS in ascending entry order. (Offsets
+// staged in LDS instead, behind a barrier of their own, measured 0.7-2.8%
+// slower; the first entry loaded from the offsets rather than the plan,
+// 1-4% slower.) Blocks over capacity read global memory.
 template <bool kDot, int P>
 __device__ __forceinline__ void gather_plan_body(const int32_t *__restrict__ bstart,
                                                  const int32_t *__restrict__ off,
@@ -1003,12 +1005,12 @@ __device__ __forceinline__ void gather_plan_body(const int32_t *__restrict__ bst
     constexpr int K = kGatherCap / kBlock;  // entries per lane, and rows per lane at most
     __shared__ double stage[kGatherCap];
     const unsigned lb = gather_block();
-    const int32_t r0 = bstart[lb], r1 = bstart[lb + 1];
+    const int32_t r0 = bstart[2 * lb], r1 = bstart[2 * lb + 2];
     const int32_t nr = r1 - r0;
     double acc = 0.0;
     bool staged = false;
     if (nr <= kGatherCap) {
-        const int32_t e0 = off[r0], ne = off[r1] - e0;
+        const int32_t e0 = bstart[2 * lb + 1], ne = bstart[2 * lb + 3] - e0;
         if (ne <= kGatherCap) {
             staged = true;
             int32_t id[K], oa[K], ob[K];
@@ -1672,7 +1674,7 @@ int cg_solve_run(bs_ctx *c, int64_t n_global, int64_t n_local, const int32_t *l2
     // operations (measured: 7-12% faster per iteration up to ~190 MB, equal
     // near 320 MB, 11% slower at 680 MB with the keeping policy).
     const int64_t working_set = 8 * (4 * n_global + n_local) + 4 * (2 * n_local + n_global + 1) +
-                                (block_starts ? 4 * (n_blocks + 1) : 0);
+                                (block_starts ? 8 * (n_blocks + 1) : 0);
     const bool keep = working_set <= kCacheResidentBytes;
     // Otherwise, while r and p alone fit, the update hands them to the
     // direction update through the cache (1-3% per iteration at 24^3-32^3,

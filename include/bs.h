@@ -151,8 +151,9 @@ int bs_scatter(bs_ctx *ctx, int64_t n_local, const int32_t *l2g, const double *v
  * ascending inside each row the result is bit-identical to Z^T v_L summed in
  * ascending local index. off int32[n_global+1], ids int32[off[n_global]],
  * v_local double[> max id], v_global double[n_global]. block_starts NULL
- * selects the row-per-lane kernel; otherwise int32[n_blocks+1] from
- * bs_gather_plan selects the LDS-staged kernel (same bits). Neither the CSR
+ * selects the row-per-lane kernel; otherwise the n_blocks+1 (row, entry)
+ * pairs, int32[2*(n_blocks+1)], of bs_gather_plan select the LDS-staged
+ * kernel (same bits). Neither the CSR
  * nor the plan is range-checked on the device: pass tables built by
  * bs_index_g2l and bs_gather_plan, or check others once with
  * bs_validate_g2l and bs_validate_plan. n_global >=
@@ -333,13 +334,15 @@ int bs_validate_l2g(int64_t n_local, int64_t n_global, const int32_t *l2g);
  * BS_OK or BS_EINVAL; BS_ERANGE for sizes beyond int32 indices. */
 int bs_validate_g2l(int64_t n_global, int64_t n_local, const int32_t *off, const int32_t *ids, const int32_t *l2g);
 
-/* Check a blockStarts plan before a gather trusts it: block_starts[0] == 0,
- * strictly increasing, block_starts[n_blocks] == n_global, 1 <= n_blocks <=
- * n_global (n_global == 0: n_blocks == 0 and block_starts[0] == 0). Blocks
- * above the LDS stage's capacity are allowed (the kernel reads them from
- * global memory). block_starts int32[n_blocks+1]. BS_OK or BS_EINVAL;
- * BS_ERANGE for n_global >= INT32_MAX. */
-int bs_validate_plan(int64_t n_global, const int32_t *block_starts, int64_t n_blocks);
+/* Check a blockStarts plan before a gather trusts it, against the CSR
+ * offsets off int32[n_global+1] it was built for: block_starts holds
+ * n_blocks+1 pairs (row, entry), int32[2*(n_blocks+1)]; the rows start at 0,
+ * increase strictly and end at n_global, 1 <= n_blocks <= n_global
+ * (n_global == 0: n_blocks == 0 and the one pair (0, off[0])); each entry is
+ * off[row] of its row. Blocks above the LDS stage's capacity are allowed (the
+ * kernel reads them from global memory). BS_OK or BS_EINVAL; BS_ERANGE for
+ * n_global >= INT32_MAX. */
+int bs_validate_plan(int64_t n_global, const int32_t *off, const int32_t *block_starts, int64_t n_blocks);
 
 /* CSR form of I_g->l: a stable counting-sort transpose of l2g. off receives
  * int32[n_global+1]; ids receives the off[n_global] local indices (at most
@@ -357,9 +360,10 @@ int bs_index_g2l(int64_t n_local, int64_t n_global, const int32_t *l2g, int32_t 
  * entries (a single longer row gets a block of its own). Every block but the
  * last then ends on a multiple of 16 rows, rounding its greedy end down,
  * unless no multiple of 16 lies after its first row: so each block writes
- * whole 128-byte lines of a 128-byte-aligned v_global. block_starts
- * receives n_blocks+1 row indices (capacity n_global+1 suffices),
- * block_starts[0] = 0 and block_starts[n_blocks] = n_global.
+ * whole 128-byte lines of a 128-byte-aligned v_global. The plan stores each
+ * block start with its first CSR entry: block_starts receives n_blocks+1
+ * pairs (row, off[row]), that is int32[2*(n_blocks+1)] (capacity
+ * 2*(n_global+1) suffices), from (0, off[0]) to (n_global, off[n_global]).
  * nodes_per_block must be in [1, 1024] (BS_EINVAL): the gather kernel stages
  * up to 1024 entries per block in LDS. */
 int bs_gather_plan(int64_t n_global, const int32_t *off, int nodes_per_block,

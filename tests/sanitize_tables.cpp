@@ -87,11 +87,11 @@ void check_tables(const std::vector<int32_t> &l2g, int64_t ng)
     CHECK(std::equal(ids.begin(), ids.begin() + m, oids.begin()));
     CHECK(bs_validate_g2l(ng, nl, off.data(), ids.data(), l2g.data()) == BS_OK);
     for (int npb : {1, 3, 64, 1000, 1024}) {
-        std::vector<int32_t> plan((size_t)ng + 1);
+        std::vector<int32_t> plan(2 * ((size_t)ng + 1));
         int64_t nb = -1;
         CHECK(bs_gather_plan(ng, off.data(), npb, plan.data(), &nb) == BS_OK);
         CHECK(nb >= 1 && nb <= ng);
-        CHECK(bs_validate_plan(ng, plan.data(), nb) == BS_OK);
+        CHECK(bs_validate_plan(ng, off.data(), plan.data(), nb) == BS_OK);
     }
     // the oracle's scatter and gather on these tables: gather(1) is the multiplicity
     std::vector<double> ones((size_t)nl, 1.0), mult((size_t)ng), vg = values(ng, 7), vl((size_t)nl);
@@ -176,7 +176,7 @@ void errors()
     std::vector<int32_t> l2g(8);
     std::vector<int32_t> notperm = {0, 1, 2, 3, 4, 5, 6, 6};
     CHECK(bs_mesh_box_l2g(2, 2, 2, 1, notperm.data(), nullptr, std::vector<int32_t>(64).data()) == BS_EINVAL);
-    std::vector<int32_t> ids = {0, 1, 5}, off(6), col(4), plan(7);
+    std::vector<int32_t> ids = {0, 1, 5}, off(6), col(4), plan(14);
     CHECK(bs_index_g2l(3, 5, ids.data(), off.data(), col.data()) == BS_EINVAL);
     CHECK(bs_validate_l2g(3, 5, ids.data()) == BS_EINVAL);
     std::vector<int32_t> good = {0, 1, 2, 3, 4}, col5(5);
@@ -184,7 +184,8 @@ void errors()
     int64_t nb = 0;
     CHECK(bs_gather_plan(5, off.data(), 0, plan.data(), &nb) == BS_EINVAL);
     CHECK(bs_gather_plan(5, off.data(), 1025, plan.data(), &nb) == BS_EINVAL);
-    CHECK(bs_validate_plan(5, nullptr, 1) == BS_EINVAL);
+    CHECK(bs_validate_plan(5, off.data(), nullptr, 1) == BS_EINVAL);
+    CHECK(bs_validate_plan(5, nullptr, plan.data(), 1) == BS_EINVAL);
     CHECK(bs_validate_g2l(-1, 0, off.data(), nullptr, nullptr) == BS_EINVAL);
     std::vector<int32_t> ev = {0, 1, 2, 3, 4, 5, 6, 7};
     int64_t ng = 0;

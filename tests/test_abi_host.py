@@ -205,7 +205,10 @@ def test_gather_plan(bs, npb):
     l2g = bs.bs_mesh_box_l2g(6, 5, 4, 3)
     ng = bs.bs_mesh_box_count(6, 5, 4, 3)[1]
     off, _ = bs.bs_index_g2l(l2g, ng)
-    plan = bs.bs_gather_plan(off, npb)
+    pairs = bs.bs_gather_plan(off, npb)
+    plan = pairs[:, 0]
+    # each block start carries its first CSR entry
+    assert pairs.shape == (plan.size, 2) and np.array_equal(pairs[:, 1], off[plan])
     assert plan[0] == 0 and plan[-1] == ng
     assert np.all(np.diff(plan) >= 1)
     ent = off[plan[1:]] - off[plan[:-1]]
@@ -223,7 +226,7 @@ def test_gather_plan_caps_rows(bs):
     # empty rows (fully masked nodes) still count against the row cap
     off = np.zeros(3001, dtype=np.int32)
     plan = bs.bs_gather_plan(off, 1024)
-    assert list(plan) == [0, 1024, 2048, 3000]
+    assert plan.tolist() == [[0, 0], [1024, 0], [2048, 0], [3000, 0]]
 
 
 @pytest.mark.parametrize("p", [1, 2, 3, 4, 5, 7, 10, 15])
@@ -249,7 +252,7 @@ def test_gather_plan_long_rows(bs):
     # one node with 10 entries, the rest single
     off = np.array([0, 1, 11, 12, 13], dtype=np.int32)
     plan = bs.bs_gather_plan(off, 4)
-    assert list(plan) == [0, 1, 2, 4]
+    assert plan.tolist() == [[0, 0], [1, 1], [2, 11], [4, 13]]
     with pytest.raises(bs.BSError):
         bs.bs_gather_plan(off, 0)
     with pytest.raises(bs.BSError):
@@ -362,11 +365,13 @@ def test_gather_plan_property(bs, rows, npb):
     order, each block within both caps unless it is a single row, and greedy
     up to the 16-row rounding of every inner boundary."""
     off = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
-    plan = bs.bs_gather_plan(off, npb)
+    pairs = bs.bs_gather_plan(off, npb)
+    plan = pairs[:, 0]
+    assert np.array_equal(pairs[:, 1], off[plan])
     ng = len(rows)
     assert plan[0] == 0 and plan[-1] == ng
     if ng == 0:
-        assert list(plan) == [0]
+        assert pairs.tolist() == [[0, 0]]
         return
     assert np.all(np.diff(plan) >= 1)
     for a, b in zip(plan[:-1], plan[1:]):
@@ -498,22 +503,30 @@ def test_validate_g2l_rejects(bs, fault):
 def test_validate_plan(bs):
     l2g, ng, off, ids = _tables(bs)
     for npb in (1, 5, 300, 1024):
-        bs.bs_validate_plan(bs.bs_gather_plan(off, npb), ng)
+        bs.bs_validate_plan(bs.bs_gather_plan(off, npb), off)
     plan = bs.bs_gather_plan(off, 64)
-    bad = [plan.copy() for _ in range(4)]
-    bad[0][0] = 1
-    bad[1][-1] = ng - 1
-    bad[2][3] = bad[2][2]
-    bad[3][2], bad[3][3] = bad[3][3], bad[3][2]
+    bad = [plan.copy() for _ in range(7)]
+    bad[0][0, 0] = 1                              # first row not 0
+    bad[1][-1, 0] = ng - 1                        # last row not n_global
+    bad[2][3, 0] = bad[2][2, 0]                   # rows not increasing
+    bad[3][2, 0], bad[3][3, 0] = bad[3][3, 0], bad[3][2, 0]
+    bad[4][2, 1] += 1                             # an entry that is not off[row]
+    bad[5][0, 1] = -1
+    bad[6][-1, 1] -= 1
     for p in bad:
         with pytest.raises(bs.BSError):
-            bs.bs_validate_plan(p, ng)
-    with pytest.raises(bs.BSError):
-        bs.bs_validate_plan(plan, ng + 1)
-    bs.bs_validate_plan(np.zeros(1, dtype=np.int32), 0)
+            bs.bs_validate_plan(p, off)
+    with pytest.raises(bs.BSError):  # a plan for other offsets
+        off2 = off.copy()
+        off2[5:] += 1
+        bs.bs_validate_plan(plan, off2)
+    with pytest.raises(ValueError):  # row starts alone are not a plan
+        bs.bs_validate_plan(plan[:, 0].copy(), off)
+    bs.bs_validate_plan(np.zeros((1, 2), dtype=np.int32), np.zeros(1, dtype=np.int32))
     L = bs._lib()
-    assert L.bs_validate_plan(2 ** 31 - 1, plan.ctypes.data, 1) == bs.BS_ERANGE
-    assert L.bs_validate_plan(ng, None, 1) == bs.BS_EINVAL
+    assert L.bs_validate_plan(2 ** 31 - 1, off.ctypes.data, plan.ctypes.data, 1) == bs.BS_ERANGE
+    assert L.bs_validate_plan(ng, off.ctypes.data, None, 1) == bs.BS_EINVAL
+    assert L.bs_validate_plan(ng, None, plan.ctypes.data, 1) == bs.BS_EINVAL
 
 
 # --------------------------------------------- element order along a curve --

@@ -381,13 +381,15 @@ def test_gather_plan_over_capacity_blocks(env):
     ol2g, _ = orc.mesh_box(6, 6, 6, 3)
     vlv = bs_inputs.uniform_pm1(85, l2g.size)
     want = orc.gather(ol2g, vlv, ng)
-    plans = [np.array([0, ng], dtype=np.int32),
-             np.array([0, 700, 2100, 2101, ng], dtype=np.int32),
-             np.arange(0, ng + 1, dtype=np.int32)]
-    for plan in plans:
+    starts = [np.array([0, ng], dtype=np.int32),
+              np.array([0, 700, 2100, 2101, ng], dtype=np.int32),
+              np.arange(0, ng + 1, dtype=np.int32)]
+    for rows in starts:
+        plan = np.stack([rows, off[rows]], axis=1).astype(np.int32)  # (row, first entry) pairs
+        bs.bs_validate_plan(plan, off)
         vg = torch.full((ng,), np.nan, dtype=torch.float64, device=d)
         bs.bs_gather(dev(torch, d, off), dev(torch, d, ids), dev(torch, d, vlv), vg, dev(torch, d, plan))
-        assert_bits(host(vg), want, f"plan with {plan.size - 1} blocks")
+        assert_bits(host(vg), want, f"plan with {rows.size - 1} blocks")
 
 
 def test_scatter_ragged_and_misaligned(env):
@@ -875,7 +877,7 @@ def test_bench_loop_scatter_gather(env):
     for p in (None, dev(torch, d, plan)):
         vg = torch.full((ng,), np.nan, dtype=torch.float64, device=d)
         bs.bs_bench_loop("gather", ng, [(dev(torch, d, off), dev(torch, d, ids), dev(torch, d, vlv), vg, p)], 2,
-                         n_blocks=0 if p is None else plan.size - 1)
+                         n_blocks=0 if p is None else plan.shape[0] - 1)
         assert_bits(host(vg), want, "gather via loop")
 
 
