@@ -265,7 +265,7 @@ struct Fin {
 
 // Called by every thread of every block with the block's partial (valid in
 // thread 0); true in the block that is to finish.
-__device__ __forceinline__ bool last_arrival(double part, const Fin &f)
+__device__ __forceinline__ bool last_arrival(double part, const Fin &f, unsigned nb)
 {
     __shared__ bool last;
     if (threadIdx.x == 0) {
@@ -279,12 +279,11 @@ __device__ __forceinline__ bool last_arrival(double part, const Fin &f)
         __builtin_amdgcn_s_waitcnt(0);
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         bool l;
-        if (gridDim.x <= kOneTicket) {
-            l = __hip_atomic_fetch_add(&f.tickets[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                gridDim.x - 1;
+        if (nb <= kOneTicket) {
+            l = __hip_atomic_fetch_add(&f.tickets[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nb - 1;
         } else {
             const unsigned g = blockIdx.x & 7u;
-            const unsigned members = gridDim.x / 8u + (g < (gridDim.x & 7u) ? 1u : 0u);
+            const unsigned members = nb / 8u + (g < (nb & 7u) ? 1u : 0u);
             unsigned *gc = &f.tickets[(1 + g) * kTicketStride];
             l = false;
             if (__hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == members - 1) {
@@ -308,10 +307,9 @@ __device__ __forceinline__ bool last_arrival(double part, const Fin &f)
 // bits: the running sum starts at +0.0 and never becomes -0.0).
 constexpr int kFinishLoads = 4;
 template <int NT = kBlock>
-__device__ __forceinline__ void finish_last(const Fin &f)
+__device__ __forceinline__ void finish_last(const Fin &f, unsigned nb)
 {
     __shared__ double wsum[NT / kWave];
-    const unsigned nb = gridDim.x;
     double s = 0.0;
     for (unsigned i0 = threadIdx.x; i0 < nb; i0 += kFinishLoads * NT) {
         double v[kFinishLoads];
@@ -340,9 +338,9 @@ __device__ __forceinline__ void finish_last(const Fin &f)
 }
 
 template <int NT = kBlock>
-__device__ __forceinline__ void finish_block(double part, const Fin &f)
+__device__ __forceinline__ void finish_block(double part, const Fin &f, unsigned nb)
 {
-    if (last_arrival(part, f)) finish_last<NT>(f);
+    if (last_arrival(part, f, nb)) finish_last<NT>(f, nb);
 }
 
 // Two-kernel reductions (the gather's folded dot, whose grid has one block
@@ -412,6 +410,15 @@ struct Split {
     int64_t tail;  // index of the trailing scalar element, or -1
 };
 
+// The body and flags of a Split as plain kernel arguments: bit 0 a head
+// element, bit 1 a tail element (which follows the body).
+__host__ __device__ inline unsigned ht_of(const Split &s) { return (s.head ? 1u : 0u) | (s.tail >= 0 ? 2u : 0u); }
+__device__ inline Split split_ht(int64_t n2, unsigned ht)
+{
+    const int64_t head = ht & 1u;
+    return Split{head, n2, (ht & 2u) ? head + 2 * n2 : -1};
+}
+
 __host__ __device__ inline Split split_of(int64_t n, int64_t head)
 {
     Split s;
@@ -427,7 +434,11 @@ __host__ __device__ inline Split split_of(int64_t n, int64_t head)
 // the ones needed first leading: the library is built to preload the leading
 // kernel arguments into SGPRs at wave launch (kernarg preload), which spares
 // every wave the scalar load of its arguments before its first memory access
-// (0.4 us of a 29 us copy). Aggregates cannot be preloaded.
+// (0.4 us of a 29 us copy). Aggregates cannot be preloaded, nor can the hidden
+// grid size behind them: the kernels that end in a reduction finish (an
+// aggregate) or have more leading arguments than the preload holds take the
+// head/tail flags packed in one word and the grid size as an argument (the
+// fused update 0.6 us faster, AXPY and dot 0.15 us).
 template <int U, int NT>
 __global__ __launch_bounds__(NT) void k_copy(int64_t n2, const double *__restrict__ x, double *__restrict__ y,
                                              int64_t head, int64_t tail)
@@ -466,13 +477,13 @@ __device__ __forceinline__ d2 axpy2(double a, d2 x, double b, d2 y)
 // p = r + beta p step of the device-resident CG iteration).
 template <int U, int P>
 __device__ __forceinline__ void axpy_body(Split sp, Coef ca, const double *x, Coef cb, double *y,
-                                          const double *cgs)
+                                          const double *cgs, unsigned nblk)
 {
     if (skipped(cgs)) return;
     const double a = ca.get(), b = cb.get();
     const d2 *xv = reinterpret_cast<const d2 *>(x + sp.head);
     d2 *yv = reinterpret_cast<d2 *>(y + sp.head);
-    const int64_t stride = (int64_t)gridDim.x * kBlock * U;
+    const int64_t stride = (int64_t)nblk * kBlock * U;
     int64_t i = (int64_t)blockIdx.x * kBlock * U + threadIdx.x;
     for (; i + (U - 1) * kBlock < sp.n2; i += stride) {
         d2 vx[U], vy[U];
@@ -497,9 +508,9 @@ __device__ __forceinline__ void axpy_body(Split sp, Coef ca, const double *x, Co
 
 template <int U>
 __global__ __launch_bounds__(kBlock) void k_axpy(int64_t n2, const double *x, double *y, double a, double b,
-                                                 int64_t head, int64_t tail)
+                                                 unsigned ht, unsigned nblk)
 {
-    axpy_body<U, kStream>(Split{head, n2, tail}, Coef{a, nullptr}, x, Coef{b, nullptr}, y, nullptr);
+    axpy_body<U, kStream>(split_ht(n2, ht), Coef{a, nullptr}, x, Coef{b, nullptr}, y, nullptr, nblk);
 }
 
 // The same with its coefficients read from device memory, for the direction
@@ -508,7 +519,7 @@ template <int U>
 __global__ __launch_bounds__(kBlock) void k_axpy_dev(Split sp, Coef ca, const double *x, Coef cb, double *y,
                                                      const double *cgs)
 {
-    axpy_body<U, kStream>(sp, ca, x, cb, y, cgs);
+    axpy_body<U, kStream>(sp, ca, x, cb, y, cgs, gridDim.x);
 }
 
 // The same with the cache-keeping policy, for the CG iteration.
@@ -516,7 +527,7 @@ template <int U>
 __global__ __launch_bounds__(kBlock) void k_axpy_keep(Split sp, Coef ca, const double *x, Coef cb, double *y,
                                                       const double *cgs)
 {
-    axpy_body<U, kKeep>(sp, ca, x, cb, y, cgs);
+    axpy_body<U, kKeep>(sp, ca, x, cb, y, cgs, gridDim.x);
 }
 
 // ------------------------------------------- pointwise scale y = x / d ----
@@ -570,12 +581,12 @@ __global__ __launch_bounds__(kBlock) void k_scale_scalar(int64_t n, const double
 // measured 0.4 us faster at 11.4M doubles; the norm measured no gain from it.
 template <int U, bool kSquare, int NT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_dot(
-    int64_t n2, const double *__restrict__ x, const double *__restrict__ y, int64_t head, int64_t tail, Fin f)
+    int64_t n2, const double *__restrict__ x, const double *__restrict__ y, unsigned ht, unsigned nblk, Fin f)
 {
-    const Split sp{head, n2, tail};
+    const Split sp = split_ht(n2, ht);
     const d2 *xv = reinterpret_cast<const d2 *>(x + sp.head);
     const d2 *yv = reinterpret_cast<const d2 *>((kSquare ? x : y) + sp.head);
-    const int64_t stride = (int64_t)gridDim.x * NT * U;
+    const int64_t stride = (int64_t)nblk * NT * U;
     int64_t i = (int64_t)blockIdx.x * NT * U + threadIdx.x;
     double acc0 = 0.0, acc1 = 0.0;
     for (; i + (U - 1) * NT < sp.n2; i += stride) {
@@ -606,7 +617,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2))) void
         if (sp.head) acc0 = __builtin_fma(x[0], yy[0], acc0);
         if (sp.tail >= 0) acc1 = __builtin_fma(x[sp.tail], yy[sp.tail], acc1);
     }
-    finish_block<NT>(block_sum<NT>(acc0 + acc1), f);
+    finish_block<NT>(block_sum<NT>(acc0 + acc1), f, nblk);
 }
 
 // -------------------------------------------------- BS5 fused CG update ----
@@ -631,7 +642,8 @@ __device__ __forceinline__ d2 minus_aq(d2 r, double a, d2 q)
 // share of r.r to the reduction.
 template <int NT = kBlock>
 __device__ __forceinline__ void cg_update_finish(Split sp, double a, const double *p, const double *q, double *x,
-                                                 double *r, double acc0, double acc1, const Fin &f)
+                                                 double *r, double acc0, double acc1, const Fin &f,
+                                                 unsigned nblk)
 {
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         if (sp.head) {
@@ -648,7 +660,7 @@ __device__ __forceinline__ void cg_update_finish(Split sp, double a, const doubl
             acc1 = __builtin_fma(nr, nr, acc1);
         }
     }
-    finish_block<NT>(block_sum<NT>(acc0 + acc1), f);
+    finish_block<NT>(block_sum<NT>(acc0 + acc1), f, nblk);
 }
 
 // Two forms of the update, the same bits either way. p, q, x and r are
@@ -669,7 +681,8 @@ __device__ __forceinline__ void cg_update_finish(Split sp, double a, const doubl
 template <int U1, int U2, int NT, int P>
 __device__ __forceinline__ void cg_update_two_pass(Split sp, Coef ca, const double *__restrict__ p,
                                                    const double *__restrict__ q, double *__restrict__ x,
-                                                   double *__restrict__ r, const Fin &f, const double *cgs)
+                                                   double *__restrict__ r, const Fin &f, const double *cgs,
+                                                   unsigned nblk)
 {
     if (skipped(cgs)) return;
     const double a = ca.get();
@@ -678,7 +691,7 @@ __device__ __forceinline__ void cg_update_two_pass(Split sp, Coef ca, const doub
     d2 *xv = reinterpret_cast<d2 *>(x + sp.head);
     d2 *rv = reinterpret_cast<d2 *>(r + sp.head);
     {
-        const int64_t stride = (int64_t)gridDim.x * NT * U1;
+        const int64_t stride = (int64_t)nblk * NT * U1;
         int64_t i = (int64_t)blockIdx.x * NT * U1 + threadIdx.x;
         for (; i + (U1 - 1) * NT < sp.n2; i += stride) {
             d2 vp[U1], vx[U1];
@@ -698,7 +711,7 @@ __device__ __forceinline__ void cg_update_two_pass(Split sp, Coef ca, const doub
     }
     double acc0 = 0.0, acc1 = 0.0;
     {
-        const int64_t stride = (int64_t)gridDim.x * NT * U2;
+        const int64_t stride = (int64_t)nblk * NT * U2;
         int64_t i = (int64_t)blockIdx.x * NT * U2 + threadIdx.x;
         for (; i + (U2 - 1) * NT < sp.n2; i += stride) {
             d2 vq[U2], vr[U2];
@@ -726,7 +739,7 @@ __device__ __forceinline__ void cg_update_two_pass(Split sp, Coef ca, const doub
             }
         }
     }
-    cg_update_finish<NT>(sp, a, p, q, x, r, acc0, acc1, f);
+    cg_update_finish<NT>(sp, a, p, q, x, r, acc0, acc1, f, nblk);
 }
 
 // One pass over all four arrays, U pairs of each per lane and loop; PP is the
@@ -778,16 +791,16 @@ __device__ __forceinline__ void cg_update_one_pass(Split sp, Coef ca, const doub
             acc1 = __builtin_fma(nr.y, nr.y, acc1);
         }
     }
-    cg_update_finish(sp, a, p, q, x, r, acc0, acc1, f);
+    cg_update_finish(sp, a, p, q, x, r, acc0, acc1, f, gridDim.x);
 }
 
 template <int U1, int U2, int NT>
 __global__ __launch_bounds__(NT) void k_cg_update(int64_t n2, const double *__restrict__ p,
                                                   const double *__restrict__ q, double *__restrict__ x,
-                                                  double *__restrict__ r, double alpha, int64_t head, int64_t tail,
+                                                  double *__restrict__ r, double alpha, unsigned ht, unsigned nblk,
                                                   Fin f)
 {
-    cg_update_two_pass<U1, U2, NT, kStream>(Split{head, n2, tail}, Coef{alpha, nullptr}, p, q, x, r, f, nullptr);
+    cg_update_two_pass<U1, U2, NT, kStream>(split_ht(n2, ht), Coef{alpha, nullptr}, p, q, x, r, f, nullptr, nblk);
 }
 
 // The same with the cache-keeping policy, for the CG iteration.
@@ -796,7 +809,7 @@ __global__ __launch_bounds__(NT) void k_cg_update_keep(Split sp, Coef ca, const 
                                                        const double *__restrict__ q, double *__restrict__ x,
                                                        double *__restrict__ r, Fin f, const double *cgs)
 {
-    cg_update_two_pass<U1, U2, NT, kKeep>(sp, ca, p, q, x, r, f, cgs);
+    cg_update_two_pass<U1, U2, NT, kKeep>(sp, ca, p, q, x, r, f, cgs, gridDim.x);
 }
 
 // One pass, non-temporal: the CG iteration's update when its vectors do not
@@ -970,12 +983,14 @@ __global__ __launch_bounds__(kBlock) void k_gather_rows(int64_t ng, const int32_
 // XCDs, shorter ones keep the window narrow: runs of 8 measured best (against
 // 4: equal on the 32^3 order-7 box, 1% faster on the tet-split mesh, 0.4% at
 // 24^3 order 15; runs of 16 and one contiguous range per XCD were slower on
-// the boxes).
+// the boxes). nblocks is the grid size, passed as a kernel argument: it
+// arrives preloaded in an SGPR, where the hidden grid-size argument would
+// cost a scalar load before the block knows its plan block.
 constexpr unsigned kXcds = 8, kXcdRun = 8;
-__device__ __forceinline__ unsigned gather_block()
+__device__ __forceinline__ unsigned gather_block(unsigned nblocks)
 {
     constexpr unsigned span = kXcds * kXcdRun;
-    const unsigned b = blockIdx.x, full = gridDim.x / span * span;
+    const unsigned b = blockIdx.x, full = nblocks / span * span;
     if (b >= full) return b;
     const unsigned x = b % kXcds, k = b / kXcds;
     return ((k / kXcdRun) * kXcds + x) * kXcdRun + k % kXcdRun;
@@ -992,57 +1007,61 @@ __device__ __forceinline__ unsigned gather_block()
 // barrier each lane sums its rows from LDS in ascending entry order. (Offsets
 // staged in LDS instead, behind a barrier of their own, measured 0.7-2.8%
 // slower; the first entry loaded from the offsets rather than the plan,
-// 1-4% slower.) Blocks over capacity read global memory.
+// 1-4% slower.) Blocks over capacity read global memory. The kernels take
+// every argument the block needs before its first vector load among the
+// preloaded ones (block count, plan, tables, cgs); with those fetched by
+// scalar loads, and the plan in two rounds, it was 0.6-1.4% slower.
 template <bool kDot, int P>
-__device__ __forceinline__ void gather_plan_body(const int32_t *__restrict__ bstart,
+__device__ __forceinline__ void gather_plan_body(unsigned nblocks, const int32_t *__restrict__ bstart,
                                                  const int32_t *__restrict__ off,
                                                  const int32_t *__restrict__ ids,
                                                  const double *__restrict__ vl,
-                                                 double *__restrict__ vg, const double *__restrict__ w,
-                                                 double *__restrict__ partials, const double *cgs)
+                                                 double *__restrict__ vg, const double *cgs,
+                                                 const double *__restrict__ w,
+                                                 double *__restrict__ partials)
 {
     if (skipped(cgs)) return;
     constexpr int K = kGatherCap / kBlock;  // entries per lane, and rows per lane at most
     __shared__ double stage[kGatherCap];
-    const unsigned lb = gather_block();
-    const int32_t r0 = bstart[2 * lb], r1 = bstart[2 * lb + 2];
-    const int32_t nr = r1 - r0;
+    const unsigned lb = gather_block(nblocks);
+    // both of the block's pairs in one round of scalar loads, before any
+    // test uses them
+    const int32_t r0 = bstart[2 * lb], e0 = bstart[2 * lb + 1];
+    const int32_t r1 = bstart[2 * lb + 2], e1 = bstart[2 * lb + 3];
+    const int32_t nr = r1 - r0, ne = e1 - e0;
     double acc = 0.0;
     bool staged = false;
-    if (nr <= kGatherCap) {
-        const int32_t e0 = bstart[2 * lb + 1], ne = bstart[2 * lb + 3] - e0;
-        if (ne <= kGatherCap) {
-            staged = true;
-            int32_t id[K], oa[K], ob[K];
+    if (nr <= kGatherCap && ne <= kGatherCap) {
+        staged = true;
+        int32_t id[K], oa[K], ob[K];
 #pragma unroll
-            for (int k = 0; k < K; ++k) {
-                const int32_t t = threadIdx.x + k * kBlock;
-                id[k] = t < ne ? ldp<P>(ids + e0 + t) : -1;
-            }
+        for (int k = 0; k < K; ++k) {
+            const int32_t t = threadIdx.x + k * kBlock;
+            id[k] = t < ne ? ldp<P>(ids + e0 + t) : -1;
+        }
 #pragma unroll
-            for (int k = 0; k < K; ++k) {
-                const int32_t r = threadIdx.x + k * kBlock;
-                oa[k] = r < nr ? off[r0 + r] : 0;
-                ob[k] = r < nr ? off[r0 + r + 1] : 0;
-            }
-            double v[K];
+        for (int k = 0; k < K; ++k) {
+            const int32_t r = threadIdx.x + k * kBlock;
+            oa[k] = r < nr ? off[r0 + r] : 0;
+            ob[k] = r < nr ? off[r0 + r + 1] : 0;
+        }
+        double v[K];
 #pragma unroll
-            for (int k = 0; k < K; ++k) v[k] = id[k] >= 0 ? vl[id[k]] : 0.0;
+        for (int k = 0; k < K; ++k) v[k] = id[k] >= 0 ? vl[id[k]] : 0.0;
 #pragma unroll
-            for (int k = 0; k < K; ++k) {
-                const int32_t t = threadIdx.x + k * kBlock;
-                if (t < ne) stage[t] = v[k];
-            }
-            __syncthreads();
+        for (int k = 0; k < K; ++k) {
+            const int32_t t = threadIdx.x + k * kBlock;
+            if (t < ne) stage[t] = v[k];
+        }
+        __syncthreads();
 #pragma unroll
-            for (int k = 0; k < K; ++k) {
-                const int32_t r = threadIdx.x + k * kBlock;
-                if (r < nr) {
-                    double s = 0.0;
-                    for (int32_t j = oa[k] - e0; j < ob[k] - e0; ++j) s = s + stage[j];
-                    stp<P>(vg + r0 + r, s);
-                    if (kDot) acc = __builtin_fma(s, w[r0 + r], acc);
-                }
+        for (int k = 0; k < K; ++k) {
+            const int32_t r = threadIdx.x + k * kBlock;
+            if (r < nr) {
+                double s = 0.0;
+                for (int32_t j = oa[k] - e0; j < ob[k] - e0; ++j) s = s + stage[j];
+                stp<P>(vg + r0 + r, s);
+                if (kDot) acc = __builtin_fma(s, w[r0 + r], acc);
             }
         }
     }
@@ -1061,26 +1080,28 @@ __device__ __forceinline__ void gather_plan_body(const int32_t *__restrict__ bst
 }
 
 template <bool kDot>
-__global__ __launch_bounds__(kBlock) void k_gather_plan(const int32_t *__restrict__ bstart,
+__global__ __launch_bounds__(kBlock) void k_gather_plan(unsigned nblocks, const int32_t *__restrict__ bstart,
                                                         const int32_t *__restrict__ off,
                                                         const int32_t *__restrict__ ids,
                                                         const double *__restrict__ vl,
-                                                        double *__restrict__ vg, const double *__restrict__ w,
-                                                        double *__restrict__ partials, const double *cgs)
+                                                        double *__restrict__ vg, const double *cgs,
+                                                        const double *__restrict__ w,
+                                                        double *__restrict__ partials)
 {
-    gather_plan_body<kDot, kStream>(bstart, off, ids, vl, vg, w, partials, cgs);
+    gather_plan_body<kDot, kStream>(nblocks, bstart, off, ids, vl, vg, cgs, w, partials);
 }
 
 // The same with the cache-keeping policy, for the CG iteration.
 template <bool kDot>
-__global__ __launch_bounds__(kBlock) void k_gather_plan_keep(const int32_t *__restrict__ bstart,
-                                                             const int32_t *__restrict__ off,
-                                                             const int32_t *__restrict__ ids,
-                                                             const double *__restrict__ vl,
-                                                             double *__restrict__ vg, const double *__restrict__ w,
-                                                             double *__restrict__ partials, const double *cgs)
+__global__ __launch_bounds__(kBlock) void k_gather_plan_keep(unsigned nblocks, const int32_t *__restrict__ bstart,
+                                                        const int32_t *__restrict__ off,
+                                                        const int32_t *__restrict__ ids,
+                                                        const double *__restrict__ vl,
+                                                        double *__restrict__ vg, const double *cgs,
+                                                        const double *__restrict__ w,
+                                                        double *__restrict__ partials)
 {
-    gather_plan_body<kDot, kKeep>(bstart, off, ids, vl, vg, w, partials, cgs);
+    gather_plan_body<kDot, kKeep>(nblocks, bstart, off, ids, vl, vg, cgs, w, partials);
 }
 
 // Scalar (8-byte) versions of the vector ops for operands whose 16-byte
@@ -1290,14 +1311,15 @@ int dot_launch(bs_ctx *c, int64_t n, const double *x, const double *y, bool squa
     int64_t head;
     if (common_head(ptrs, 2, &head)) {
         const Split sp = split_of(n, head);
-        if (square)
-            launch(c, (k_dot<kNormShape.unroll, true, kNormShape.threads>),
-                   dim3(vector_grid(c, sp.n2, kNormShape, true)), dim3(kNormShape.threads), 0, st, sp.n2, x, x,
-                   sp.head, sp.tail, f);
-        else
-            launch(c, (k_dot<kDotShape.unroll, false, kDotShape.threads>),
-                   dim3(vector_grid(c, sp.n2, kDotShape, true)), dim3(kDotShape.threads), 0, st, sp.n2, x, y,
-                   sp.head, sp.tail, f);
+        if (square) {
+            const unsigned g = vector_grid(c, sp.n2, kNormShape, true);
+            launch(c, (k_dot<kNormShape.unroll, true, kNormShape.threads>), dim3(g), dim3(kNormShape.threads), 0, st,
+                   sp.n2, x, x, ht_of(sp), g, f);
+        } else {
+            const unsigned g = vector_grid(c, sp.n2, kDotShape, true);
+            launch(c, (k_dot<kDotShape.unroll, false, kDotShape.threads>), dim3(g), dim3(kDotShape.threads), 0, st,
+                   sp.n2, x, y, ht_of(sp), g, f);
+        }
         return launch_status();
     }
     const unsigned nb = scalar_grid(c, n);
@@ -1322,14 +1344,14 @@ int gather_launch(bs_ctx *c, int64_t ng, const int32_t *off, const int32_t *ids,
     if (bstart) {
         *nb = (unsigned)nblocks;
         if (w && keep)
-            launch(c, k_gather_plan_keep<true>, dim3(*nb), dim3(kBlock), 0, st, bstart, off, ids, vl, vg, w,
-                   c->partials, cgs);
+            launch(c, k_gather_plan_keep<true>, dim3(*nb), dim3(kBlock), 0, st, *nb, bstart, off, ids, vl, vg,
+                   cgs, w, c->partials);
         else if (w)
-            launch(c, k_gather_plan<true>, dim3(*nb), dim3(kBlock), 0, st, bstart, off, ids, vl, vg, w,
-                   c->partials, cgs);
+            launch(c, k_gather_plan<true>, dim3(*nb), dim3(kBlock), 0, st, *nb, bstart, off, ids, vl, vg, cgs,
+                   w, c->partials);
         else
-            launch(c, k_gather_plan<false>, dim3(*nb), dim3(kBlock), 0, st, bstart, off, ids, vl, vg,
-                   nullptr, nullptr, cgs);
+            launch(c, k_gather_plan<false>, dim3(*nb), dim3(kBlock), 0, st, *nb, bstart, off, ids, vl, vg,
+                   cgs, nullptr, nullptr);
     } else {
         const int64_t per = (int64_t)kBlock * kGatherRowR;
         *nb = (unsigned)((ng + per - 1) / per);
@@ -1491,8 +1513,8 @@ int bs_axpy(bs_ctx *c, int64_t n, double alpha, const double *x, double beta, do
     int64_t head;
     if (common_head(ptrs, 2, &head)) {
         const Split sp = split_of(n, head);
-        launch(c, k_axpy<kAxpyShape.unroll>, dim3(vector_grid(c, sp.n2, kAxpyShape, false)), dim3(kBlock),
-               0, st, sp.n2, x, y, alpha, beta, sp.head, sp.tail);
+        const unsigned g = vector_grid(c, sp.n2, kAxpyShape, false);
+        launch(c, k_axpy<kAxpyShape.unroll>, dim3(g), dim3(kBlock), 0, st, sp.n2, x, y, alpha, beta, ht_of(sp), g);
     } else {
         launch(c, k_axpy_scalar, dim3(scalar_grid(c, n)), dim3(kBlock), 0, st, n, alpha, x, beta, y);
     }
@@ -1559,9 +1581,9 @@ int bs_cg_update(bs_ctx *c, int64_t n, double alpha, const double *p, const doub
     int64_t head;
     if (common_head(ptrs, 4, &head)) {
         const Split sp = split_of(n, head);
-        launch(c, k_cg_update<kCgShape.unroll, kCgRUnroll, kCgShape.threads>,
-               dim3(vector_grid(c, sp.n2, kCgShape, true)), dim3(kCgShape.threads), 0, st, sp.n2, p, q, x, r, alpha,
-               sp.head, sp.tail, fin_out(c, rr, false));
+        const unsigned g = vector_grid(c, sp.n2, kCgShape, true);
+        launch(c, k_cg_update<kCgShape.unroll, kCgRUnroll, kCgShape.threads>, dim3(g), dim3(kCgShape.threads), 0, st,
+               sp.n2, p, q, x, r, alpha, ht_of(sp), g, fin_out(c, rr, false));
         return launch_status();
     }
     const unsigned nb = scalar_grid(c, n);
