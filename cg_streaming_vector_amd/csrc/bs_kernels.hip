@@ -264,7 +264,8 @@ struct Fin {
 };
 
 // Called by every thread of every block with the block's partial (valid in
-// thread 0); true in the block that is to finish.
+// thread 0) and the grid's block count nb; true in the block that is to
+// finish.
 __device__ __forceinline__ bool last_arrival(double part, const Fin &f, unsigned nb)
 {
     __shared__ bool last;
