@@ -160,9 +160,11 @@ class Mesh:
     ORDER = ["copy_x", "copy_y", "axpy_x", "axpy_y", "norm_x", "dot_x", "dot_y", "cg_p", "cg_q", "cg_x",
              "cg_r", "l2g", "sc_vg", "sc_vl", "off", "ids", "plan", "ga_vl", "ga_vg", "out"]
 
-    def __init__(self, bs, torch, dev, name, E, N, gather_lds, layout="arena", tables=None):
+    def __init__(self, bs, torch, dev, name, E, N, gather_lds, layout="arena", tables=None, plan_region=0):
         """A box of E^3 elements of order N, or, with tables = (l2g, n_global),
-        any mesh whose I_l->g is given."""
+        any mesh whose I_l->g is given. plan_region > 0: the gather plan
+        places its blocks by mesh region (a local layout made by
+        bs_mesh_xcd_interleave with runs of plan_region entries)."""
         self.name, self.E, self.N = name, E, N
         self.torch, self.dev, self.layout = torch, dev, layout
         if tables is None:
@@ -173,7 +175,7 @@ class Mesh:
             l2g, self.ng = tables
             self.nl = l2g.size
         off, ids = bs.bs_index_g2l(l2g, self.ng)
-        plan = bs.bs_gather_plan(off, GATHER_NPB)
+        plan = bs.bs_gather_plan(off, GATHER_NPB, ids, plan_region)
         v = bs_inputs.vectors(name, self.ng)
         b = bs_inputs.base_seed(name)
         self.gather_lds = gather_lds
@@ -219,7 +221,7 @@ class Mesh:
         P = lambda t: t.data_ptr()  # noqa: E731
         o = P(self.out)
         plan = P(self.plan) if self.gather_lds else None
-        nb = self.plan.shape[0] - 1 if self.gather_lds else 0
+        nb = self.plan.shape[0] if self.gather_lds else 0
         a = dict(
             copy=(L.bs_copy, (h, n, P(self.copy_x), P(self.copy_y), stream)),
             axpy=(L.bs_axpy, (h, n, 0.37, P(self.axpy_x), 1.0, P(self.axpy_y), stream)),
@@ -251,7 +253,7 @@ class Mesh:
             "cg_update": (self.ng, (self.cg_p, self.cg_q, self.cg_x, self.cg_r), 0),
             "scatter": (self.nl, (self.l2g, self.sc_vg, self.sc_vl), 0),
             "gather": (self.ng, (self.off, self.ids, self.ga_vl, self.ga_vg, plan),
-                       self.plan.shape[0] - 1 if self.gather_lds else 0),
+                       self.plan.shape[0] if self.gather_lds else 0),
         }[op]
 
     def bytes(self, op):
@@ -448,32 +450,41 @@ def sweep_summary(fits):
                  f["plateau_GBps"]] for op, f in fits.items()}
 
 
+XCD_CHUNK = 64  # elements per run of the XCD-interleaved storage order
+
+
 def tet_split_tables(bs, cubes, N, seed, order="gen"):
     """I_l->g of the unstructured tet-split mesh (cubes^3 unit cubes, 24
     hexahedra each, every element in a random orientation), with its elements
     stored in the generator's order (cube by cube, x fastest: "gen"), in a
-    random order, as a mesh file might present them ("shuffled"), or in that
+    random order, as a mesh file might present them ("shuffled"), in that
     random order put back along the library's Hilbert curve through the
-    element centroids (bs_mesh_hex_order: "curve"). Global ids are numbered by
-    first appearance in storage order, so they follow the element order."""
+    element centroids (bs_mesh_hex_order: "curve"), or in the generator's
+    order cut into eight regions interleaved in runs of XCD_CHUNK elements
+    (bs_mesh_xcd_interleave: "xcd"; its gather plan places blocks by region).
+    Global ids are numbered by first appearance in storage order, so they
+    follow the element order."""
     ev, nv, coords = bs_inputs.hex_tet_split(cubes, cubes, cubes)
     ev, _ = bs_inputs.hex_orient(ev, seed)
     if order in ("shuffled", "curve"):
         ev = np.ascontiguousarray(ev[bs_inputs.permutation(seed + 1, len(ev))])
     if order == "curve":
         ev = np.ascontiguousarray(ev[bs.bs_mesh_hex_order(coords[ev])])
+    if order == "xcd":
+        ev = np.ascontiguousarray(ev[bs.bs_mesh_xcd_interleave(len(ev), XCD_CHUNK)])
     return bs.bs_mesh_hex_l2g(ev, N, nv)
 
 
-WORKLOADS = ["shuffled40_N5", "tetsplit11_N7", "tetsplit11_N7_shuffled", "tetsplit11_N7_curve", "slab32x32x4_N7",
-             "box24_N15", "cg_box32_N7"]
+WORKLOADS = ["shuffled40_N5", "tetsplit11_N7", "tetsplit11_N7_xcd", "tetsplit11_N7_shuffled", "tetsplit11_N7_curve",
+             "slab32x32x4_N7", "box24_N15", "cg_box32_N7"]
 
 
 def workloads(bs, torch, dev, gather_lds, steps=30, only=None):
     """The shuffled 40^3 order-5 mesh (scatter, gather), the unstructured
     tet-split mesh of 11^3 cubes (31944 hexahedra) at order 7 (scatter,
-    gather) with its elements in the generator's order, in a random order,
-    and in that random order put back along the Hilbert curve, one GPU's share of the 32^3 order-7 mesh cut into eight z-slabs
+    gather) with its elements in the generator's order, interleaved by region
+    for the XCDs, in a random order, and in that random order put back along
+    the Hilbert curve, one GPU's share of the 32^3 order-7 mesh cut into eight z-slabs
     (32 x 32 x 4 elements, all 7 ops, and the CG streaming sequence, whose
     device-resident iteration there fits in the last-level cache), the 24^3
     order-15 mesh (all 7 ops, and the CG streaming sequence) and the CG
@@ -483,6 +494,7 @@ def workloads(bs, torch, dev, gather_lds, steps=30, only=None):
     out = {}
     for name, E, N, ops in [("shuffled40_N5", 40, 5, ["scatter", "gather"]),
                             ("tetsplit11_N7", 11, 7, ["scatter", "gather"]),
+                            ("tetsplit11_N7_xcd", 11, 7, ["scatter", "gather"]),
                             ("tetsplit11_N7_shuffled", 11, 7, ["scatter", "gather"]),
                             ("tetsplit11_N7_curve", 11, 7, ["scatter", "gather"]),
                             ("slab32x32x4_N7", 32, 7, OPS),
@@ -493,13 +505,14 @@ def workloads(bs, torch, dev, gather_lds, steps=30, only=None):
         tables = None
         if name.startswith("tetsplit"):
             tables = tet_split_tables(bs, E, N, bs_inputs.base_seed("tetsplit11_N7") + bs_inputs.SEED_ELEM,
-                                      order={"tetsplit11_N7_shuffled": "shuffled",
-                                             "tetsplit11_N7_curve": "curve"}.get(name, "gen"))
+                                      order={"tetsplit11_N7_shuffled": "shuffled", "tetsplit11_N7_curve": "curve",
+                                             "tetsplit11_N7_xcd": "xcd"}.get(name, "gen"))
         elif name.startswith("slab"):
             tables = (bs.bs_mesh_box_l2g(E, E, 4, N), bs.bs_mesh_box_count(E, E, 4, N)[1])
         # the CG-only workload runs on the step's own mesh and inputs
         src = "box32_N7" if name == "cg_box32_N7" else "tetsplit11_N7" if name.startswith("tetsplit") else name
-        m = Mesh(bs, torch, dev, src, E, N, gather_lds, tables=tables)
+        region = XCD_CHUNK * (N + 1) ** 3 if name.endswith("_xcd") else 0
+        m = Mesh(bs, torch, dev, src, E, N, gather_lds, tables=tables, plan_region=region)
         if tables is not None:
             out[name + "_mesh"] = {"elements": 24 * E ** 3 if name.startswith("tetsplit") else E * E * 4, "order": N,
                                    "n_local": m.nl, "n_global": m.ng}
@@ -533,7 +546,7 @@ def cg_sequence(bs, torch, dev, m, iters=100):
     q, pl = torch.empty_like(b), m.sc_vl
     o = torch.zeros(2, dtype=torch.float64, device=dev)
     plan = P(m.plan) if m.gather_lds else None
-    nb = m.plan.shape[0] - 1 if m.gather_lds else 0
+    nb = m.plan.shape[0] if m.gather_lds else 0
 
     def it(alpha, beta):
         assert L.bs_scatter(h, nl, P(m.l2g), P(p), P(pl), st) == 0

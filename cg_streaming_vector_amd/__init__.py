@@ -77,7 +77,8 @@ SIGNATURES = {
     "bs_validate_g2l": ([_i64, _i64, _ptr, _ptr, _ptr], _int),
     "bs_validate_plan": ([_i64, _ptr, _ptr, _i64], _int),
     "bs_index_g2l": ([_i64, _i64, _ptr, _ptr, _ptr], _int),
-    "bs_gather_plan": ([_i64, _ptr, _int, _ptr, ctypes.POINTER(_i64)], _int),
+    "bs_gather_plan": ([_i64, _ptr, _ptr, _int, _i64, _ptr, ctypes.POINTER(_i64)], _int),
+    "bs_mesh_xcd_interleave": ([_i64, _i64, _ptr], _int),
     "bs_bench_loop": ([_ptr, _int, _i64, _dbl, _dbl, _i64, _int, _ptr, _ptr, _int, _ptr, ctypes.POINTER(_dbl)],
                       _int),
 }
@@ -210,14 +211,14 @@ def _ctx_dev(t, ctx, stream=None):
 
 def _plan_dev(block_starts):
     """(pointer, n_blocks) of a device gather plan, or (None, 0) for none: the
-    (n_blocks + 1, 2) int32 tensor of (row, first entry) pairs that
-    bs_gather_plan builds."""
+    (n_blocks, 4) int32 tensor of (first row, end row, first entry, end
+    entry) blocks in launch order that bs_gather_plan builds."""
     import torch
     if block_starts is None:
         return None, 0
-    if block_starts.dim() != 2 or block_starts.shape[1] != 2 or block_starts.shape[0] < 1:
-        raise ValueError("block_starts must be the (n_blocks + 1, 2) pairs of bs_gather_plan")
-    return _dev_tensor(block_starts, torch.int32, "block_starts"), block_starts.shape[0] - 1
+    if block_starts.dim() != 2 or block_starts.shape[1] != 4 or block_starts.shape[0] < 1:
+        raise ValueError("block_starts must be the (n_blocks, 4) plan of bs_gather_plan")
+    return _dev_tensor(block_starts, torch.int32, "block_starts"), block_starts.shape[0]
 
 
 def _scalar_out(out, like):
@@ -518,18 +519,18 @@ def bs_validate_g2l(off, ids, n_local, l2g=None):
            "bs_validate_g2l")
 
 
-def bs_validate_plan(block_starts, off):
-    """Raise BSError unless block_starts is a well-formed gather plan for the
-    CSR offsets off (n_global + 1 entries): (n_blocks + 1, 2) int32 pairs of
-    (row, first entry)."""
-    bs_ = np.asarray(block_starts)
-    if bs_.ndim != 2 or bs_.shape[1] != 2 or bs_.shape[0] < 1:
-        raise ValueError("block_starts must be (n_blocks + 1, 2) pairs")
-    bs_ = _host_i32(bs_, "block_starts")
+def bs_validate_plan(plan, off):
+    """Raise BSError unless plan is a well-formed gather plan for the CSR
+    offsets off (n_global + 1 entries): (n_blocks, 4) int32 blocks of (first
+    row, end row, first entry, end entry)."""
+    p = np.asarray(plan)
+    if p.ndim != 2 or p.shape[1] != 4:
+        raise ValueError("plan must be (n_blocks, 4)")
+    p = _host_i32(p, "plan")
     off = _host_i32(off, "off")
     if off.size < 1:
         raise ValueError("off needs n_global + 1 >= 1 entries")
-    _check(_lib().bs_validate_plan(off.size - 1, off.ctypes.data, bs_.ctypes.data, bs_.shape[0] - 1),
+    _check(_lib().bs_validate_plan(off.size - 1, off.ctypes.data, p.ctypes.data if p.size else None, p.shape[0]),
            "bs_validate_plan")
 
 
@@ -543,16 +544,34 @@ def bs_index_g2l(l2g, n_global):
     return off, ids[:int(off[-1])]
 
 
-def bs_gather_plan(off, nodes_per_block=1024):
-    """blockStarts for the LDS-staged gather: an int32 numpy array of shape
-    (n_blocks + 1, 2), each block's first row and its first CSR entry."""
+def bs_gather_plan(off, nodes_per_block=1024, ids=None, region_entries=0):
+    """The LDS-staged gather's plan: an int32 numpy array of shape
+    (n_blocks, 4), each block's (first row, end row, first entry, end entry)
+    in launch order. region_entries > 0 places the blocks by mesh region
+    (the local layout of bs_mesh_xcd_interleave) and needs the CSR ids."""
     off = _host_i32(off, "off")
     ng = off.size - 1
-    bs = np.empty((ng + 1, 2), dtype=np.int32)
+    if int(region_entries) > 0:
+        if ids is None:
+            raise ValueError("region placement needs the CSR ids")
+        ids = _host_i32(ids, "ids")
+        if ids.size < int(off[-1]):
+            raise ValueError("ids holds fewer entries than off names")
+    plan = np.empty((max(ng, 1), 4), dtype=np.int32)
     nb = _i64()
-    _check(_lib().bs_gather_plan(ng, off.ctypes.data, int(nodes_per_block), bs.ctypes.data, ctypes.byref(nb)),
+    _check(_lib().bs_gather_plan(ng, off.ctypes.data, None if ids is None else ids.ctypes.data,
+                                 int(nodes_per_block), int(region_entries), plan.ctypes.data, ctypes.byref(nb)),
            "bs_gather_plan")
-    return bs[:nb.value + 1].copy()
+    return plan[:nb.value].copy()
+
+
+def bs_mesh_xcd_interleave(n_elements, chunk):
+    """Storage order interleaving eight consecutive regions of the given
+    element order in runs of chunk elements: int32 perm, perm[s] = the
+    element stored at slot s."""
+    perm = np.empty(max(int(n_elements), 1), dtype=np.int32)
+    _check(_lib().bs_mesh_xcd_interleave(int(n_elements), int(chunk), perm.ctypes.data), "bs_mesh_xcd_interleave")
+    return perm[:int(n_elements)].copy()
 
 
 BS_OP = {"copy": 0, "axpy": 1, "norm": 2, "dot": 3, "cg_update": 4, "scale": 5, "scatter": 6, "gather": 7}
@@ -567,7 +586,7 @@ def bs_bench_loop(op, n, sets, reps, result=None, alpha=0.37, beta=1.0, *, n_blo
     cycling through `sets` (a list of tuples of device tensors in the order
     the header lists for the op). Vector operations take n = their length,
     scatter n = n_local, gather n = n_global; a gather set's fifth tensor is
-    the blockStarts plan ((n_blocks + 1, 2) pairs) or None."""
+    the gather plan ((n_blocks, 4) blocks) or None."""
     import torch
     if op not in BS_OP:
         raise ValueError(f"unknown op {op!r}")
@@ -587,9 +606,9 @@ def bs_bench_loop(op, n, sets, reps, result=None, alpha=0.37, beta=1.0, *, n_blo
         elif op == "gather":
             if group[0].numel() < n + 1 or group[3].numel() < n:
                 raise ValueError("gather: off needs n_global + 1 entries and v_global n_global")
-            if group[4] is not None and (group[4].dim() != 2 or group[4].shape[1] != 2 or
-                                         group[4].shape[0] < n_blocks + 1):
-                raise ValueError("gather: block_starts must be (>= n_blocks + 1, 2) pairs")
+            if group[4] is not None and (group[4].dim() != 2 or group[4].shape[1] != 4 or
+                                         group[4].shape[0] < n_blocks):
+                raise ValueError("gather: block_starts must be a (>= n_blocks, 4) plan")
         for j, (t, kind) in enumerate(zip(group, slots)):
             if t is None:
                 if not (op == "gather" and j == 4):
@@ -615,5 +634,5 @@ __all__ = [
     "bs_copy", "bs_axpy", "bs_norm", "bs_dot", "bs_cg_update", "bs_scatter", "bs_gather",
     "bs_gather_dot", "bs_cg_solve", "bs_cg_solve_static", "bs_scale", "bs_gll", "bs_mesh_box_mass",
     "bs_bench_loop", "BS_OP", "BS_BENCH_SET",
-    "bs_mesh_box_count", "bs_mesh_box_l2g", "bs_mesh_hex_l2g", "bs_mesh_hex_mass", "bs_mesh_hex_order", "bs_validate_l2g", "bs_validate_g2l", "bs_validate_plan", "bs_index_g2l", "bs_gather_plan",
+    "bs_mesh_box_count", "bs_mesh_box_l2g", "bs_mesh_hex_l2g", "bs_mesh_hex_mass", "bs_mesh_hex_order", "bs_validate_l2g", "bs_validate_g2l", "bs_validate_plan", "bs_index_g2l", "bs_gather_plan", "bs_mesh_xcd_interleave",
 ]

@@ -30,6 +30,11 @@
 #include "bs.h"
 
 namespace {
+// MI355X has eight XCDs; gather plans place their blocks for them.
+constexpr int64_t kXcds = 8, kXcdRun = 8;
+}  // namespace
+
+namespace {
 
 // Throws std::bad_alloc; every caller converts that into BS_ENOMEM.
 bool is_permutation(const int32_t *p, int64_t n)
@@ -527,20 +532,29 @@ int bs_validate_g2l(int64_t n_global, int64_t n_local, const int32_t *off, const
     return BS_OK;
 }
 
-int bs_validate_plan(int64_t n_global, const int32_t *off, const int32_t *block_starts, int64_t n_blocks)
+int bs_validate_plan(int64_t n_global, const int32_t *off, const int32_t *plan, int64_t n_blocks)
 {
-    if (n_global < 0 || n_blocks < 0 || !block_starts || !off) return BS_EINVAL;
+    if (n_global < 0 || n_blocks < 0 || !off || (n_blocks > 0 && !plan)) return BS_EINVAL;
     if (n_global >= INT32_MAX) return BS_ERANGE;
-    if (n_global == 0)
-        return n_blocks == 0 && block_starts[0] == 0 && block_starts[1] == off[0] ? BS_OK : BS_EINVAL;
+    if (n_global == 0) return n_blocks == 0 ? BS_OK : BS_EINVAL;
     if (n_blocks < 1 || n_blocks > n_global) return BS_EINVAL;
-    if (block_starts[0] != 0 || block_starts[2 * n_blocks] != n_global) return BS_EINVAL;
-    for (int64_t b = 0; b < n_blocks; ++b)
-        if (block_starts[2 * b + 2] <= block_starts[2 * b]) return BS_EINVAL;
-    // each block's first entry is the CSR offset of its first row (the rows
-    // are in range now)
-    for (int64_t b = 0; b <= n_blocks; ++b)
-        if (block_starts[2 * b + 1] != off[block_starts[2 * b]]) return BS_EINVAL;
+    try {
+        // each block a non-empty row range with the offsets of its ends; the
+        // ranges, in any launch order, tile [0, n_global) once
+        std::vector<std::pair<int32_t, int32_t>> rows((size_t)n_blocks);
+        for (int64_t b = 0; b < n_blocks; ++b) {
+            const int32_t *q = plan + 4 * b;
+            if (q[0] < 0 || q[0] >= q[1] || q[1] > n_global) return BS_EINVAL;
+            if (q[2] != off[q[0]] || q[3] != off[q[1]]) return BS_EINVAL;
+            rows[(size_t)b] = {q[0], q[1]};
+        }
+        std::sort(rows.begin(), rows.end());
+        if (rows.front().first != 0 || rows.back().second != n_global) return BS_EINVAL;
+        for (size_t b = 1; b < rows.size(); ++b)
+            if (rows[b].first != rows[b - 1].second) return BS_EINVAL;
+    } catch (const std::bad_alloc &) {
+        return BS_ENOMEM;
+    }
     return BS_OK;
 }
 
@@ -571,39 +585,112 @@ int bs_index_g2l(int64_t n_local, int64_t n_global, const int32_t *l2g, int32_t 
     return BS_OK;
 }
 
-int bs_gather_plan(int64_t n_global, const int32_t *off, int nodes_per_block, int32_t *block_starts,
-                   int64_t *n_blocks)
+int bs_gather_plan(int64_t n_global, const int32_t *off, const int32_t *ids, int nodes_per_block,
+                   int64_t region_entries, int32_t *plan, int64_t *n_blocks)
 {
-    if (n_global < 0 || !off || !block_starts || !n_blocks) return BS_EINVAL;
+    if (n_global < 0 || !off || (n_global > 0 && !plan) || !n_blocks || region_entries < 0) return BS_EINVAL;
+    if (region_entries > 0 && n_global > 0 && !ids) return BS_EINVAL;
     if (nodes_per_block < 1 || nodes_per_block > 1024) return BS_EINVAL;
     if (n_global >= INT32_MAX) return BS_ERANGE;
-    // greedy: extend the block row by row while it holds at most
-    // nodes_per_block rows and nodes_per_block entries; a row longer than
-    // that gets a block of its own. Then, unless it is the last block, its
-    // end is rounded down to a multiple of kPlanAlign rows if that leaves
-    // the block non-empty: every block then writes whole 128-byte lines of
-    // v_global (16 doubles), where blocks cut at arbitrary rows left two
-    // partial lines each (measured 2-3% faster gathers on the boxes, 1.6%
-    // on an unstructured mesh, same bits). Each block start is stored with
-    // its first CSR entry, off[row], so that the gather kernel starts its
-    // id loads without first loading the offset (2-4% faster).
+    // Blocks in row order, greedily: extend the block row by row while it
+    // holds at most nodes_per_block rows and nodes_per_block entries; a row
+    // longer than that gets a block of its own. Then, unless it is the last
+    // block, its end is rounded down to a multiple of kPlanAlign rows if that
+    // leaves the block non-empty: every block then writes whole 128-byte
+    // lines of v_global (16 doubles), where blocks cut at arbitrary rows left
+    // two partial lines each (measured 2-3% faster gathers on the boxes, 1.6%
+    // on an unstructured mesh, same bits).
     constexpr int64_t kPlanAlign = 16;
-    int64_t nb = 0;
-    int64_t g = 0;
-    block_starts[0] = 0;
-    block_starts[1] = off[0];
-    while (g < n_global) {
-        const int64_t start = off[g];
-        int64_t end = g + 1;
-        while (end < n_global && end - g < nodes_per_block && (int64_t)off[end + 1] - start <= nodes_per_block)
-            ++end;
-        if (end < n_global && end - end % kPlanAlign > g) end -= end % kPlanAlign;
-        ++nb;
-        block_starts[2 * nb] = (int32_t)end;
-        block_starts[2 * nb + 1] = off[end];
-        g = end;
+    try {
+        std::vector<int32_t> start;
+        for (int64_t g = 0; g < n_global;) {
+            const int64_t first = off[g];
+            int64_t end = g + 1;
+            while (end < n_global && end - g < nodes_per_block && (int64_t)off[end + 1] - first <= nodes_per_block)
+                ++end;
+            if (end < n_global && end - end % kPlanAlign > g) end -= end % kPlanAlign;
+            start.push_back((int32_t)g);
+            g = end;
+        }
+        const int64_t nb = (int64_t)start.size();
+        start.push_back((int32_t)n_global);
+        // Launch order. The hardware hands the workgroups of a launch to the
+        // eight XCDs in turn (workgroup s to XCD s mod 8), each XCD with an
+        // L2 of its own, and blocks that read the same lines of v_local
+        // should meet in one L2.
+        std::vector<int64_t> order((size_t)nb);
+        if (region_entries == 0) {
+            // Neighbouring blocks read neighbouring lines: each XCD takes
+            // runs of kXcdRun consecutive blocks while the eight XCDs work
+            // in one narrow window of the arrays (runs of 8 measured best
+            // against 4, 16 and one contiguous range per XCD). Slots past
+            // the last whole round keep their own block.
+            const int64_t span = kXcds * kXcdRun, full = nb / span * span;
+            for (int64_t s = 0; s < nb; ++s) {
+                const int64_t x = s % kXcds, k = s / kXcds;
+                order[(size_t)s] = s >= full ? s : ((k / kXcdRun) * kXcds + x) * kXcdRun + k % kXcdRun;
+            }
+        } else {
+            // Local storage interleaves eight regions in runs of
+            // region_entries entries (bs_mesh_xcd_interleave): a block
+            // belongs to the region of its first entry, which is its first
+            // row's first copy, and XCD x takes the blocks of region x in
+            // order. An XCD whose region has run out takes from the region
+            // with the most blocks left.
+            std::vector<std::vector<int64_t>> queue(kXcds);
+            for (int64_t b = 0; b < nb; ++b) {
+                const int32_t e0 = off[start[(size_t)b]], e1 = off[start[(size_t)b + 1]];
+                const int64_t x = e1 > e0 ? ((int64_t)ids[e0] / region_entries) % kXcds : b % kXcds;
+                queue[(size_t)x].push_back(b);
+            }
+            size_t next[kXcds] = {};
+            for (int64_t s = 0; s < nb; ++s) {
+                int64_t x = s % kXcds;
+                if (next[x] == queue[(size_t)x].size()) {
+                    size_t most = 0;
+                    for (int64_t y = 0; y < kXcds; ++y) {
+                        const size_t left = queue[(size_t)y].size() - next[y];
+                        if (left > most) most = left, x = y;
+                    }
+                }
+                order[(size_t)s] = queue[(size_t)x][next[x]++];
+            }
+        }
+        // Each block as (first row, end row, first entry, end entry), the
+        // entries being off at those rows, so that a block's whole extent
+        // arrives in one round of scalar loads.
+        for (int64_t s = 0; s < nb; ++s) {
+            const int64_t b = order[(size_t)s];
+            const int32_t r0 = start[(size_t)b], r1 = start[(size_t)b + 1];
+            int32_t *q = plan + 4 * s;
+            q[0] = r0;
+            q[1] = r1;
+            q[2] = off[r0];
+            q[3] = off[r1];
+        }
+        *n_blocks = nb;
+    } catch (const std::bad_alloc &) {
+        return BS_ENOMEM;
     }
-    *n_blocks = nb;
+    return BS_OK;
+}
+
+int bs_mesh_xcd_interleave(int64_t n_elements, int64_t chunk, int32_t *perm)
+{
+    if (n_elements < 0 || chunk < 1 || (n_elements > 0 && !perm)) return BS_EINVAL;
+    if (n_elements > INT32_MAX) return BS_ERANGE;
+    // Region x owns the storage slots s with (s / chunk) mod 8 == x and takes
+    // the next count[x] elements of the given order, keeping their order.
+    const int64_t round = kXcds * chunk, full = n_elements / round, rest = n_elements % round;
+    int64_t first[kXcds];
+    for (int64_t x = 0, sum = 0; x < kXcds; ++x) {
+        first[x] = sum;
+        sum += full * chunk + std::min(std::max(rest - x * chunk, (int64_t)0), chunk);
+    }
+    for (int64_t s = 0; s < n_elements; ++s) {
+        const int64_t x = (s / chunk) % kXcds;
+        perm[s] = (int32_t)(first[x] + (s / round) * chunk + s % chunk);
+    }
     return BS_OK;
 }
 

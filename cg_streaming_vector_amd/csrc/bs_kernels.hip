@@ -975,45 +975,22 @@ __global__ __launch_bounds__(kBlock) void k_gather_rows(int64_t ng, const int32_
     }
 }
 
-// Which blockStarts block a workgroup takes. The hardware hands consecutive
-// workgroups to the eight XCDs in turn, each XCD with its own L2, and
-// neighbouring node blocks read neighbouring lines of v_L; so each XCD gets
-// runs of kXcdRun consecutive node blocks, while the eight XCDs still work in
-// one narrow window of the arrays. Workgroups past the last whole round keep
-// their own index. Longer runs leave fewer v_L lines to be fetched by two
-// XCDs, shorter ones keep the window narrow: runs of 8 measured best (against
-// 4: equal on the 32^3 order-7 box, 1% faster on the tet-split mesh, 0.4% at
-// 24^3 order 15; runs of 16 and one contiguous range per XCD were slower on
-// the boxes). nblocks is the grid size, passed as a kernel argument: it
-// arrives preloaded in an SGPR, where the hidden grid-size argument would
-// cost a scalar load before the block knows its plan block.
-constexpr unsigned kXcds = 8, kXcdRun = 8;
-__device__ __forceinline__ unsigned gather_block(unsigned nblocks)
-{
-    constexpr unsigned span = kXcds * kXcdRun;
-    const unsigned b = blockIdx.x, full = nblocks / span * span;
-    if (b >= full) return b;
-    const unsigned x = b % kXcds, k = b / kXcds;
-    return ((k / kXcdRun) * kXcds + x) * kXcdRun + k % kXcdRun;
-}
-
-// LDS-staged kernel after the blockStarts scheme of the paper: the plan
-// holds (row, first CSR entry) pairs, and block b owns rows bs[2b] ..
-// bs[2b+2]), which bs_gather_plan caps at kGatherCap rows and kGatherCap
-// entries (a single longer row gets a block of its own). The block reads its
-// rows and its first and end entry from the plan with uniform (scalar)
-// loads, so each lane can then issue at once its CSR ids (consecutive lanes
-// on consecutive entries) and the two offsets of each row it will sum. The
-// v_L values the ids name are fetched, staged in LDS, and after the one
-// barrier each lane sums its rows from LDS in ascending entry order. (Offsets
-// staged in LDS instead, behind a barrier of their own, measured 0.7-2.8%
-// slower; the first entry loaded from the offsets rather than the plan,
-// 1-4% slower.) Blocks over capacity read global memory. The kernels take
-// every argument the block needs before its first vector load among the
-// preloaded ones (block count, plan, tables, cgs); with those fetched by
-// scalar loads, and the plan in two rounds, it was 0.6-1.4% slower.
+// LDS-staged kernel after the blockStarts scheme of the paper: workgroup s
+// takes plan block s, rows r0 .. r1) with CSR entries e0 .. e1), which
+// bs_gather_plan caps at kGatherCap rows and kGatherCap entries (a single
+// longer row gets a block of its own) and orders for the XCDs. The block
+// reads its four plan words with uniform (scalar) loads in one round, so
+// each lane can then issue at once its CSR ids (consecutive lanes on
+// consecutive entries) and the two offsets of each row it will sum. The v_L
+// values the ids name are fetched, staged in LDS, and after the one barrier
+// each lane sums its rows from LDS in ascending entry order. (Offsets staged
+// in LDS instead, behind a barrier of their own, measured 0.7-2.8% slower;
+// the entries loaded from the offsets rather than the plan, 1-4% slower.)
+// Blocks over capacity read global memory. Every argument the block needs
+// before its first vector load is among the preloaded ones (plan, tables,
+// cgs).
 template <bool kDot, int P>
-__device__ __forceinline__ void gather_plan_body(unsigned nblocks, const int32_t *__restrict__ bstart,
+__device__ __forceinline__ void gather_plan_body(const int32_t *__restrict__ plan,
                                                  const int32_t *__restrict__ off,
                                                  const int32_t *__restrict__ ids,
                                                  const double *__restrict__ vl,
@@ -1024,11 +1001,10 @@ __device__ __forceinline__ void gather_plan_body(unsigned nblocks, const int32_t
     if (skipped(cgs)) return;
     constexpr int K = kGatherCap / kBlock;  // entries per lane, and rows per lane at most
     __shared__ double stage[kGatherCap];
-    const unsigned lb = gather_block(nblocks);
-    // both of the block's pairs in one round of scalar loads, before any
+    // the block's four plan words in one round of scalar loads, before any
     // test uses them
-    const int32_t r0 = bstart[2 * lb], e0 = bstart[2 * lb + 1];
-    const int32_t r1 = bstart[2 * lb + 2], e1 = bstart[2 * lb + 3];
+    const int32_t *q = static_cast<const int32_t *>(__builtin_assume_aligned(plan + 4 * blockIdx.x, 16));
+    const int32_t r0 = q[0], r1 = q[1], e0 = q[2], e1 = q[3];
     const int32_t nr = r1 - r0, ne = e1 - e0;
     double acc = 0.0;
     bool staged = false;
@@ -1081,7 +1057,7 @@ __device__ __forceinline__ void gather_plan_body(unsigned nblocks, const int32_t
 }
 
 template <bool kDot>
-__global__ __launch_bounds__(kBlock) void k_gather_plan(unsigned nblocks, const int32_t *__restrict__ bstart,
+__global__ __launch_bounds__(kBlock) void k_gather_plan(const int32_t *__restrict__ plan,
                                                         const int32_t *__restrict__ off,
                                                         const int32_t *__restrict__ ids,
                                                         const double *__restrict__ vl,
@@ -1089,12 +1065,12 @@ __global__ __launch_bounds__(kBlock) void k_gather_plan(unsigned nblocks, const 
                                                         const double *__restrict__ w,
                                                         double *__restrict__ partials)
 {
-    gather_plan_body<kDot, kStream>(nblocks, bstart, off, ids, vl, vg, cgs, w, partials);
+    gather_plan_body<kDot, kStream>(plan, off, ids, vl, vg, cgs, w, partials);
 }
 
 // The same with the cache-keeping policy, for the CG iteration.
 template <bool kDot>
-__global__ __launch_bounds__(kBlock) void k_gather_plan_keep(unsigned nblocks, const int32_t *__restrict__ bstart,
+__global__ __launch_bounds__(kBlock) void k_gather_plan_keep(const int32_t *__restrict__ plan,
                                                         const int32_t *__restrict__ off,
                                                         const int32_t *__restrict__ ids,
                                                         const double *__restrict__ vl,
@@ -1102,7 +1078,7 @@ __global__ __launch_bounds__(kBlock) void k_gather_plan_keep(unsigned nblocks, c
                                                         const double *__restrict__ w,
                                                         double *__restrict__ partials)
 {
-    gather_plan_body<kDot, kKeep>(nblocks, bstart, off, ids, vl, vg, cgs, w, partials);
+    gather_plan_body<kDot, kKeep>(plan, off, ids, vl, vg, cgs, w, partials);
 }
 
 // Scalar (8-byte) versions of the vector ops for operands whose 16-byte
@@ -1345,13 +1321,13 @@ int gather_launch(bs_ctx *c, int64_t ng, const int32_t *off, const int32_t *ids,
     if (bstart) {
         *nb = (unsigned)nblocks;
         if (w && keep)
-            launch(c, k_gather_plan_keep<true>, dim3(*nb), dim3(kBlock), 0, st, *nb, bstart, off, ids, vl, vg,
+            launch(c, k_gather_plan_keep<true>, dim3(*nb), dim3(kBlock), 0, st, bstart, off, ids, vl, vg,
                    cgs, w, c->partials);
         else if (w)
-            launch(c, k_gather_plan<true>, dim3(*nb), dim3(kBlock), 0, st, *nb, bstart, off, ids, vl, vg, cgs,
+            launch(c, k_gather_plan<true>, dim3(*nb), dim3(kBlock), 0, st, bstart, off, ids, vl, vg, cgs,
                    w, c->partials);
         else
-            launch(c, k_gather_plan<false>, dim3(*nb), dim3(kBlock), 0, st, *nb, bstart, off, ids, vl, vg,
+            launch(c, k_gather_plan<false>, dim3(*nb), dim3(kBlock), 0, st, bstart, off, ids, vl, vg,
                    cgs, nullptr, nullptr);
     } else {
         const int64_t per = (int64_t)kBlock * kGatherRowR;
@@ -1375,7 +1351,8 @@ int gather_args(const bs_ctx *c, int64_t n_global, const int32_t *off, const int
                          misaligned(v_global, 8)))
         return BS_EALIGN;
     if (block_starts && n_global > 0) {
-        if (n_blocks < 1 || n_blocks > n_global || misaligned(block_starts, 4)) return BS_EINVAL;
+        if (n_blocks < 1 || n_blocks > n_global) return BS_EINVAL;
+        if (misaligned(block_starts, 16)) return BS_EALIGN;
     }
     // the fused dot writes one partial per block
     const int64_t rows_per_block = (int64_t)kBlock * kGatherRowR;
@@ -1697,7 +1674,7 @@ int cg_solve_run(bs_ctx *c, int64_t n_global, int64_t n_local, const int32_t *l2
     // operations (measured: 7-12% faster per iteration up to ~190 MB, equal
     // near 320 MB, 11% slower at 680 MB with the keeping policy).
     const int64_t working_set = 8 * (4 * n_global + n_local) + 4 * (2 * n_local + n_global + 1) +
-                                (block_starts ? 8 * (n_blocks + 1) : 0);
+                                (block_starts ? 16 * n_blocks : 0);
     const bool keep = working_set <= kCacheResidentBytes;
     // Otherwise, while r and p alone fit, the update hands them to the
     // direction update through the cache (1-3% per iteration at 24^3-32^3,

@@ -87,10 +87,13 @@ void check_tables(const std::vector<int32_t> &l2g, int64_t ng)
     CHECK(std::equal(ids.begin(), ids.begin() + m, oids.begin()));
     CHECK(bs_validate_g2l(ng, nl, off.data(), ids.data(), l2g.data()) == BS_OK);
     for (int npb : {1, 3, 64, 1000, 1024}) {
-        std::vector<int32_t> plan(2 * ((size_t)ng + 1));
+        std::vector<int32_t> plan(4 * (size_t)ng);
         int64_t nb = -1;
-        CHECK(bs_gather_plan(ng, off.data(), npb, plan.data(), &nb) == BS_OK);
+        CHECK(bs_gather_plan(ng, off.data(), ids.data(), npb, 0, plan.data(), &nb) == BS_OK);
         CHECK(nb >= 1 && nb <= ng);
+        CHECK(bs_validate_plan(ng, off.data(), plan.data(), nb) == BS_OK);
+        // placed by region as if the local vector interleaved runs of 37 entries
+        CHECK(bs_gather_plan(ng, off.data(), ids.data(), npb, 37, plan.data(), &nb) == BS_OK);
         CHECK(bs_validate_plan(ng, off.data(), plan.data(), nb) == BS_OK);
     }
     // the oracle's scatter and gather on these tables: gather(1) is the multiplicity
@@ -176,14 +179,27 @@ void errors()
     std::vector<int32_t> l2g(8);
     std::vector<int32_t> notperm = {0, 1, 2, 3, 4, 5, 6, 6};
     CHECK(bs_mesh_box_l2g(2, 2, 2, 1, notperm.data(), nullptr, std::vector<int32_t>(64).data()) == BS_EINVAL);
-    std::vector<int32_t> ids = {0, 1, 5}, off(6), col(4), plan(14);
+    std::vector<int32_t> ids = {0, 1, 5}, off(6), col(4), plan(20);
     CHECK(bs_index_g2l(3, 5, ids.data(), off.data(), col.data()) == BS_EINVAL);
     CHECK(bs_validate_l2g(3, 5, ids.data()) == BS_EINVAL);
     std::vector<int32_t> good = {0, 1, 2, 3, 4}, col5(5);
     CHECK(bs_index_g2l(5, 5, good.data(), off.data(), col5.data()) == BS_OK);
     int64_t nb = 0;
-    CHECK(bs_gather_plan(5, off.data(), 0, plan.data(), &nb) == BS_EINVAL);
-    CHECK(bs_gather_plan(5, off.data(), 1025, plan.data(), &nb) == BS_EINVAL);
+    CHECK(bs_gather_plan(5, off.data(), nullptr, 0, 0, plan.data(), &nb) == BS_EINVAL);
+    CHECK(bs_gather_plan(5, off.data(), nullptr, 1025, 0, plan.data(), &nb) == BS_EINVAL);
+    CHECK(bs_gather_plan(5, off.data(), nullptr, 4, 8, plan.data(), &nb) == BS_EINVAL);
+    CHECK(bs_gather_plan(5, off.data(), nullptr, 4, -1, plan.data(), &nb) == BS_EINVAL);
+    {
+        std::vector<int32_t> perm(1000);
+        CHECK(bs_mesh_xcd_interleave(1000, 13, perm.data()) == BS_OK);
+        std::vector<int32_t> seen(1000, 0);
+        for (int32_t v : perm) {
+            CHECK(v >= 0 && v < 1000);
+            ++seen[(size_t)v];
+        }
+        for (int32_t c : seen) CHECK(c == 1);
+        CHECK(bs_mesh_xcd_interleave(10, 0, perm.data()) == BS_EINVAL);
+    }
     CHECK(bs_validate_plan(5, off.data(), nullptr, 1) == BS_EINVAL);
     CHECK(bs_validate_plan(5, nullptr, plan.data(), 1) == BS_EINVAL);
     CHECK(bs_validate_g2l(-1, 0, off.data(), nullptr, nullptr) == BS_EINVAL);

@@ -200,17 +200,37 @@ def plan_rule(off, npb):
     return starts
 
 
+def plan_tiling(plan, off):
+    """Row starts of a plan's blocks in row order, after checking each block's
+    entries against the offsets and that the row ranges tile [0, n_global)."""
+    ng = len(off) - 1
+    assert plan.ndim == 2 and plan.shape[1] == 4
+    assert np.array_equal(plan[:, 2], off[plan[:, 0]]) and np.array_equal(plan[:, 3], off[plan[:, 1]])
+    rows = plan[np.argsort(plan[:, 0], kind="stable"), :2]
+    assert rows[0, 0] == 0 and rows[-1, 1] == ng and np.array_equal(rows[1:, 0], rows[:-1, 1])
+    assert np.all(rows[:, 1] > rows[:, 0])
+    return list(rows[:, 0]) + [ng]
+
+
+def runs_slots(nb):
+    """Block (in row order) launched at each slot with runs of 8 per XCD: in
+    round r of 64 blocks, XCD x's k-th slot, 64r + 8k + x, takes block
+    64r + 8x + k; slots past the last whole round keep their own block."""
+    out = list(range(nb))
+    for r in range(nb // 64):
+        for x in range(8):
+            for k in range(8):
+                out[64 * r + 8 * k + x] = 64 * r + 8 * x + k
+    return out
+
+
 @pytest.mark.parametrize("npb", [1, 8, 256, 512, 1000, 1024])
 def test_gather_plan(bs, npb):
     l2g = bs.bs_mesh_box_l2g(6, 5, 4, 3)
     ng = bs.bs_mesh_box_count(6, 5, 4, 3)[1]
     off, _ = bs.bs_index_g2l(l2g, ng)
-    pairs = bs.bs_gather_plan(off, npb)
-    plan = pairs[:, 0]
-    # each block start carries its first CSR entry
-    assert pairs.shape == (plan.size, 2) and np.array_equal(pairs[:, 1], off[plan])
-    assert plan[0] == 0 and plan[-1] == ng
-    assert np.all(np.diff(plan) >= 1)
+    blocks = bs.bs_gather_plan(off, npb)
+    plan = np.asarray(plan_tiling(blocks, off))
     ent = off[plan[1:]] - off[plan[:-1]]
     rows = np.diff(plan)
     # never above the target unless the block is one long row
@@ -220,13 +240,63 @@ def test_gather_plan(bs, npb):
     inner = plan[1:-1]
     assert np.all((inner % 16 == 0) | (inner // 16 * 16 <= plan[:-2]))
     assert list(plan) == plan_rule(off, npb)
+    # launch order: runs of 8 blocks per XCD
+    assert list(blocks[:, 0]) == [plan[b] for b in runs_slots(len(plan) - 1)]
 
 
 def test_gather_plan_caps_rows(bs):
     # empty rows (fully masked nodes) still count against the row cap
     off = np.zeros(3001, dtype=np.int32)
     plan = bs.bs_gather_plan(off, 1024)
-    assert plan.tolist() == [[0, 0], [1024, 0], [2048, 0], [3000, 0]]
+    assert plan.tolist() == [[0, 1024, 0, 0], [1024, 2048, 0, 0], [2048, 3000, 0, 0]]
+
+
+def test_xcd_interleave(bs):
+    """Region x takes the slots s with (s // chunk) % 8 == x and holds the
+    next consecutive run of the given order there, in order."""
+    for E, chunk in [(0, 4), (1, 1), (7, 1), (100, 3), (513, 64), (31944, 64), (1000, 200)]:
+        perm = bs.bs_mesh_xcd_interleave(E, chunk)
+        assert sorted(perm.tolist()) == list(range(E))
+        slots = np.arange(E)
+        expect_next = 0
+        for x in range(8):
+            got = perm[(slots // chunk) % 8 == x]
+            assert np.array_equal(got, np.arange(expect_next, expect_next + got.size))
+            expect_next += got.size
+    with pytest.raises(bs.BSError):
+        bs.bs_mesh_xcd_interleave(10, 0)
+
+
+@pytest.mark.parametrize("chunk", [1, 4, 64])
+def test_gather_plan_by_region(bs, chunk):
+    """With the local layout interleaved by region, XCD x (the slots s with
+    s % 8 == x) takes the blocks of region x in row order, and only as many
+    slots go elsewhere as the regions' block counts differ."""
+    ev, nv, _ = bs_inputs.hex_tet_split(4, 4, 4)
+    ev, _ = bs_inputs.hex_orient(ev, 77)
+    N = 3
+    ev = np.ascontiguousarray(ev[bs.bs_mesh_xcd_interleave(len(ev), chunk)])
+    l2g, ng = bs.bs_mesh_hex_l2g(ev, N, nv)
+    off, ids = bs.bs_index_g2l(l2g, ng)
+    region = chunk * (N + 1) ** 3
+    for npb in (64, 1024):
+        blocks = bs.bs_gather_plan(off, npb, ids, region)
+        starts = plan_tiling(blocks, off)
+        assert starts == plan_rule(off, npb)
+        bs.bs_validate_plan(blocks, off)
+        nb = len(blocks)
+        reg = (ids[blocks[:, 2]] // region) % 8
+        counts = np.bincount(reg, minlength=8)
+        on_own = reg == np.arange(nb) % 8
+        # every region's blocks go to its own XCD until that XCD's slots or
+        # the region's blocks run out
+        slots = np.bincount(np.arange(nb) % 8, minlength=8)
+        assert on_own.sum() >= sum(min(int(c), int(t)) for c, t in zip(counts, slots)) - 8
+        for x in range(8):
+            mine = blocks[(np.arange(nb) % 8 == x) & on_own, 0]
+            assert np.all(np.diff(mine) > 0)
+    with pytest.raises(ValueError):
+        bs.bs_gather_plan(off, 1024, None, region)
 
 
 @pytest.mark.parametrize("p", [1, 2, 3, 4, 5, 7, 10, 15])
@@ -252,7 +322,7 @@ def test_gather_plan_long_rows(bs):
     # one node with 10 entries, the rest single
     off = np.array([0, 1, 11, 12, 13], dtype=np.int32)
     plan = bs.bs_gather_plan(off, 4)
-    assert plan.tolist() == [[0, 0], [1, 1], [2, 11], [4, 13]]
+    assert plan.tolist() == [[0, 1, 0, 1], [1, 2, 1, 11], [2, 4, 11, 13]]
     with pytest.raises(bs.BSError):
         bs.bs_gather_plan(off, 0)
     with pytest.raises(bs.BSError):
@@ -363,17 +433,15 @@ def test_g2l_property(bs, orc, n_local, n_global, seed, mask_mod):
 def test_gather_plan_property(bs, rows, npb):
     """blockStarts of any row-length profile: covers every row once, in
     order, each block within both caps unless it is a single row, and greedy
-    up to the 16-row rounding of every inner boundary."""
+    up to the 16-row rounding of every inner boundary; launched in runs of 8
+    per XCD."""
     off = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
-    pairs = bs.bs_gather_plan(off, npb)
-    plan = pairs[:, 0]
-    assert np.array_equal(pairs[:, 1], off[plan])
+    blocks = bs.bs_gather_plan(off, npb)
     ng = len(rows)
-    assert plan[0] == 0 and plan[-1] == ng
     if ng == 0:
-        assert pairs.tolist() == [[0, 0]]
+        assert blocks.shape == (0, 4)
         return
-    assert np.all(np.diff(plan) >= 1)
+    plan = plan_tiling(blocks, off)
     for a, b in zip(plan[:-1], plan[1:]):
         ent, nr = off[b] - off[a], b - a
         assert nr == 1 or (ent <= npb and nr <= npb)
@@ -384,7 +452,8 @@ def test_gather_plan_property(bs, rows, npb):
             while g < ng and g - a < npb and off[g + 1] - off[a] <= npb:
                 g += 1
             assert (b % 16 == 0 and b <= g < b + 16) or (b == g and g // 16 * 16 <= a)
-    assert list(plan) == plan_rule(off, npb)
+    assert plan == plan_rule(off, npb)
+    assert list(blocks[:, 0]) == [plan[b] for b in runs_slots(len(plan) - 1)]
 
 
 @settings(max_examples=25, deadline=None, derandomize=True)
@@ -505,14 +574,19 @@ def test_validate_plan(bs):
     for npb in (1, 5, 300, 1024):
         bs.bs_validate_plan(bs.bs_gather_plan(off, npb), off)
     plan = bs.bs_gather_plan(off, 64)
+    # any launch order is a plan
+    bs.bs_validate_plan(plan[::-1].copy(), off)
     bad = [plan.copy() for _ in range(7)]
-    bad[0][0, 0] = 1                              # first row not 0
-    bad[1][-1, 0] = ng - 1                        # last row not n_global
-    bad[2][3, 0] = bad[2][2, 0]                   # rows not increasing
-    bad[3][2, 0], bad[3][3, 0] = bad[3][3, 0], bad[3][2, 0]
-    bad[4][2, 1] += 1                             # an entry that is not off[row]
-    bad[5][0, 1] = -1
-    bad[6][-1, 1] -= 1
+    bad[0][0, 1] = bad[0][0, 0]                   # an empty block
+    bad[1][0, 2] += 1                             # an entry that is not off[row]
+    bad[2][-1, 3] -= 1
+    r = plan[:, 0].argsort()
+    bad[3][r[1], 0] -= 1                          # two blocks overlap
+    bad[3][r[1], 2] = off[bad[3][r[1], 0]]
+    bad[4][r[1], 0] += 1                          # a gap between two blocks
+    bad[4][r[1], 2] = off[bad[4][r[1], 0]]
+    bad[5][1] = bad[5][0]                         # one block twice, another missing
+    bad[6][r[-1], 1] = ng + 1                     # past the end
     for p in bad:
         with pytest.raises(bs.BSError):
             bs.bs_validate_plan(p, off)
@@ -522,11 +596,12 @@ def test_validate_plan(bs):
         bs.bs_validate_plan(plan, off2)
     with pytest.raises(ValueError):  # row starts alone are not a plan
         bs.bs_validate_plan(plan[:, 0].copy(), off)
-    bs.bs_validate_plan(np.zeros((1, 2), dtype=np.int32), np.zeros(1, dtype=np.int32))
+    bs.bs_validate_plan(np.zeros((0, 4), dtype=np.int32), np.zeros(1, dtype=np.int32))
     L = bs._lib()
     assert L.bs_validate_plan(2 ** 31 - 1, off.ctypes.data, plan.ctypes.data, 1) == bs.BS_ERANGE
     assert L.bs_validate_plan(ng, off.ctypes.data, None, 1) == bs.BS_EINVAL
     assert L.bs_validate_plan(ng, None, plan.ctypes.data, 1) == bs.BS_EINVAL
+    assert L.bs_validate_plan(ng, off.ctypes.data, plan.ctypes.data, ng + 1) == bs.BS_EINVAL
 
 
 # --------------------------------------------- element order along a curve --

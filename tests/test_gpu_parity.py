@@ -385,7 +385,8 @@ def test_gather_plan_over_capacity_blocks(env):
               np.array([0, 700, 2100, 2101, ng], dtype=np.int32),
               np.arange(0, ng + 1, dtype=np.int32)]
     for rows in starts:
-        plan = np.stack([rows, off[rows]], axis=1).astype(np.int32)  # (row, first entry) pairs
+        # blocks (first row, end row, first entry, end entry) in row order
+        plan = np.stack([rows[:-1], rows[1:], off[rows[:-1]], off[rows[1:]]], axis=1).astype(np.int32)
         bs.bs_validate_plan(plan, off)
         vg = torch.full((ng,), np.nan, dtype=torch.float64, device=d)
         bs.bs_gather(dev(torch, d, off), dev(torch, d, ids), dev(torch, d, vlv), vg, dev(torch, d, plan))
@@ -691,7 +692,7 @@ def unstructured_case(env, kind):
     """A mesh with arbitrary element orientation: the library builds the
     tables it runs on, the oracle builds its own from the same corners."""
     bs, orc, torch, d = env
-    if kind in ("tet_split", "tet_split_curve"):
+    if kind.startswith("tet_split"):
         ev, nv, coords = bs_inputs.hex_tet_split(6, 5, 6)  # 4320 hexahedra, not a lattice
         N = 5
     else:
@@ -702,7 +703,10 @@ def unstructured_case(env, kind):
         # stored along the library's Hilbert curve; both builders get the same corners
         ev = np.ascontiguousarray(ev[bs.bs_mesh_hex_order(coords[ev])])
     ev, nv = bs_inputs.hex_relabel(ev, nv, 702, spare=5)
-    if kind != "tet_split_curve":
+    if kind == "tet_split_xcd":
+        # eight regions of the generator's order interleaved in runs of 16 elements
+        ev = np.ascontiguousarray(ev[bs.bs_mesh_xcd_interleave(len(ev), 16)])
+    elif kind != "tet_split_curve":
         ev = ev[bs_inputs.permutation(703, len(ev))]
     l2g, ng = bs.bs_mesh_hex_l2g(ev, N, nv)
     off, ids = bs.bs_index_g2l(l2g, ng)
@@ -711,7 +715,7 @@ def unstructured_case(env, kind):
     return l2g, off, ids, ol2g, ng
 
 
-@pytest.mark.parametrize("kind", ["tet_split", "tet_split_curve", "torus"])
+@pytest.mark.parametrize("kind", ["tet_split", "tet_split_curve", "tet_split_xcd", "torus"])
 def test_unstructured_scatter_gather(env, kind):
     bs, orc, torch, d = env
     l2g, off, ids, ol2g, ng = unstructured_case(env, kind)
@@ -723,7 +727,10 @@ def test_unstructured_scatter_gather(env, kind):
     assert_bits(host(vl), orc.scatter(ol2g, vgv), f"scatter {kind}")
     want = orc.gather(ol2g, vlv, ng)
     doff, dids, dvl = dev(torch, d, off), dev(torch, d, ids), dev(torch, d, vlv)
-    for plan in (None, bs.bs_gather_plan(off, 1024), bs.bs_gather_plan(off, 300)):
+    plans = [None, bs.bs_gather_plan(off, 1024), bs.bs_gather_plan(off, 300)]
+    if kind == "tet_split_xcd":  # blocks placed on the XCDs by region
+        plans += [bs.bs_gather_plan(off, 1024, ids, 16 * 6 ** 3), bs.bs_gather_plan(off, 300, ids, 16 * 6 ** 3)]
+    for plan in plans:
         dplan = None if plan is None else dev(torch, d, plan)
         vg = torch.full((ng,), np.nan, dtype=torch.float64, device=d)
         bs.bs_gather(doff, dids, dvl, vg, dplan)
@@ -755,20 +762,27 @@ def test_unstructured_cg_solve(env):
     check_cg(h, ohist, host(x), ox, m, b, iters, "tet-split")
 
 
-@pytest.mark.parametrize("curve", [False, True])
-def test_unstructured_cg_solve_handoff(env, curve):
+@pytest.mark.parametrize("order", ["gen", "curve", "xcd"])
+def test_unstructured_cg_solve_handoff(env, order):
     """The device CG on the benchmark's tet-split mesh (11^3 cubes, 31944
     randomly oriented hexahedra, order 7: 11.1M global nodes). Its vectors and
     tables exceed the 256 MB last-level cache while r and p (177 MB) fit, so
     the update hands them to the direction update through the cache. Library
     and oracle build their own tables from the same corners; the residual
-    history follows the oracle's CG and x reaches b / m."""
+    history follows the oracle's CG and x reaches b / m. Elements in the
+    generator's order, along the Hilbert curve, or interleaved by region for
+    the XCDs with the gather plan placed by region (the benchmark's element
+    orders)."""
     bs, orc, torch, d = env
     ev, nv, coords = bs_inputs.hex_tet_split(11, 11, 11)
     ev, _ = bs_inputs.hex_orient(ev, 731)
-    if curve:  # the element order the benchmark's tet-split workload uses
-        ev = np.ascontiguousarray(ev[bs.bs_mesh_hex_order(coords[ev])])
     N = 7
+    region = 0
+    if order == "curve":
+        ev = np.ascontiguousarray(ev[bs.bs_mesh_hex_order(coords[ev])])
+    elif order == "xcd":
+        ev = np.ascontiguousarray(ev[bs.bs_mesh_xcd_interleave(len(ev), 64)])
+        region = 64 * (N + 1) ** 3
     l2g, ng = bs.bs_mesh_hex_l2g(ev, N, nv)
     ol2g, ong = orc.mesh_hex(ev, N, nv)
     assert ong == ng and 16 * ng <= 210 << 20
@@ -778,13 +792,13 @@ def test_unstructured_cg_solve_handoff(env, curve):
     b = bs_inputs.uniform_pm1(732, ng)
     ox, _, ohist = orc.cg_sequence(ol2g, ng, b, iters)
     t = {k: dev(torch, d, v) for k, v in (("l2g", l2g), ("off", off), ("ids", ids),
-                                           ("plan", bs.bs_gather_plan(off, 1024)))}
+                                           ("plan", bs.bs_gather_plan(off, 1024, ids, region)))}
     x = torch.zeros(ng, dtype=torch.float64, device=d)
     r, p = dev(torch, d, b), dev(torch, d, b)
     q = torch.empty(ng, dtype=torch.float64, device=d)
     pl = torch.empty(l2g.size, dtype=torch.float64, device=d)
     h = host(bs.bs_cg_solve(t["l2g"], t["off"], t["ids"], x, r, p, q, pl, iters, 0.0, t["plan"]))
-    check_cg(h, ohist, host(x), ox, m, b, iters, f"tet-split 11^3 curve={curve}")
+    check_cg(h, ohist, host(x), ox, m, b, iters, f"tet-split 11^3 order={order}")
     # scatter and gather on the same tables, as the benchmark launches them
     vgv = bs_inputs.uniform_pm1(733, ng)
     vl = torch.empty(l2g.size, dtype=torch.float64, device=d)
@@ -877,7 +891,7 @@ def test_bench_loop_scatter_gather(env):
     for p in (None, dev(torch, d, plan)):
         vg = torch.full((ng,), np.nan, dtype=torch.float64, device=d)
         bs.bs_bench_loop("gather", ng, [(dev(torch, d, off), dev(torch, d, ids), dev(torch, d, vlv), vg, p)], 2,
-                         n_blocks=0 if p is None else plan.shape[0] - 1)
+                         n_blocks=0 if p is None else plan.shape[0])
         assert_bits(host(vg), want, "gather via loop")
 
 

@@ -36,7 +36,7 @@ def mesh(bs, torch, d, dims, N, seed, npb=1024):
 
     def t(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(d)
-    return {"l2g": t(l2g), "off": t(off), "ids": t(ids), "plan": t(plan), "nb": plan.shape[0] - 1,
+    return {"l2g": t(l2g), "off": t(off), "ids": t(ids), "plan": t(plan), "nb": plan.shape[0],
             "b": t(bs_inputs.uniform_pm1(seed, ng)), "ng": ng, "nl": l2g.size}
 
 
