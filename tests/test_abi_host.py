@@ -456,6 +456,44 @@ def test_gather_plan_property(bs, rows, npb):
     assert list(blocks[:, 0]) == [plan[b] for b in runs_slots(len(plan) - 1)]
 
 
+def region_slots(off, ids, starts, region):
+    """Launch order of plan blocks placed by region, as the rule states it:
+    a block's region is that of its first entry's local index (an empty
+    block's, its own index mod 8); slot s goes to XCD s mod 8, which takes
+    its region's next block in row order, or, once that region has run out,
+    the next block of the region with the most left (the lowest such
+    region)."""
+    nb = len(starts) - 1
+    queues = [[] for _ in range(8)]
+    for b in range(nb):
+        e0, e1 = off[starts[b]], off[starts[b + 1]]
+        x = (ids[e0] // region) % 8 if e1 > e0 else b % 8
+        queues[x].append(b)
+    out = []
+    for s in range(nb):
+        x = s % 8
+        if not queues[x]:
+            x = max(range(8), key=lambda y: (len(queues[y]), -y))
+        out.append(queues[x].pop(0))
+    return out
+
+
+@settings(max_examples=60, deadline=None, derandomize=True)
+@given(st.lists(st.integers(0, 9), min_size=1, max_size=400), st.integers(1, 1024), st.integers(1, 50),
+       st.integers(0, 2 ** 32 - 1))
+def test_gather_plan_region_property(bs, rows, npb, region, seed):
+    """Any row-length profile and any assignment of local indices to the
+    entries: the plan's rows follow the greedy rule and its launch order
+    follows the region rule exactly."""
+    off = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+    ne = int(off[-1])
+    ids = np.random.default_rng(seed).permutation(max(ne, 1))[:ne].astype(np.int32)
+    blocks = bs.bs_gather_plan(off, npb, ids, region)
+    starts = plan_tiling(blocks, off)
+    assert starts == plan_rule(off, npb)
+    assert list(blocks[:, 0]) == [starts[b] for b in region_slots(off, ids, starts, region)]
+
+
 @settings(max_examples=25, deadline=None, derandomize=True)
 @given(st.integers(1, 4), st.integers(1, 4), st.integers(1, 3), st.integers(1, 6), st.integers(0, 2 ** 32 - 1),
        st.booleans())
