@@ -514,21 +514,23 @@ __global__ __launch_bounds__(kBlock) void k_axpy(int64_t n2, const double *x, do
     axpy_body<U, kStream>(split_ht(n2, ht), Coef{a, nullptr}, x, Coef{b, nullptr}, y, nullptr, nblk);
 }
 
-// The same with its coefficients read from device memory, for the direction
-// update p = r + beta p of the CG iteration (streaming policy).
+// The direction update p = (1 r) + (beta p) of the CG iteration, beta read
+// from device memory (streaming policy). Like the standalone kernels, the
+// CG iteration's kernels take plain arguments that the preload holds (1-3%
+// per iteration at 12^3-32^3 order 7 against aggregate arguments).
 template <int U>
-__global__ __launch_bounds__(kBlock) void k_axpy_dev(Split sp, Coef ca, const double *x, Coef cb, double *y,
-                                                     const double *cgs)
+__global__ __launch_bounds__(kBlock) void k_axpy_dev(int64_t n2, const double *x, double *y, const double *cgs,
+                                                     unsigned ht, unsigned nblk)
 {
-    axpy_body<U, kStream>(sp, ca, x, cb, y, cgs, gridDim.x);
+    axpy_body<U, kStream>(split_ht(n2, ht), Coef{1.0, nullptr}, x, Coef{0.0, cgs + kBeta}, y, cgs, nblk);
 }
 
-// The same with the cache-keeping policy, for the CG iteration.
+// The same with the cache-keeping policy.
 template <int U>
-__global__ __launch_bounds__(kBlock) void k_axpy_keep(Split sp, Coef ca, const double *x, Coef cb, double *y,
-                                                      const double *cgs)
+__global__ __launch_bounds__(kBlock) void k_axpy_keep(int64_t n2, const double *x, double *y, const double *cgs,
+                                                      unsigned ht, unsigned nblk)
 {
-    axpy_body<U, kKeep>(sp, ca, x, cb, y, cgs, gridDim.x);
+    axpy_body<U, kKeep>(split_ht(n2, ht), Coef{1.0, nullptr}, x, Coef{0.0, cgs + kBeta}, y, cgs, nblk);
 }
 
 // ------------------------------------------- pointwise scale y = x / d ----
@@ -752,7 +754,8 @@ __device__ __forceinline__ void cg_update_two_pass(Split sp, Coef ca, const doub
 template <int U, int P, int PP = P, int PR = P>
 __device__ __forceinline__ void cg_update_one_pass(Split sp, Coef ca, const double *__restrict__ p,
                                                    const double *__restrict__ q, double *__restrict__ x,
-                                                   double *__restrict__ r, const Fin &f, const double *cgs)
+                                                   double *__restrict__ r, const Fin &f, const double *cgs,
+                                                   unsigned nblk)
 {
     if (skipped(cgs)) return;
     const double a = ca.get();
@@ -760,7 +763,7 @@ __device__ __forceinline__ void cg_update_one_pass(Split sp, Coef ca, const doub
     const d2 *qv = reinterpret_cast<const d2 *>(q + sp.head);
     d2 *xv = reinterpret_cast<d2 *>(x + sp.head);
     d2 *rv = reinterpret_cast<d2 *>(r + sp.head);
-    const int64_t stride = (int64_t)gridDim.x * kBlock * U;
+    const int64_t stride = (int64_t)nblk * kBlock * U;
     int64_t i = (int64_t)blockIdx.x * kBlock * U + threadIdx.x;
     double acc0 = 0.0, acc1 = 0.0;
     for (; i + (U - 1) * kBlock < sp.n2; i += stride) {
@@ -792,7 +795,7 @@ __device__ __forceinline__ void cg_update_one_pass(Split sp, Coef ca, const doub
             acc1 = __builtin_fma(nr.y, nr.y, acc1);
         }
     }
-    cg_update_finish(sp, a, p, q, x, r, acc0, acc1, f, gridDim.x);
+    cg_update_finish(sp, a, p, q, x, r, acc0, acc1, f, nblk);
 }
 
 template <int U1, int U2, int NT>
@@ -806,22 +809,23 @@ __global__ __launch_bounds__(NT) void k_cg_update(int64_t n2, const double *__re
 
 // The same with the cache-keeping policy, for the CG iteration.
 template <int U1, int U2, int NT>
-__global__ __launch_bounds__(NT) void k_cg_update_keep(Split sp, Coef ca, const double *__restrict__ p,
+__global__ __launch_bounds__(NT) void k_cg_update_keep(int64_t n2, const double *__restrict__ p,
                                                        const double *__restrict__ q, double *__restrict__ x,
-                                                       double *__restrict__ r, Fin f, const double *cgs)
+                                                       double *__restrict__ r, const double *cgs, unsigned ht,
+                                                       unsigned nblk, Fin f)
 {
-    cg_update_two_pass<U1, U2, NT, kKeep>(sp, ca, p, q, x, r, f, cgs, gridDim.x);
+    cg_update_two_pass<U1, U2, NT, kKeep>(split_ht(n2, ht), Coef{0.0, cgs + kAlpha}, p, q, x, r, f, cgs, nblk);
 }
 
 // One pass, non-temporal: the CG iteration's update when its vectors do not
 // fit in the last-level cache.
 template <int U>
-__global__ __launch_bounds__(kBlock) void k_cg_update_one_pass(Split sp, Coef ca, const double *__restrict__ p,
+__global__ __launch_bounds__(kBlock) void k_cg_update_one_pass(int64_t n2, const double *__restrict__ p,
                                                                const double *__restrict__ q,
                                                                double *__restrict__ x, double *__restrict__ r,
-                                                               Fin f, const double *cgs)
+                                                               const double *cgs, unsigned ht, unsigned nblk, Fin f)
 {
-    cg_update_one_pass<U, kStream>(sp, ca, p, q, x, r, f, cgs);
+    cg_update_one_pass<U, kStream>(split_ht(n2, ht), Coef{0.0, cgs + kAlpha}, p, q, x, r, f, cgs, nblk);
 }
 
 // The same, for a CG iteration whose vectors do not fit in the last-level
@@ -829,12 +833,12 @@ __global__ __launch_bounds__(kBlock) void k_cg_update_one_pass(Split sp, Coef ca
 // policy, so the direction update p = r + beta p that follows finds both
 // there.
 template <int U>
-__global__ __launch_bounds__(kBlock) void k_cg_update_handoff(Split sp, Coef ca, const double *__restrict__ p,
-                                                              const double *__restrict__ q,
-                                                              double *__restrict__ x, double *__restrict__ r,
-                                                              Fin f, const double *cgs)
+__global__ __launch_bounds__(kBlock) void k_cg_update_handoff(int64_t n2, const double *__restrict__ p,
+                                                               const double *__restrict__ q,
+                                                               double *__restrict__ x, double *__restrict__ r,
+                                                               const double *cgs, unsigned ht, unsigned nblk, Fin f)
 {
-    cg_update_one_pass<U, kStream, kKeep, kKeep>(sp, ca, p, q, x, r, f, cgs);
+    cg_update_one_pass<U, kStream, kKeep, kKeep>(split_ht(n2, ht), Coef{0.0, cgs + kAlpha}, p, q, x, r, f, cgs, nblk);
 }
 
 // --------------------------------------------------------- BS7 scatter ----
@@ -1695,21 +1699,21 @@ int cg_solve_run(bs_ctx *c, int64_t n_global, int64_t n_local, const int32_t *l2
         // which overlaps the cached part of p (left by the scatter) with HBM.
         if (keep)
             launch(c, k_cg_update_keep<kCgShape.unroll, kCgRUnroll, kCgShape.threads>, dim3(cg_nb),
-                   dim3(kCgShape.threads), 0, st, sp,
-                   Coef{0.0, cgs + kAlpha}, p, q, x, r, fin_cg(c, kSetBeta, rr_hist, k, iters, 0.0), cgs);
+                   dim3(kCgShape.threads), 0, st, sp.n2, p, q, x, r, cgs, ht_of(sp), cg_nb,
+                   fin_cg(c, kSetBeta, rr_hist, k, iters, 0.0));
         else if (handoff)
-            launch(c, k_cg_update_handoff<kCgOnePassShape.unroll>, dim3(cg1_nb), dim3(kBlock), 0, st, sp,
-                   Coef{0.0, cgs + kAlpha}, p, q, x, r, fin_cg(c, kSetBeta, rr_hist, k, iters, 0.0), cgs);
+            launch(c, k_cg_update_handoff<kCgOnePassShape.unroll>, dim3(cg1_nb), dim3(kBlock), 0, st, sp.n2, p, q,
+                   x, r, cgs, ht_of(sp), cg1_nb, fin_cg(c, kSetBeta, rr_hist, k, iters, 0.0));
         else
-            launch(c, k_cg_update_one_pass<kCgOnePassShape.unroll>, dim3(cg1_nb), dim3(kBlock), 0, st, sp,
-                   Coef{0.0, cgs + kAlpha}, p, q, x, r, fin_cg(c, kSetBeta, rr_hist, k, iters, 0.0), cgs);
+            launch(c, k_cg_update_one_pass<kCgOnePassShape.unroll>, dim3(cg1_nb), dim3(kBlock), 0, st, sp.n2, p,
+                   q, x, r, cgs, ht_of(sp), cg1_nb, fin_cg(c, kSetBeta, rr_hist, k, iters, 0.0));
         // p = (1 r) + (beta p)
         if (keep || handoff)
-            launch(c, k_axpy_keep<kAxpyShape.unroll>, dim3(ax_nb), dim3(kBlock), 0, st, sp, Coef{1.0, nullptr}, r,
-                   Coef{0.0, cgs + kBeta}, p, cgs);
+            launch(c, k_axpy_keep<kAxpyShape.unroll>, dim3(ax_nb), dim3(kBlock), 0, st, sp.n2, r, p, cgs, ht_of(sp),
+                   ax_nb);
         else
-            launch(c, k_axpy_dev<kAxpyShape.unroll>, dim3(ax_nb), dim3(kBlock), 0, st, sp, Coef{1.0, nullptr}, r,
-                   Coef{0.0, cgs + kBeta}, p, cgs);
+            launch(c, k_axpy_dev<kAxpyShape.unroll>, dim3(ax_nb), dim3(kBlock), 0, st, sp.n2, r, p, cgs, ht_of(sp),
+                   ax_nb);
         if (hipGetLastError() != hipSuccess) return BS_EHIP;
     }
     return BS_OK;
