@@ -49,3 +49,21 @@ def test_cg_solve_rejects_a_short_history_before_any_launch(monkeypatch):
     with pytest.raises(ValueError, match="inconsistent"):
         bs.bs_cg_solve(*_cg_args(ng=5)[0][:3], *[torch.zeros(6, dtype=torch.float64)] * 4,
                        torch.zeros(8, dtype=torch.float64), 3)
+
+
+def test_a_plan_of_the_wrong_shape_is_rejected_before_any_launch(monkeypatch):
+    """A gather plan is (n_blocks, 4) int32 blocks; row starts alone, or pairs,
+    would make the kernel read past the array, so the binding refuses them
+    before it reaches the library."""
+    def no_lib():
+        raise AssertionError("the library was reached")
+    monkeypatch.setattr(bs, "_lib", no_lib)
+    for bad in (torch.zeros(5, dtype=torch.int32), torch.zeros((5, 2), dtype=torch.int32),
+                torch.zeros((0, 4), dtype=torch.int32)):
+        with pytest.raises(ValueError, match="block_starts"):
+            bs._plan_dev(bad)
+    assert bs._plan_dev(None) == (None, 0)
+    with pytest.raises(ValueError, match="block_starts"):
+        bs.bs_bench_loop("gather", 4, [(torch.zeros(5, dtype=torch.int32), torch.zeros(3, dtype=torch.int32),
+                                        torch.zeros(3, dtype=torch.float64), torch.zeros(4, dtype=torch.float64),
+                                        torch.zeros((2, 2), dtype=torch.int32))], 1, n_blocks=2)
