@@ -391,7 +391,7 @@ int bs_gather_plan(int64_t n_global, const int32_t *off, const int32_t *ids, int
  * (N+1)^3; the regions should be spatially compact, so the given order should
  * be a local one (a generator's sweep, or bs_mesh_hex_order). Measured on a
  * tet-split mesh of 11^3 cubes at order 7 with runs of 64: gather counter
- * traffic 1.20x -> 1.08x the algorithmic bytes, 60.6 -> 60.3 us.
+ * traffic 1.20x -> 1.08x the algorithmic bytes, 60.8 -> 60.5 us.
  * BS_EINVAL for chunk < 1, BS_ERANGE for n_elements > INT32_MAX. */
 int bs_mesh_xcd_interleave(int64_t n_elements, int64_t chunk, int32_t *perm);
 
