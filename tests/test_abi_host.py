@@ -478,6 +478,22 @@ def region_slots(off, ids, starts, region):
     return out
 
 
+@settings(max_examples=80, deadline=None, derandomize=True)
+@given(st.integers(0, 5000), st.integers(1, 700))
+def test_xcd_interleave_property(bs, E, chunk):
+    """Any element count and run length: a permutation in which slot s holds
+    region (s // chunk) % 8, each region being the next consecutive run of
+    the given order, kept in order."""
+    perm = bs.bs_mesh_xcd_interleave(E, chunk)
+    assert perm.size == E and np.array_equal(np.sort(perm), np.arange(E))
+    region = (np.arange(E) // chunk) % 8
+    nxt = 0
+    for x in range(8):
+        got = perm[region == x]
+        assert np.array_equal(got, np.arange(nxt, nxt + got.size))
+        nxt += got.size
+
+
 @settings(max_examples=60, deadline=None, derandomize=True)
 @given(st.lists(st.integers(0, 9), min_size=1, max_size=400), st.integers(1, 1024), st.integers(1, 50),
        st.integers(0, 2 ** 32 - 1))
