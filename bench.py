@@ -61,6 +61,7 @@ KERNEL_NAME = {  # op -> its kernels as rocprofv3 names them (namespace and argu
 GATHER_NPB = 1024
 PER_OP_FIELDS = ["bytes", "us", "us_best", "GBps", "pct_peak", "pct_copy_ceiling", "hot_us"]
 EVENT_STRIDE = 4  # default: timed steps per step whose dominant kernel records events
+MIN_TIMED_LAUNCHES = 10  # a short run times the dominant kernel more often, down to every step
 
 
 def op_bytes(op, n=0, nl=0, ng=0):
@@ -649,8 +650,9 @@ def main():
     ap.add_argument("--event-fence", choices=["none", "system"], default="none",
                     help="timing events of the dominant kernel: none = created with hipEventDisableSystemFence, "
                          "system = torch's events (a system-scope fence each)")
-    ap.add_argument("--event-stride", type=int, default=EVENT_STRIDE,
-                    help="the dominant kernel records its timing events in every this many timed steps")
+    ap.add_argument("--event-stride", type=int, default=None,
+                    help="the dominant kernel records its timing events in every this many timed steps "
+                         f"(default {EVENT_STRIDE}, less when that would time fewer than {MIN_TIMED_LAUNCHES} launches)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the size sweep and the other workloads (profiling runs of the step)")
     ap.add_argument("--sweep-layout", choices=["arena", "torch"], default="arena",
@@ -703,13 +705,16 @@ def main():
     # (the library launches it with them, as armed by time_next), on its
     # stream. The events are fence-free (TimingEvents); even so a timed
     # launch costs its step about 1 us (events in every step: 319.9 against
-    # 319.2 us per step), so by default every fourth step carries them.
+    # 319.2 us per step), so by default every fourth step carries them; a
+    # run of fewer than 40 steps times more of its steps (20 steps: every
+    # second one), since an average of five launches moves by a few percent
+    # from run to run.
     step_launch = [m.launchers(bs, stream) for m in sets]
     for w in range(args.warmup):
         for op in OPS:
             step_launch[w % len(sets)][op]()
     cur = torch.cuda.current_stream()
-    stride = args.event_stride
+    stride = args.event_stride or max(1, min(EVENT_STRIDE, args.steps // MIN_TIMED_LAUNCHES))
     ev = TimingEvents(torch, (args.steps + stride - 1) // stride, args.event_fence)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
