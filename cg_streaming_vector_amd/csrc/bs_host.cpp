@@ -592,6 +592,12 @@ int bs_gather_plan(int64_t n_global, const int32_t *off, const int32_t *ids, int
     if (region_entries > 0 && n_global > 0 && !ids) return BS_EINVAL;
     if (nodes_per_block < 1 || nodes_per_block > 1024) return BS_EINVAL;
     if (n_global >= INT32_MAX) return BS_ERANGE;
+    // The offsets must be those of a CSR (non-decreasing from a non-negative
+    // first entry): the blocks copy them, and region placement reads ids at
+    // them.
+    if (n_global > 0 && off[0] < 0) return BS_EINVAL;
+    for (int64_t g = 0; g < n_global; ++g)
+        if (off[g + 1] < off[g]) return BS_EINVAL;
     // Blocks in row order, greedily: extend the block row by row while it
     // holds at most nodes_per_block rows and nodes_per_block entries; a row
     // longer than that gets a block of its own. Then, unless it is the last
@@ -640,6 +646,7 @@ int bs_gather_plan(int64_t n_global, const int32_t *off, const int32_t *ids, int
             std::vector<std::vector<int64_t>> queue(kXcds);
             for (int64_t b = 0; b < nb; ++b) {
                 const int32_t e0 = off[start[(size_t)b]], e1 = off[start[(size_t)b + 1]];
+                if (e1 > e0 && ids[e0] < 0) return BS_EINVAL;  // not a local index
                 const int64_t x = e1 > e0 ? ((int64_t)ids[e0] / region_entries) % kXcds : b % kXcds;
                 queue[(size_t)x].push_back(b);
             }
@@ -679,6 +686,9 @@ int bs_mesh_xcd_interleave(int64_t n_elements, int64_t chunk, int32_t *perm)
 {
     if (n_elements < 0 || chunk < 1 || (n_elements > 0 && !perm)) return BS_EINVAL;
     if (n_elements > INT32_MAX) return BS_ERANGE;
+    // A run as long as the mesh puts every element in region 0 (the identity),
+    // as any longer one does; the clamp keeps 8 * chunk from overflowing.
+    chunk = std::min(chunk, std::max(n_elements, (int64_t)1));
     // Region x owns the storage slots s with (s / chunk) mod 8 == x and takes
     // the next count[x] elements of the given order, keeping their order.
     const int64_t round = kXcds * chunk, full = n_elements / round, rest = n_elements % round;

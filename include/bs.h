@@ -375,8 +375,10 @@ int bs_index_g2l(int64_t n_local, int64_t n_global, const int32_t *l2g, int32_t 
  * of region x in row order (an XCD whose region has run out takes from the
  * region with the most left). ids is then the CSR ids of off.
  * nodes_per_block must be in [1, 1024] (BS_EINVAL): the gather kernel stages
- * up to 1024 entries per block in LDS. BS_ENOMEM without host memory for the
- * row starts. */
+ * up to 1024 entries per block in LDS. off must be non-decreasing from a
+ * non-negative off[0], and in region placement a block's first id must be
+ * non-negative (BS_EINVAL otherwise; ids must hold off[n_global] entries).
+ * BS_ENOMEM without host memory for the row starts. */
 int bs_gather_plan(int64_t n_global, const int32_t *off, const int32_t *ids, int nodes_per_block,
                    int64_t region_entries, int32_t *plan, int64_t *n_blocks);
 
@@ -392,7 +394,8 @@ int bs_gather_plan(int64_t n_global, const int32_t *off, const int32_t *ids, int
  * be a local one (a generator's sweep, or bs_mesh_hex_order). Measured on a
  * tet-split mesh of 11^3 cubes at order 7 with runs of 64: gather counter
  * traffic 1.20x -> 1.08x the algorithmic bytes, 60.8 -> 60.5 us.
- * BS_EINVAL for chunk < 1, BS_ERANGE for n_elements > INT32_MAX. */
+ * BS_EINVAL for chunk < 1, BS_ERANGE for n_elements > INT32_MAX; a chunk of
+ * n_elements or more gives the identity. */
 int bs_mesh_xcd_interleave(int64_t n_elements, int64_t chunk, int32_t *perm);
 
 /* ------------------------------------------------------------ measurement --

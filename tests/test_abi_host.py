@@ -265,6 +265,21 @@ def test_xcd_interleave(bs):
             expect_next += got.size
     with pytest.raises(bs.BSError):
         bs.bs_mesh_xcd_interleave(10, 0)
+    # a run as long as the mesh or longer is the identity, up to the largest chunk
+    for chunk in (100, 101, 2 ** 40, 2 ** 62, 2 ** 63 - 1):
+        assert np.array_equal(bs.bs_mesh_xcd_interleave(100, chunk), np.arange(100))
+
+
+def test_gather_plan_rejects_bad_offsets(bs):
+    """Offsets that are not a CSR's, and a negative id where region placement
+    reads one, are refused before any block is written."""
+    for off in ([0, 3, 2, 5], [-1, 0, 1], [0, 1, 0]):
+        with pytest.raises(bs.BSError):
+            bs.bs_gather_plan(np.array(off, dtype=np.int32), 16)
+    off = np.array([0, 1, 2, 3], dtype=np.int32)
+    assert bs.bs_gather_plan(off, 16, np.array([0, 1, 2], dtype=np.int32), 1).shape == (1, 4)
+    with pytest.raises(bs.BSError):
+        bs.bs_gather_plan(off, 16, np.array([-5, 1, 2], dtype=np.int32), 1)
 
 
 @pytest.mark.parametrize("chunk", [1, 4, 64])
