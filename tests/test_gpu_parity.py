@@ -940,8 +940,15 @@ def test_random_meshes(env, case):
     assert_bits(host(vl), orc.scatter(ol2g, vgv), f"scatter case {case}")
     want = orc.gather(ol2g, vlv, ng)
     doff, dids, dvl, dw = dev(torch, d, off), dev(torch, d, ids), dev(torch, d, vlv), dev(torch, d, wv)
-    for cap in (None, 1 + npb % 1024, 1024):
-        plan = None if cap is None else dev(torch, d, bs.bs_gather_plan(off, cap))
+    # plans of several capacities, and one whose blocks launch in the
+    # region order (any block order must give the same bits)
+    region = 1 + (npb >> 10) % 5000
+    plans = {None: None, 1 + npb % 1024: None, 1024: None, "region": bs.bs_gather_plan(off, 1024, ids, region)}
+    for cap in plans:
+        host_plan = plans[cap] if cap == "region" else None if cap is None else bs.bs_gather_plan(off, cap)
+        if host_plan is not None:
+            bs.bs_validate_plan(host_plan, off)
+        plan = None if host_plan is None else dev(torch, d, host_plan)
         vg = torch.full((ng,), np.nan, dtype=torch.float64, device=d)
         bs.bs_gather(doff, dids, dvl, vg, plan)
         assert_bits(host(vg), want, f"gather case {case} cap {cap}")
@@ -976,7 +983,8 @@ def test_random_unstructured(env, case):
     bs.bs_scatter(dev(torch, d, l2g), dev(torch, d, vgv), vl)
     assert_bits(host(vl), orc.scatter(ol2g, vgv), f"scatter unstructured {case}")
     want = orc.gather(ol2g, vlv, ng)
-    for plan in (None, bs.bs_gather_plan(off, 1024)):
+    region = (N + 1) ** 3 * (1 + a % 4)  # runs of 1-4 elements
+    for plan in (None, bs.bs_gather_plan(off, 1024), bs.bs_gather_plan(off, 1024, ids, region)):
         vg = torch.full((ng,), np.nan, dtype=torch.float64, device=d)
         bs.bs_gather(dev(torch, d, off), dev(torch, d, ids), dev(torch, d, vlv), vg,
                      None if plan is None else dev(torch, d, plan))
