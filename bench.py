@@ -639,7 +639,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--gather", choices=["rows", "lds"], default="lds")
+    ap.add_argument("--gather", choices=["span", "lds"], default="lds",
+                    help="lds: the gather with a blockStarts plan; span: without a plan (fixed spans of 512 rows)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-ceiling", action="store_true", help="skip the 2^28-double copy (profiling runs)")
     ap.add_argument("--rotate", type=int, default=12, help="array sets cycled in the per-op loops")

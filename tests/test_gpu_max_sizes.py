@@ -93,7 +93,7 @@ def test_scatter_gather_at_int32_max(env):
         vg = torch.full((G,), float("nan"), dtype=torch.float64, device=d)
         bs.bs_gather(off, ids, vl, vg, p)
         got = vg[torch.from_numpy(gs).to(d)].cpu().numpy()
-        assert np.array_equal(got.view(np.uint64), want.view(np.uint64)), "plan" if p is not None else "rows"
+        assert np.array_equal(got.view(np.uint64), want.view(np.uint64)), "plan" if p is not None else "no plan"
         # every node written: the sum of all of v_G equals the sum of v_L
         assert not torch.isnan(vg).any().item()
         del vg

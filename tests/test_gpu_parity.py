@@ -371,6 +371,33 @@ def test_gather_long_row_fallback(env):
         assert_bits(host(vg), want, "long rows")
 
 
+def test_gather_spans_at_and_over_capacity(env):
+    """Without a plan the rows go in spans of 512: spans of exactly 2048
+    entries are staged, spans of more take the global-memory path, and the
+    spans are launched out of row order (runs per XCD over the whole rounds,
+    the rest in order); every row gets the oracle's bits, also in the folded
+    dot."""
+    bs, orc, torch, d = env
+    span, rows = 512, 79 * 512 + 300  # 80 spans: one round of 64 remapped, 16 in order
+    length = np.empty(rows, dtype=np.int64)
+    for s in range(80):
+        length[s * span:(s + 1) * span] = [4, 5, 1, 8, 0, 3][s % 6]  # 2048, 2560, 512, 4096, 0, 1536
+    l2g = np.repeat(np.arange(rows, dtype=np.int32), length)
+    vlv = bs_inputs.uniform_pm1(86, l2g.size)
+    wv = bs_inputs.uniform_pm1(87, rows)
+    off, ids = bs.bs_index_g2l(l2g, rows)
+    assert off[span] - off[0] == 2048 and off[2 * span] - off[span] == 2560
+    want = orc.gather(l2g, vlv, rows)
+    vg = torch.full((rows,), np.nan, dtype=torch.float64, device=d)
+    doff, dids, dvl = dev(torch, d, off), dev(torch, d, ids), dev(torch, d, vlv)
+    bs.bs_gather(doff, dids, dvl, vg)
+    assert_bits(host(vg), want, "spans at and over capacity")
+    vg.fill_(np.nan)
+    got = bs.bs_gather_dot(doff, dids, dvl, vg, dev(torch, d, wv)).item()
+    assert_bits(host(vg), want, "spans at and over capacity, folded dot")
+    assert_rel(got, orc.dot(want, wv), "span gather dot")
+
+
 def test_gather_plan_over_capacity_blocks(env):
     """A hand-made plan whose blocks exceed the LDS capacity (rows or
     entries) takes the global-memory path, with the same bits."""
