@@ -942,8 +942,11 @@ __global__ __launch_bounds__(kBlock) void k_scatter_scalar(int64_t nl, const int
 // share an L2. Measured against a row-per-lane kernel (one lane per row,
 // its ids and values loaded row by row): 58.9 against 79.5 us at 32^3 N=7,
 // 207.1 against 270.9 us at 24^3 N=15, 61.8 against 96.1 us on the
-// tet-split mesh, the same bits; 2-5% behind a plan.
-template <bool kDot>
+// tet-split mesh, the same bits; 2-5% behind a plan. P is the cache policy
+// of its streams (ids, v_G): the CG iteration takes kKeep when its working set
+// fits in the last-level cache (41.6 against 42.8 us per iteration on a
+// 32 x 32 x 4-element slab at N=7 without a plan).
+template <bool kDot, int P>
 __global__ __launch_bounds__(kBlock) void k_gather_span(int64_t ng, const int32_t *__restrict__ off,
                                                         const int32_t *__restrict__ ids,
                                                         const double *__restrict__ vl,
@@ -970,7 +973,7 @@ __global__ __launch_bounds__(kBlock) void k_gather_span(int64_t ng, const int32_
 #pragma unroll
         for (int q = 0; q < K; ++q) {
             const int32_t t = threadIdx.x + q * kBlock;
-            id[q] = t < ne ? __builtin_nontemporal_load(ids + e0 + t) : -1;
+            id[q] = t < ne ? ldp<P>(ids + e0 + t) : -1;
         }
 #pragma unroll
         for (int q = 0; q < RL; ++q) {
@@ -993,7 +996,7 @@ __global__ __launch_bounds__(kBlock) void k_gather_span(int64_t ng, const int32_
             if (r < nr) {
                 double sum = 0.0;
                 for (int32_t j = oa[q] - e0; j < ob[q] - e0; ++j) sum = sum + stage[j];
-                __builtin_nontemporal_store(sum, vg + r0 + r);
+                stp<P>(vg + r0 + r, sum);
                 if (kDot) acc = __builtin_fma(sum, w[r0 + r], acc);
             }
         }
@@ -1368,11 +1371,14 @@ int gather_launch(bs_ctx *c, int64_t ng, const int32_t *off, const int32_t *ids,
                    cgs, nullptr, nullptr);
     } else {
         *nb = (unsigned)((ng + kSpanRows - 1) / kSpanRows);
-        if (w)
-            launch(c, k_gather_span<true>, dim3(*nb), dim3(kBlock), 0, st, ng, off, ids, vl, vg, cgs, w,
+        if (w && keep)
+            launch(c, k_gather_span<true, kKeep>, dim3(*nb), dim3(kBlock), 0, st, ng, off, ids, vl, vg, cgs, w,
+                   c->partials);
+        else if (w)
+            launch(c, k_gather_span<true, kStream>, dim3(*nb), dim3(kBlock), 0, st, ng, off, ids, vl, vg, cgs, w,
                    c->partials);
         else
-            launch(c, k_gather_span<false>, dim3(*nb), dim3(kBlock), 0, st, ng, off, ids, vl, vg, cgs,
+            launch(c, k_gather_span<false, kStream>, dim3(*nb), dim3(kBlock), 0, st, ng, off, ids, vl, vg, cgs,
                    nullptr, nullptr);
     }
     return launch_status();
