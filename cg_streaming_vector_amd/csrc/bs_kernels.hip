@@ -1122,26 +1122,65 @@ __global__ __launch_bounds__(kBlock) void k_gather_plan_keep(const int32_t *__re
 }
 
 // Scalar (8-byte) versions of the vector ops for operands whose 16-byte
-// phases differ.
+// phases differ. Block b's tile is kScalarUnroll * kBlock consecutive
+// elements, lane t taking t, t + kBlock, ...: every load of the tile issued
+// before any store or sum (measured at 11.4M doubles, against one element
+// per lane per step: AXPY 49.4 against 57.2 us, fused update 104.0 against
+// 116.0 us, copy and dot unchanged; the aligned kernels take 43.3 and 85.9).
+constexpr int kScalarUnroll = 4;  // elements per lane in flight in the 8-byte kernels
+
 __global__ __launch_bounds__(kBlock) void k_copy_scalar(int64_t n, const double *x, double *y)
 {
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += (int64_t)gridDim.x * kBlock)
-        y[i] = x[i];
+    constexpr int U = kScalarUnroll;
+    const int64_t stride = kBlock, step = (int64_t)gridDim.x * U * kBlock;
+    int64_t i = (int64_t)blockIdx.x * U * kBlock + threadIdx.x;
+    for (; i + (U - 1) * stride < n; i += step) {
+        double v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = x[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < U; ++u) y[i + u * stride] = v[u];
+    }
+    for (; i < n; i += stride) y[i] = x[i];
 }
 
 __global__ __launch_bounds__(kBlock) void k_axpy_scalar(int64_t n, double a, const double *x,
                                                         double b, double *y)
 {
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += (int64_t)gridDim.x * kBlock)
-        y[i] = a * x[i] + b * y[i];
+    constexpr int U = kScalarUnroll;
+    const int64_t stride = kBlock, step = (int64_t)gridDim.x * U * kBlock;
+    int64_t i = (int64_t)blockIdx.x * U * kBlock + threadIdx.x;
+    for (; i + (U - 1) * stride < n; i += step) {
+        double vx[U], vy[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            vx[u] = x[i + u * stride];
+            vy[u] = y[i + u * stride];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) y[i + u * stride] = a * vx[u] + b * vy[u];
+    }
+    for (; i < n; i += stride) y[i] = a * x[i] + b * y[i];
 }
 
 __global__ __launch_bounds__(kBlock) void k_dot_scalar(int64_t n, const double *x, const double *y,
                                                        double *partials)
 {
+    constexpr int U = kScalarUnroll;
+    const int64_t stride = kBlock, step = (int64_t)gridDim.x * U * kBlock;
+    int64_t i = (int64_t)blockIdx.x * U * kBlock + threadIdx.x;
     double acc = 0.0;
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += (int64_t)gridDim.x * kBlock)
-        acc = __builtin_fma(x[i], y[i], acc);
+    for (; i + (U - 1) * stride < n; i += step) {
+        double vx[U], vy[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            vx[u] = x[i + u * stride];
+            vy[u] = y[i + u * stride];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc = __builtin_fma(vx[u], vy[u], acc);
+    }
+    for (; i < n; i += stride) acc = __builtin_fma(x[i], y[i], acc);
     const double part = block_sum(acc);
     if (threadIdx.x == 0) partials[blockIdx.x] = part;
 }
@@ -1150,8 +1189,28 @@ __global__ __launch_bounds__(kBlock) void k_cg_update_scalar(int64_t n, double a
                                                              const double *q, double *x, double *r,
                                                              double *partials)
 {
+    constexpr int U = kScalarUnroll;
+    const int64_t stride = kBlock, step = (int64_t)gridDim.x * U * kBlock;
+    int64_t i = (int64_t)blockIdx.x * U * kBlock + threadIdx.x;
     double acc = 0.0;
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += (int64_t)gridDim.x * kBlock) {
+    for (; i + (U - 1) * stride < n; i += step) {
+        double vp[U], vq[U], vx[U], vr[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            vp[u] = p[i + u * stride];
+            vq[u] = q[i + u * stride];
+            vx[u] = x[i + u * stride];
+            vr[u] = r[i + u * stride];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            x[i + u * stride] = vx[u] + a * vp[u];
+            const double nr = vr[u] - a * vq[u];
+            r[i + u * stride] = nr;
+            acc = __builtin_fma(nr, nr, acc);
+        }
+    }
+    for (; i < n; i += stride) {
         x[i] = x[i] + a * p[i];
         const double nr = r[i] - a * q[i];
         r[i] = nr;
@@ -1218,10 +1277,14 @@ inline unsigned vector_grid(const bs_ctx *c, int64_t n2, VecShape s, bool reduct
     return (unsigned)g;
 }
 
-inline unsigned scalar_grid(const bs_ctx *c, int64_t n)
+// Grid of an 8-byte kernel: one tile per block, at most 2^22 blocks (the
+// kernels loop over whatever a smaller grid leaves), and for a reduction at
+// most the partials the context holds.
+inline unsigned scalar_grid(const bs_ctx *c, int64_t n, bool reduction = false)
 {
-    int64_t g = (n + kBlock - 1) / kBlock;
-    const int64_t cap = (int64_t)c->cus * 8;
+    const int64_t per = (int64_t)kBlock * kScalarUnroll;
+    int64_t g = (n + per - 1) / per;
+    const int64_t cap = reduction ? (int64_t)c->max_partials : (int64_t)1 << 22;
     if (g > cap) g = cap;
     if (g < 1) g = 1;
     return (unsigned)g;
@@ -1339,7 +1402,7 @@ int dot_launch(bs_ctx *c, int64_t n, const double *x, const double *y, bool squa
         }
         return launch_status();
     }
-    const unsigned nb = scalar_grid(c, n);
+    const unsigned nb = scalar_grid(c, n, true);
     launch(c, k_dot_scalar, dim3(nb), dim3(kBlock), 0, st, n, x, y, c->partials);
     if (hipGetLastError() != hipSuccess) return BS_EHIP;
     return finish_two_stage(c, nb, f, st);
@@ -1605,7 +1668,7 @@ int bs_cg_update(bs_ctx *c, int64_t n, double alpha, const double *p, const doub
                sp.n2, p, q, x, r, alpha, ht_of(sp), g, fin_out(c, rr, false));
         return launch_status();
     }
-    const unsigned nb = scalar_grid(c, n);
+    const unsigned nb = scalar_grid(c, n, true);
     launch(c, k_cg_update_scalar, dim3(nb), dim3(kBlock), 0, st, n, alpha, p, q, x, r, c->partials);
     if (hipGetLastError() != hipSuccess) return BS_EHIP;
     return finish_launch(c, nb, rr, false, st);
