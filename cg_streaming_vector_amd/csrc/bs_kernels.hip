@@ -953,18 +953,21 @@ __global__ __launch_bounds__(kBlock) void k_scatter_scalar(int64_t nl, const int
 // scalar loads; without a plan nothing else can name them), issues its ids
 // (consecutive lanes on consecutive entries) and the two offsets of each of
 // its rows at once, stages the v_L values in LDS and, after the one barrier,
-// sums each row from LDS in ascending order. kSpanCap covers every span of a
-// hexahedral box of order 2 or more (at most 8 entries per row on a corner
-// line, 4.6 on average along the densest line), so only unusual meshes take
-// the global-memory path. Spans go to the XCDs in runs of kSpanRun, as plan
-// blocks do, so that neighbouring spans, which read neighbouring v_L lines,
-// share an L2. Measured against a row-per-lane kernel (one lane per row,
-// its ids and values loaded row by row): 58.9 against 79.5 us at 32^3 N=7,
-// 207.1 against 270.9 us at 24^3 N=15, 61.8 against 96.1 us on the
-// tet-split mesh, the same bits; 2-5% behind a plan. P is the cache policy
-// of its streams (ids, v_G): the CG iteration takes kKeep when its working set
-// fits in the last-level cache (41.6 against 42.8 us per iteration on a
-// 32 x 32 x 4-element slab at N=7 without a plan).
+// sums each row from LDS in ascending order. A span over kSpanCap entries
+// takes the global-memory path. On a box of order N the densest rows, the
+// lines through element corners, average 4 (1 + 1/N) entries, so only spans
+// lying mostly on such a line overflow: none at 32^3 order 7, whose lines are
+// 225 rows long (at most about 1700 entries in a span), and about one span
+// in N^2 where lines are longer than a span. Spans go to the XCDs in runs
+// of kSpanRun, as plan blocks do, so that neighbouring spans, which read
+// neighbouring v_L lines, share an L2. Measured against a row-per-lane
+// kernel (one lane per row, its ids and values loaded row by row): 58.9
+// against 79.5 us at 32^3 N=7, 207.1 against 270.9 us at 24^3 N=15, 61.8
+// against 96.1 us on the tet-split mesh, the same bits; 2-5% behind a plan.
+// P is the cache policy of its streams (ids, v_G): the CG iteration takes
+// kKeep when its working set fits in the last-level cache (41.6 against
+// 42.8 us per iteration on a 32 x 32 x 4-element slab at N=7 without a
+// plan).
 template <bool kDot, int P>
 __global__ __launch_bounds__(kBlock) void k_gather_span(int64_t ng, const int32_t *__restrict__ off,
                                                         const int32_t *__restrict__ ids,
