@@ -398,6 +398,27 @@ def test_gather_spans_at_and_over_capacity(env):
     assert_rel(got, orc.dot(want, wv), "span gather dot")
 
 
+def test_gather_span_over_capacity_on_a_long_box(env):
+    """An 80 x 2 x 2 box at order 7: its interior line of element corners is
+    561 rows long, so one 512-row span holds more entries than the span
+    kernel stages (2120 > 2048) and goes through global memory, between
+    spans that are staged; with and without a plan, the oracle's bits."""
+    bs, orc, torch, d = env
+    l2g = bs.bs_mesh_box_l2g(80, 2, 2, 7)
+    ng = bs.bs_mesh_box_count(80, 2, 2, 7)[1]
+    off, ids = bs.bs_index_g2l(l2g, ng)
+    spans = np.diff(off[np.minimum(np.arange(0, ng + 512, 512), ng)])
+    assert spans.max() > 2048 and (spans <= 2048).sum() > 200
+    ol2g, _ = orc.mesh_box(80, 2, 2, 7)
+    vlv = bs_inputs.uniform_pm1(88, l2g.size)
+    want = orc.gather(ol2g, vlv, ng)
+    for plan in (None, bs.bs_gather_plan(off, 1024)):
+        vg = torch.full((ng,), np.nan, dtype=torch.float64, device=d)
+        bs.bs_gather(dev(torch, d, off), dev(torch, d, ids), dev(torch, d, vlv), vg,
+                     None if plan is None else dev(torch, d, plan))
+        assert_bits(host(vg), want, f"long box, plan={plan is not None}")
+
+
 def test_gather_plan_over_capacity_blocks(env):
     """A hand-made plan whose blocks exceed the LDS capacity (rows or
     entries) takes the global-memory path, with the same bits."""
