@@ -26,9 +26,10 @@
  *    must be 8-byte aligned and int32 pointers 4-byte aligned (BS_EALIGN).
  *    The vector operations run fastest on operands that share one 16-byte
  *    phase (all aligned, or all 8 bytes off); operands in different phases
- *    take 8-byte kernels, 15-20% slower for AXPY and the fused update. The
+ *    take 8-byte kernels, 14-21% slower for AXPY and the fused update. The
  *    scatter likewise wants l2g 8-byte and v_local 16-byte aligned (else
- *    about 7% slower). Results are the same either way.
+ *    about 7% slower). Elementwise results are the same bits either way;
+ *    reductions sum in another fixed order, within the same tolerance.
  *  - A context owns the reduction scratch of one device. Calls that use the
  *    same context must be ordered (one stream, or explicit dependencies);
  *    concurrent reductions on one context race.
